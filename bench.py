@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV cache hot path on one MI355X.
+
+One step = one decode step of one attention layer over one batch: the
+slot-mapped KV write of every sequence's new token, then paged decode
+attention over the whole context (split-K with the partition reduce).  Inputs
+are seeded synthetic data resident in HBM before timing starts.  Steps rotate
+over several layer pools (each its own K/V tensors) so a pool is not still
+resident in the 256 MB last-level cache when it is read again.
+
+Prints ONE JSON line:
+  value  = KV bytes read per step / wall time per step (GB/s, decimal)
+  roofline = the decode call's KV bytes / its event-timed duration vs 8 TB/s
+  cpu_baseline = the fp64 oracle timed on this host on the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c4bs32", "c5"])
+    p.add_argument("--partition", type=int, default=512, help="split-K tokens (0 = single pass)")
+    p.add_argument("--waves", type=int, default=4)
+    p.add_argument("--layers", type=int, default=0, help="layer pools to rotate (0 = auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    return p.parse_args()
+
+
+def build_workload(name):
+    import workloads
+    if name == "c2":
+        return workloads.c2_qwen_decode()
+    if name == "c3":
+        return workloads.c3_shared_prefix()
+    if name == "c4":
+        return workloads.c4_long_context(block_size=16)
+    if name == "c4bs32":
+        return workloads.c4_long_context(block_size=32)
+    return workloads.c5_fp8()
+
+
+def cpu_baseline(case, seconds):
+    """The fp64 oracle (write + decode of one step) on this host's cores."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    kc, vc = case.key_cache.copy(), case.value_cache.copy()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        if case.k_new is not None:
+            oracle.paged_kv_write(case.k_new, case.v_new, case.slot_mapping, kc, vc,
+                                  case.k_scale, case.v_scale)
+        oracle.paged_attention_decode(case.q, kc, vc, case.block_tables, case.context_lens,
+                                      case.scale, case.block_size, case.k_scale, case.v_scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": case.kv_bytes() * reps / el / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"the whole {case.name} step (write + fp64 decode of all {case.num_seqs} "
+                  f"sequences), repeated {reps} times in {el:.1f} s",
+        "tokens_per_s_per_layer": case.num_seqs * reps / el,
+        "cpu_model": model,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path needs no cross-GPU exchange; see DESIGN.md for sharding)",
+              file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_135_amd as pkv
+
+    def dev(a):
+        # host arrays carry bf16 as uint16 bits and E4M3 as uint8 codes
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    pkv.load()
+    print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
+    case = build_workload(args.workload)
+    pool_bytes = case.key_cache.nbytes * 2
+    layers = args.layers or max(2, math.ceil(4 * MALL_BYTES / pool_bytes))
+    layers = min(layers, 16)
+
+    q = dev(case.q)
+    tables, lens = dev(case.block_tables), dev(case.context_lens)
+    kc0, vc0 = dev(case.key_cache), dev(case.value_cache)
+    if case.fill_k is not None:  # pools that start empty are filled through the write
+        pkv.paged_kv_write(dev(case.fill_k), dev(case.fill_v), dev(case.fill_slots), kc0, vc0,
+                           k_scale=case.k_scale, v_scale=case.v_scale)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(layers - 1)]
+    knew, vnew, slots = dev(case.k_new), dev(case.v_new), dev(case.slot_mapping)
+    out = torch.empty_like(q)
+    ws = None
+    if args.partition:
+        nbytes = pkv.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
+                                            case.block_tables.shape[1], case.block_size,
+                                            args.partition)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    writes = [pkv.WriteLaunch(knew, vnew, slots, kc, vc, k_scale=case.k_scale,
+                              v_scale=case.v_scale) for kc, vc in pools]
+    decodes = [pkv.DecodeLaunch(out, q, kc, vc, tables, lens, case.scale, case.block_size,
+                                k_scale=case.k_scale, v_scale=case.v_scale,
+                                partition_size=args.partition, waves_per_group=args.waves,
+                                workspace=ws) for kc, vc in pools]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def run_steps(n, ev=None):
+        for i in range(n):
+            li = i % layers
+            if ev is not None:
+                ev[i][0].record(stream)
+            writes[li]()
+            if ev is not None:
+                ev[i][1].record(stream)
+            decodes[li]()
+            if ev is not None:
+                ev[i][2].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps, {layers} layer pools", file=sys.stderr, flush=True)
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+
+    # timed region 1: wall clock over K steps (no per-step events)
+    K = args.steps
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_steps(layers)
+        torch.cuda.synchronize()
+        reps = max(1, K // layers)
+        K = reps * layers
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_steps(K)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+
+    # timed region 2: per-launch HIP events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    run_steps(K, ev)
+    torch.cuda.synchronize()
+    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    wr_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    dec_s = float(dec_ms.mean()) / 1e3
+
+    kv = case.kv_bytes()
+    value = kv / (ms_per_step / 1e3) / 1e9
+    achieved = kv / dec_s / 1e9
+    print(f"[bench] decode {dec_ms.mean()*1e3:.1f} us (p10 {np.percentile(dec_ms,10)*1e3:.1f}, "
+          f"p90 {np.percentile(dec_ms,90)*1e3:.1f}), write {wr_ms.mean()*1e3:.1f} us, "
+          f"step {ms_per_step*1e3:.1f} us", file=sys.stderr, flush=True)
+
+    res = {
+        "metric": "paged decode attn: KV GB/s read (% of MI355X HBM peak) + decode tokens/s per layer",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8_e4m3/bf16", "f32": "f32"}[case.cache_dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": case.name,
+            "num_seqs": case.num_seqs,
+            "num_q_heads": case.num_q_heads,
+            "num_kv_heads": case.num_kv_heads,
+            "head_dim": case.head_dim,
+            "block_size": case.block_size,
+            "context_tokens": int(case.context_lens.astype(np.int64).sum()),
+            "partition_size": args.partition,
+            "waves_per_group": args.waves,
+            "layer_pools": layers,
+            "graph": bool(args.graph),
+        },
+        "kv_bytes_per_step": kv,
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_tokens_per_s_per_layer": round(case.num_seqs / (ms_per_step / 1e3), 1),
+        "decode_us": round(dec_s * 1e6, 2),
+        "write_us": round(float(wr_ms.mean()) * 1e3, 2),
+        "roofline": {
+            "kernel": "paged_attention_decode (partition + reduce)" if args.partition
+                      else "paged_attention_decode",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+    }
+    if case.cache_dtype != "bf16" or case.shared_blocks:
+        res["unique_kv_bytes_per_step"] = case.unique_kv_bytes()
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,196 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: the paged KV cache hot path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Two device operations:
+ *
+ *   paged_kv_write          the slot-mapped KV-cache write.  Each new token's
+ *                           key and value rows land in one slot (physical
+ *                           block, offset) of a shared pool of fixed-size
+ *                           blocks.  Source: "PagedAttention, clearly
+ *                           explained" (a block holds the K/V of a fixed number
+ *                           of consecutive tokens; a sequence only holds blocks
+ *                           it has written) and "What problem does
+ *                           PagedAttention solve for the KV cache in vLLM?",
+ *                           section "The paging idea" (blocks are allocated as
+ *                           the sequence grows).
+ *
+ *   paged_attention_decode  attention for one new query token per sequence,
+ *                           with keys and values gathered through the
+ *                           sequence's block table.  Source: the same thread (at
+ *                           each decode step the kernel reads the block table
+ *                           and gathers K/V from whichever physical blocks they
+ *                           landed in) and "pipe-paged-block-allocation-kv-cache",
+ *                           sections "In and out" (the table is handed to the
+ *                           attention kernel, which gathers through that
+ *                           indirection; output is identical given the same
+ *                           reduction order) and "Concept" (attention is a
+ *                           weighted sum over logically ordered positions).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are passed as pkv_tensor descriptors.  The library never
+ *    allocates, frees or retains caller memory; every buffer is owned by the
+ *    caller and must stay alive until the work queued on the stream is done.
+ *  - Device entry points are asynchronous on `hip_stream` (a hipStream_t; NULL
+ *    means the default stream).  They do not synchronize and do not allocate.
+ *  - Validation looks only at descriptors, never at device memory.  On failure
+ *    nothing is launched, a status other than PKV_OK is returned and
+ *    pkv_last_error() describes it.  Kernels never trap: block ids, context
+ *    lengths and slots are the caller's contract (see pkv_validate_* to check
+ *    host copies).
+ *  - Layouts (all row-major and dense, strides in elements):
+ *      k, v            [T, Hkv, D]         new tokens
+ *      slot_mapping    [T] int32           slot = block * block_size + offset; < 0 skips
+ *      key_cache,
+ *      value_cache     [NB, Hkv, bs, D]    one layer's pool (a block id names the
+ *                                          same block in every layer's pool)
+ *      q, out          [S, Hq, D]          query head h reads KV head h / (Hq / Hkv)
+ *      block_tables    [S, max_blocks] int32  entry j = physical block of tokens
+ *                                          j*bs .. j*bs+bs-1
+ *      context_lens    [S] int32           tokens attended by sequence s (the new
+ *                                          token included: write first, then decode)
+ *  - Element types: f32 cache with f32 q/out/k/v; bf16 cache with bf16
+ *    q/out/k/v; E4M3 cache (OCP 8-bit float, 1 sign / 4 exponent (bias 7) /
+ *    3 mantissa bits, no infinities, max 448) with bf16 q/out, f32 or bf16
+ *    k/v for the write, and a per-tensor scale carried in the cache
+ *    descriptor: stored value = code value * scale.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+#define PKV_MAX_DIMS 4
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3 = 2,
+  PKV_I32 = 3
+} pkv_dtype;
+
+typedef struct {
+  void* data;                    /* device pointer (host pointer for pkv_validate_*) */
+  int32_t dtype;                 /* pkv_dtype */
+  int32_t ndim;                  /* number of used entries in shape/stride, <= 4 */
+  int64_t shape[PKV_MAX_DIMS];
+  int64_t stride[PKV_MAX_DIMS];  /* in elements; the kernels require dense row-major */
+  float scale;                   /* E4M3 tensors: dequantisation scale (> 0, finite);
+                                    ignored for other element types */
+} pkv_tensor;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required descriptor or data pointer is NULL */
+  PKV_ERR_DTYPE = 2,       /* unsupported or mismatched element types */
+  PKV_ERR_SHAPE = 3,       /* ranks or sizes disagree */
+  PKV_ERR_LAYOUT = 4,      /* not dense row-major, or an output aliases an input */
+  PKV_ERR_UNSUPPORTED = 5, /* head_dim, block_size, group size or partition size outside
+                              what the kernels are built for */
+  PKV_ERR_WORKSPACE = 6,   /* split-K workspace missing or too small */
+  PKV_ERR_HIP = 7,         /* the HIP runtime reported an error at launch */
+  PKV_ERR_RANGE = 8        /* pkv_validate_*: an id, length or slot is out of range */
+} pkv_status;
+
+typedef struct {
+  /* 0: one workgroup per (sequence, KV head) walks the whole context.
+     > 0: split-K; each workgroup covers `partition_size` tokens (a multiple of
+     16), writes its partial softmax state to the workspace, and a reduce kernel
+     merges the partitions in a fixed order.  Sequences that fit in one
+     partition skip the reduce. */
+  int32_t partition_size;
+  /* wavefronts per workgroup, each walking a disjoint subset of the tiles:
+     0 = library default, else 1, 2, 4 or 8 */
+  int32_t waves_per_group;
+  void* workspace;          /* device memory, >= paged_attention_decode_workspace_bytes() */
+  size_t workspace_bytes;
+} pkv_decode_opts;
+
+/* Version of this header the library was built from (PKV_ABI_VERSION). */
+int32_t pkv_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if
+ * none).  The pointer stays valid until the next call on the same thread. */
+const char* pkv_last_error(void);
+
+/*
+ * Slot-mapped KV-cache write.
+ *   k, v          [T, Hkv, D], f32 or bf16 (same type for both)
+ *   slot_mapping  [T] int32; token t goes to block slot / bs, offset slot % bs;
+ *                 a negative slot skips the token
+ *   key_cache,
+ *   value_cache   [NB, Hkv, bs, D]
+ * Same element type in and out: the bits are copied.  E4M3 cache: each value
+ * is multiplied in f32 by inv = 1.0f / cache.scale (inv formed once in f32)
+ * and rounded to the nearest E4M3 value, ties to even; magnitudes past 448
+ * and infinities become +-448; NaN becomes code 0x7F.
+ * Slots must be distinct and < NB * bs (caller contract; duplicates race,
+ * out-of-range slots write outside the pool).  Cache bytes of slots not named
+ * are never touched.
+ * Errors: PKV_ERR_NULL, PKV_ERR_DTYPE, PKV_ERR_SHAPE, PKV_ERR_LAYOUT,
+ * PKV_ERR_UNSUPPORTED (D not a multiple of 8), PKV_ERR_HIP.
+ */
+pkv_status paged_kv_write(const pkv_tensor* k, const pkv_tensor* v,
+                          const pkv_tensor* slot_mapping, pkv_tensor* key_cache,
+                          pkv_tensor* value_cache, void* hip_stream);
+
+/*
+ * Decode attention over the paged cache.
+ *   out           [S, Hq, D], same element type as q (f32 or bf16)
+ *   q             [S, Hq, D]
+ *   key_cache,
+ *   value_cache   [NB, Hkv, bs, D]; bs == block_size
+ *   block_tables  [S, max_blocks] int32; entries j < ceil(len/bs) must be in [0, NB)
+ *   context_lens  [S] int32; 0 <= len <= max_blocks * bs
+ *   scale         multiplies q.k before the softmax (e.g. 1/sqrt(D))
+ *   opts          NULL = single pass with the default wave count
+ * For each sequence s and query head h (KV head hk = h / (Hq / Hkv)):
+ *   out[s,h,:] = sum_t softmax_t(scale * q[s,h,:].K[t,:]) V[t,:] over t < len,
+ *   K/V rows read through the table; len == 0 gives zeros.  Slots past len and
+ *   blocks not listed may hold any bits, NaN included: they never reach out.
+ * Supported: Hq % Hkv == 0 with Hq / Hkv <= 16, D in {64, 128}, block_size a
+ * multiple of 16 up to 256, partition_size 0 or a positive multiple of 16.
+ * Results are deterministic and do not depend on which physical blocks hold
+ * the tokens.
+ * Errors: PKV_ERR_NULL, PKV_ERR_DTYPE, PKV_ERR_SHAPE, PKV_ERR_LAYOUT,
+ * PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ */
+pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q,
+                                  const pkv_tensor* key_cache, const pkv_tensor* value_cache,
+                                  const pkv_tensor* block_tables,
+                                  const pkv_tensor* context_lens, float scale,
+                                  int32_t block_size, const pkv_decode_opts* opts,
+                                  void* hip_stream);
+
+/* Workspace bytes split-K needs for these sizes (0 when partition_size == 0).
+ * Returns 0 as well for invalid arguments (negative sizes). */
+size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t head_dim, int32_t max_blocks_per_seq,
+                                              int32_t block_size, int32_t partition_size);
+
+/*
+ * Opt-in host-side checks of the caller contract, on HOST copies.
+ * pkv_validate_slots: every slot < num_blocks * block_size and no slot
+ *   repeated among the non-negative ones.
+ * pkv_validate_decode_inputs: every context length in [0, max_blocks * bs]
+ *   and every table entry j < ceil(len / bs) in [0, num_blocks).
+ * Return PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE (bad sizes) or PKV_ERR_RANGE.
+ */
+pkv_status pkv_validate_slots(const int32_t* slots, int64_t num_tokens, int64_t num_blocks,
+                              int32_t block_size);
+pkv_status pkv_validate_decode_inputs(const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int32_t block_size);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

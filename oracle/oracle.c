@@ -153,6 +153,8 @@ int orc_paged_kv_write(const void* k, const void* v, int in_dtype, const int32_t
     int64_t slot = slot_mapping[t];
     if (slot >= NB * (int64_t)bs) return ORC_ERR_RANGE;
   }
+  /* tokens name distinct slots (caller contract), so they are independent */
+#pragma omp parallel for schedule(static)
   for (t = 0; t < T; ++t) {
     int64_t slot = slot_mapping[t], blk, off;
     int32_t h, d;

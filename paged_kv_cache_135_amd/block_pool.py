@@ -1,0 +1,224 @@
+"""Host-side block allocator for the paged KV cache (bookkeeping only, no GPU).
+
+What it keeps, by page and section:
+  * a pool of fixed-size physical blocks carved once, handed out from a free
+    stack ("pipe-paged-block-allocation-kv-cache", section "In and out": the
+    free-block pool is a stack of physical indices into one pre-allocated
+    tensor per layer);
+  * a block table per sequence mapping logical block j (tokens j*bs ..
+    j*bs+bs-1) to a physical id ("PagedAttention, clearly explained"; foundry
+    section "Concept": a page table by another name);
+  * on-demand growth: a sequence starts with just enough blocks for its prompt
+    and gains one block each time the last one fills ("What problem does
+    PagedAttention solve...", section "The paging idea");
+  * release on finish: blocks return to the pool when no table lists them;
+  * reference counts and copy-on-write: forks list the same physical blocks,
+    and a shared block is copied before one branch writes into it
+    ("PagedAttention Memory Management", section "Complex Topologies and
+    Memory Sharing"; katajob section "Sharing, the second dividend");
+  * pool sizing from the memory left after weights and a reserve, with the
+    per-block byte formula ("PagedAttention Memory Management", section
+    "Calculating Physical Block Sizes").
+
+Slots handed to the KV write are ``physical_block * block_size + offset``.
+Copy-on-write returns (source, destination) physical block pairs; copying the
+block contents on the device is the caller's job before the write lands.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+class OutOfBlocks(MemoryError):
+    """The free stack cannot satisfy a request (the point where a scheduler
+    would preempt a sequence)."""
+
+
+def block_bytes(num_layers: int, num_kv_heads: int, head_dim: int, block_size: int,
+                elem_bytes: int) -> int:
+    """Bytes of one physical block over all layers, K and V."""
+    return 2 * num_layers * num_kv_heads * head_dim * block_size * elem_bytes
+
+
+def blocks_for_memory(free_bytes: int, one_block_bytes: int) -> int:
+    """Whole blocks that fit in ``free_bytes``."""
+    if one_block_bytes <= 0:
+        raise ValueError("block bytes must be positive")
+    return max(0, int(free_bytes) // int(one_block_bytes))
+
+
+@dataclass
+class _Seq:
+    table: list = field(default_factory=list)
+    num_tokens: int = 0
+
+
+class BlockPool:
+    """Free stack + per-sequence block tables + reference counts."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_model_len: int | None = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        if max_model_len is not None and num_blocks * block_size < max_model_len:
+            # a pool that cannot hold one sequence of the maximum length is refused
+            raise OutOfBlocks(
+                f"pool of {num_blocks} x {block_size} slots cannot hold one sequence of "
+                f"{max_model_len} tokens")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        # pop() takes the top: start with block 0 on top
+        self._free = list(range(self.num_blocks - 1, -1, -1))
+        self._ref = np.zeros(self.num_blocks, dtype=np.int64)
+        self._seqs: dict = {}
+
+    # ------------------------------------------------------------ queries
+    @property
+    def num_free(self) -> int:
+        return len(self._free)
+
+    def refcount(self, block: int) -> int:
+        return int(self._ref[block])
+
+    def table(self, seq) -> list:
+        return list(self._seqs[seq].table)
+
+    def num_tokens(self, seq) -> int:
+        return self._seqs[seq].num_tokens
+
+    def blocks_needed(self, n_tokens: int) -> int:
+        return -(-int(n_tokens) // self.block_size)
+
+    def slot(self, seq, position: int) -> int:
+        s = self._seqs[seq]
+        if not 0 <= position < s.num_tokens:
+            raise IndexError("position outside the sequence")
+        return s.table[position // self.block_size] * self.block_size + position % self.block_size
+
+    # -------------------------------------------------------------- edits
+    def _pop(self) -> int:
+        if not self._free:
+            raise OutOfBlocks("no free block")
+        b = self._free.pop()
+        self._ref[b] = 1
+        return b
+
+    def _release(self, b: int) -> None:
+        self._ref[b] -= 1
+        if self._ref[b] == 0:
+            self._free.append(b)
+        elif self._ref[b] < 0:  # pragma: no cover - bookkeeping bug
+            raise AssertionError("negative reference count")
+
+    def allocate(self, seq, n_tokens: int, prefix_of=None, prefix_blocks: int = 0) -> np.ndarray:
+        """Admit a sequence with ``n_tokens`` prompt tokens; returns their slots.
+
+        ``prefix_of``/``prefix_blocks``: the first ``prefix_blocks`` logical
+        blocks are the ones another sequence already lists (a shared prompt
+        prefix); only the rest are taken from the pool."""
+        if seq in self._seqs:
+            raise KeyError(f"sequence {seq!r} exists")
+        n_tokens = int(n_tokens)
+        need = self.blocks_needed(n_tokens)
+        shared = []
+        if prefix_of is not None:
+            src = self._seqs[prefix_of]
+            if prefix_blocks > len(src.table) or prefix_blocks * self.block_size > n_tokens:
+                raise ValueError("prefix longer than the source or the new sequence")
+            if prefix_blocks * self.block_size > src.num_tokens:
+                raise ValueError("only filled blocks can be shared")
+            shared = src.table[:prefix_blocks]
+        fresh = need - len(shared)
+        if fresh > len(self._free):
+            raise OutOfBlocks(f"need {fresh} blocks, {len(self._free)} free")
+        for b in shared:
+            self._ref[b] += 1
+        s = _Seq(table=list(shared) + [self._pop() for _ in range(fresh)], num_tokens=n_tokens)
+        self._seqs[seq] = s
+        return self._slots(s, 0, n_tokens)
+
+    def append(self, seq, n: int = 1):
+        """Grow a sequence by ``n`` tokens.  Returns (slots, cow_pairs): the new
+        tokens' slots and the (source, destination) physical blocks to copy
+        before writing (copy-on-write of a shared, partly filled last block)."""
+        s = self._seqs[seq]
+        bs = self.block_size
+        cow = []
+        n = int(n)
+        if n <= 0:
+            return np.zeros(0, np.int32), cow
+        new_total = s.num_tokens + n
+        extra = self.blocks_needed(new_total) - len(s.table)
+        partial_shared = s.num_tokens % bs != 0 and self._ref[s.table[-1]] > 1
+        if extra + (1 if partial_shared else 0) > len(self._free):
+            raise OutOfBlocks(f"need {extra + partial_shared} blocks, {len(self._free)} free")
+        if partial_shared:
+            old = s.table[-1]
+            new = self._pop()
+            self._ref[old] -= 1
+            s.table[-1] = new
+            cow.append((old, new))
+        for _ in range(extra):
+            s.table.append(self._pop())
+        first = s.num_tokens
+        s.num_tokens = new_total
+        return self._slots(s, first, new_total), cow
+
+    def fork(self, seq, new_seq) -> None:
+        """New sequence listing the same blocks (parallel sampling, beam search)."""
+        if new_seq in self._seqs:
+            raise KeyError(f"sequence {new_seq!r} exists")
+        s = self._seqs[seq]
+        for b in s.table:
+            self._ref[b] += 1
+        self._seqs[new_seq] = _Seq(table=list(s.table), num_tokens=s.num_tokens)
+
+    def free(self, seq) -> None:
+        """Finish a sequence: its blocks go back to the pool once unreferenced."""
+        s = self._seqs.pop(seq)
+        for b in reversed(s.table):
+            self._release(b)
+
+    # ---------------------------------------------------- kernel inputs
+    def _slots(self, s: _Seq, lo: int, hi: int) -> np.ndarray:
+        pos = np.arange(lo, hi, dtype=np.int64)
+        tab = np.asarray(s.table, dtype=np.int64)
+        return (tab[pos // self.block_size] * self.block_size + pos % self.block_size).astype(np.int32)
+
+    def block_tables(self, seqs, pad: int = 0) -> np.ndarray:
+        """int32 [len(seqs), max blocks] tables, padded with ``pad``."""
+        seqs = list(seqs)
+        width = max([1] + [len(self._seqs[q].table) for q in seqs])
+        out = np.full((len(seqs), width), pad, dtype=np.int32)
+        for i, q in enumerate(seqs):
+            t = self._seqs[q].table
+            out[i, :len(t)] = t
+        return out
+
+    def context_lens(self, seqs) -> np.ndarray:
+        return np.array([self._seqs[q].num_tokens for q in seqs], dtype=np.int32)
+
+    def stats(self) -> dict:
+        """Live-KV fraction (tokens held / slots of blocks in use, each physical
+        block counted once) and per-sequence tail waste."""
+        in_use = int((self._ref > 0).sum())
+        bs = self.block_size
+        live = set()
+        for s in self._seqs.values():
+            for j, b in enumerate(s.table):
+                filled = min(bs, s.num_tokens - j * bs)
+                live.add((b, filled))
+        # a shared block counts its filled slots once (the largest fill seen)
+        best = {}
+        for b, f in live:
+            best[b] = max(best.get(b, 0), f)
+        held = sum(best.values())
+        waste = {q: (-s.num_tokens) % bs if s.table else 0 for q, s in self._seqs.items()}
+        return {
+            "blocks_in_use": in_use,
+            "blocks_free": len(self._free),
+            "live_fraction": held / (in_use * bs) if in_use else 1.0,
+            "waste_per_seq": waste,
+            "max_waste": max(waste.values()) if waste else 0,
+        }

@@ -1,0 +1,330 @@
+// extern "C" entry points of libpagedkv.so: descriptor validation, launch
+// parameters and error reporting.  Declarations and contracts: include/pagedkv.h.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+int64_t elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+    case PKV_I32: return 4;
+    default: return 0;
+  }
+}
+
+int64_t numel(const pkv_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+// rank, non-negative sizes, dense row-major strides, data present when non-empty
+pkv_status check_tensor(const pkv_tensor* t, const char* name, int ndim) {
+  if (!t) return fail(PKV_ERR_NULL, "%s: descriptor is NULL", name);
+  if (t->ndim != ndim) return fail(PKV_ERR_SHAPE, "%s: expected %d dims, got %d", name, ndim, t->ndim);
+  if (elem_bytes(t->dtype) == 0) return fail(PKV_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+  int64_t expect = 1;
+  for (int i = ndim - 1; i >= 0; --i) {
+    if (t->shape[i] < 0) return fail(PKV_ERR_SHAPE, "%s: negative size in dim %d", name, i);
+    if (t->shape[i] > 1 && t->stride[i] != expect)
+      return fail(PKV_ERR_LAYOUT, "%s: not dense row-major (dim %d stride %lld, expected %lld)",
+                  name, i, (long long)t->stride[i], (long long)expect);
+    expect *= t->shape[i];
+  }
+  if (numel(t) > 0 && !t->data) return fail(PKV_ERR_NULL, "%s: data pointer is NULL", name);
+  return PKV_OK;
+}
+
+pkv_status check_align(const pkv_tensor* t, const char* name, uintptr_t align) {
+  if (numel(t) > 0 && (reinterpret_cast<uintptr_t>(t->data) % align) != 0)
+    return fail(PKV_ERR_LAYOUT, "%s: data must be %u-byte aligned", name, (unsigned)align);
+  return PKV_OK;
+}
+
+bool overlap(const pkv_tensor* a, const pkv_tensor* b) {
+  const int64_t na = numel(a) * elem_bytes(a->dtype), nb = numel(b) * elem_bytes(b->dtype);
+  if (na == 0 || nb == 0) return false;
+  const char* pa = static_cast<const char*>(a->data);
+  const char* pb = static_cast<const char*>(b->data);
+  return pa < pb + nb && pb < pa + na;
+}
+
+pkv_status check_scale(const pkv_tensor* t, const char* name) {
+  if (t->dtype == PKV_FP8_E4M3 && !(std::isfinite(t->scale) && t->scale > 0.f))
+    return fail(PKV_ERR_SHAPE, "%s: E4M3 scale must be finite and > 0 (got %g)", name,
+                (double)t->scale);
+  return PKV_OK;
+}
+
+#define PKV_TRY(expr)                \
+  do {                               \
+    pkv_status st_ = (expr);         \
+    if (st_ != PKV_OK) return st_;   \
+  } while (0)
+
+int64_t num_partitions(int64_t max_blocks, int64_t block_size, int64_t partition_size) {
+  if (partition_size <= 0) return 1;
+  const int64_t tokens = max_blocks * block_size;
+  const int64_t np = (tokens + partition_size - 1) / partition_size;
+  return np < 1 ? 1 : np;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+pkv_status paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+                          pkv_tensor* key_cache, pkv_tensor* value_cache, void* hip_stream) {
+  PKV_TRY(check_tensor(k, "k", 3));
+  PKV_TRY(check_tensor(v, "v", 3));
+  PKV_TRY(check_tensor(slot_mapping, "slot_mapping", 1));
+  PKV_TRY(check_tensor(key_cache, "key_cache", 4));
+  PKV_TRY(check_tensor(value_cache, "value_cache", 4));
+  if (k->dtype != PKV_F32 && k->dtype != PKV_BF16)
+    return fail(PKV_ERR_DTYPE, "k: must be f32 or bf16");
+  if (v->dtype != k->dtype) return fail(PKV_ERR_DTYPE, "v: dtype differs from k");
+  if (slot_mapping->dtype != PKV_I32) return fail(PKV_ERR_DTYPE, "slot_mapping: must be int32");
+  if (value_cache->dtype != key_cache->dtype)
+    return fail(PKV_ERR_DTYPE, "value_cache: dtype differs from key_cache");
+  if (key_cache->dtype != k->dtype && key_cache->dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_DTYPE, "key_cache: must match k's dtype or be E4M3");
+  for (int i = 0; i < 3; ++i)
+    if (v->shape[i] != k->shape[i]) return fail(PKV_ERR_SHAPE, "v: shape differs from k");
+  for (int i = 0; i < 4; ++i)
+    if (value_cache->shape[i] != key_cache->shape[i])
+      return fail(PKV_ERR_SHAPE, "value_cache: shape differs from key_cache");
+  const int64_t T = k->shape[0], H = k->shape[1], D = k->shape[2];
+  const int64_t NB = key_cache->shape[0], bs = key_cache->shape[2];
+  if (slot_mapping->shape[0] != T) return fail(PKV_ERR_SHAPE, "slot_mapping: expected [%lld]", (long long)T);
+  if (key_cache->shape[1] != H || key_cache->shape[3] != D)
+    return fail(PKV_ERR_SHAPE, "key_cache: heads/head_dim differ from k");
+  if (D <= 0 || D % 8 != 0 || D > 1024)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %lld: must be a positive multiple of 8, <= 1024", (long long)D);
+  if (bs <= 0 || H <= 0 || H > 1024)
+    return fail(PKV_ERR_SHAPE, "block_size and num_kv_heads must be positive (heads <= 1024)");
+  if (NB * bs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "pool has more than 2^31-1 slots");
+  PKV_TRY(check_scale(key_cache, "key_cache"));
+  PKV_TRY(check_scale(value_cache, "value_cache"));
+  PKV_TRY(check_align(k, "k", 16));
+  PKV_TRY(check_align(v, "v", 16));
+  PKV_TRY(check_align(key_cache, "key_cache", 16));
+  PKV_TRY(check_align(value_cache, "value_cache", 16));
+  if (overlap(key_cache, value_cache)) return fail(PKV_ERR_LAYOUT, "key_cache and value_cache overlap");
+  const pkv_tensor* inputs[] = {k, v, slot_mapping};
+  for (const pkv_tensor* in : inputs)
+    if (overlap(in, key_cache) || overlap(in, value_cache))
+      return fail(PKV_ERR_LAYOUT, "an input overlaps a cache");
+  if (T == 0) return ok();
+
+  pkv::WriteArgs a{};
+  a.k = k->data;
+  a.v = v->data;
+  a.slots = static_cast<const int32_t*>(slot_mapping->data);
+  a.kc = key_cache->data;
+  a.vc = value_cache->data;
+  a.num_tokens = T;
+  a.num_heads = (int32_t)H;
+  a.head_dim = (int32_t)D;
+  a.block_size = (int32_t)bs;
+  a.in_dtype = k->dtype;
+  a.cache_dtype = key_cache->dtype;
+  a.inv_k = key_cache->dtype == PKV_FP8_E4M3 ? 1.0f / key_cache->scale : 1.0f;
+  a.inv_v = value_cache->dtype == PKV_FP8_E4M3 ? 1.0f / value_cache->scale : 1.0f;
+  const hipError_t e = pkv::launch_kv_write(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "paged_kv_write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t head_dim, int32_t max_blocks_per_seq,
+                                              int32_t block_size, int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads < 0 || head_dim < 0 || max_blocks_per_seq < 0 ||
+      block_size < 0 || partition_size < 0)
+    return 0;
+  const int64_t np = num_partitions(max_blocks_per_seq, block_size, partition_size);
+  if (np <= 1) return 0;
+  return (size_t)num_seqs * (size_t)num_q_heads * (size_t)np * ((size_t)head_dim + 2) * 4u;
+}
+
+pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q, const pkv_tensor* key_cache,
+                                  const pkv_tensor* value_cache, const pkv_tensor* block_tables,
+                                  const pkv_tensor* context_lens, float scale, int32_t block_size,
+                                  const pkv_decode_opts* opts, void* hip_stream) {
+  PKV_TRY(check_tensor(out, "out", 3));
+  PKV_TRY(check_tensor(q, "q", 3));
+  PKV_TRY(check_tensor(key_cache, "key_cache", 4));
+  PKV_TRY(check_tensor(value_cache, "value_cache", 4));
+  PKV_TRY(check_tensor(block_tables, "block_tables", 2));
+  PKV_TRY(check_tensor(context_lens, "context_lens", 1));
+  if (q->dtype != PKV_F32 && q->dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "q: must be f32 or bf16");
+  if (out->dtype != q->dtype) return fail(PKV_ERR_DTYPE, "out: dtype differs from q");
+  if (value_cache->dtype != key_cache->dtype)
+    return fail(PKV_ERR_DTYPE, "value_cache: dtype differs from key_cache");
+  const int32_t ct = key_cache->dtype;
+  if (!((ct == PKV_F32 && q->dtype == PKV_F32) || (ct == PKV_BF16 && q->dtype == PKV_BF16) ||
+        (ct == PKV_FP8_E4M3 && q->dtype == PKV_BF16)))
+    return fail(PKV_ERR_DTYPE, "cache/q dtypes: supported are f32/f32, bf16/bf16, e4m3/bf16");
+  if (block_tables->dtype != PKV_I32 || context_lens->dtype != PKV_I32)
+    return fail(PKV_ERR_DTYPE, "block_tables and context_lens must be int32");
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(PKV_ERR_SHAPE, "out: shape differs from q");
+  for (int i = 0; i < 4; ++i)
+    if (value_cache->shape[i] != key_cache->shape[i])
+      return fail(PKV_ERR_SHAPE, "value_cache: shape differs from key_cache");
+  const int64_t S = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  const int64_t Hkv = key_cache->shape[1], bs = key_cache->shape[2];
+  const int64_t maxb = block_tables->shape[1];
+  if (key_cache->shape[3] != D) return fail(PKV_ERR_SHAPE, "key_cache: head_dim differs from q");
+  if (block_tables->shape[0] != S || context_lens->shape[0] != S)
+    return fail(PKV_ERR_SHAPE, "block_tables/context_lens: leading dim must be num_seqs");
+  if (bs != block_size) return fail(PKV_ERR_SHAPE, "block_size %d != key_cache.shape[2] %lld",
+                                    block_size, (long long)bs);
+  if (bs < 16 || bs > 256 || bs % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %lld: must be a multiple of 16 in [16, 256]", (long long)bs);
+  if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %lld: must be 64 or 128", (long long)D);
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0)
+    return fail(PKV_ERR_SHAPE, "num_q_heads %lld must be a positive multiple of num_kv_heads %lld",
+                (long long)Hq, (long long)Hkv);
+  if (Hq / Hkv > 16) return fail(PKV_ERR_UNSUPPORTED, "group size %lld > 16", (long long)(Hq / Hkv));
+  if (S > 65535 || Hkv > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 sequences or KV heads");
+  if (S > 0 && maxb <= 0) return fail(PKV_ERR_SHAPE, "block_tables: needs at least one column");
+  if (maxb * bs > INT32_MAX / 2) return fail(PKV_ERR_UNSUPPORTED, "max_blocks * block_size too large");
+  PKV_TRY(check_scale(key_cache, "key_cache"));
+  PKV_TRY(check_scale(value_cache, "value_cache"));
+  PKV_TRY(check_align(out, "out", 16));
+  PKV_TRY(check_align(q, "q", 16));
+  PKV_TRY(check_align(key_cache, "key_cache", 16));
+  PKV_TRY(check_align(value_cache, "value_cache", 16));
+  PKV_TRY(check_align(block_tables, "block_tables", 4));
+  PKV_TRY(check_align(context_lens, "context_lens", 4));
+  const pkv_tensor* inputs[] = {q, key_cache, value_cache, block_tables, context_lens};
+  for (const pkv_tensor* t : inputs)
+    if (overlap(out, t)) return fail(PKV_ERR_LAYOUT, "out overlaps an input");
+
+  int32_t part = opts ? opts->partition_size : 0;
+  int32_t waves = opts ? opts->waves_per_group : 0;
+  if (part < 0 || part % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "partition_size %d: must be 0 or a positive multiple of 16", part);
+  if (waves == 0) waves = 4;
+  if (waves != 1 && waves != 2 && waves != 4 && waves != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "waves_per_group %d: must be 0, 1, 2, 4 or 8", waves);
+
+  const int64_t max_tiles = (maxb * bs + 15) / 16;
+  const int64_t np = num_partitions(maxb, bs, part);
+  const int64_t part_tiles = np > 1 ? part / 16 : (max_tiles > 0 ? max_tiles : 1);
+  pkv::DecodeArgs a{};
+  if (np > 1) {
+    const size_t need = paged_attention_decode_workspace_bytes((int32_t)S, (int32_t)Hq, (int32_t)D,
+                                                               (int32_t)maxb, (int32_t)bs, part);
+    if (!opts->workspace || opts->workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "split-K needs a workspace of %zu bytes (got %zu)", need,
+                  opts->workspace ? opts->workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16 != 0)
+      return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (np > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "too many partitions");
+    a.ws_acc = static_cast<float*>(opts->workspace);
+    a.ws_ml = a.ws_acc + (size_t)S * Hq * np * D;
+  }
+  if (S == 0) return ok();
+
+  a.q = q->data;
+  a.out = out->data;
+  a.kc = key_cache->data;
+  a.vc = value_cache->data;
+  a.tables = static_cast<const int32_t*>(block_tables->data);
+  a.lens = static_cast<const int32_t*>(context_lens->data);
+  a.num_seqs = (int32_t)S;
+  a.num_q_heads = (int32_t)Hq;
+  a.num_kv_heads = (int32_t)Hkv;
+  a.group = (int32_t)(Hq / Hkv);
+  a.head_dim = (int32_t)D;
+  a.block_size = (int32_t)bs;
+  a.max_blocks = (int32_t)maxb;
+  a.part_tiles = (int32_t)part_tiles;
+  a.num_parts = (int32_t)np;
+  a.waves = waves;
+  a.cache_dtype = ct;
+  const double log2e = 1.4426950408889634;
+  const double kscale = ct == PKV_FP8_E4M3 ? (double)key_cache->scale : 1.0;
+  a.qk_scale = (float)((double)scale * log2e * kscale);
+  a.v_scale = ct == PKV_FP8_E4M3 ? value_cache->scale : 1.0f;
+  const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "paged_attention_decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pkv_status pkv_validate_slots(const int32_t* slots, int64_t num_tokens, int64_t num_blocks,
+                              int32_t block_size) {
+  if (num_tokens < 0 || num_blocks < 0 || block_size <= 0)
+    return fail(PKV_ERR_SHAPE, "negative sizes or non-positive block_size");
+  if (num_tokens > 0 && !slots) return fail(PKV_ERR_NULL, "slots is NULL");
+  const int64_t cap = num_blocks * block_size;
+  std::vector<int32_t> live;
+  live.reserve((size_t)num_tokens);
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    if (slots[t] < 0) continue;
+    if (slots[t] >= cap)
+      return fail(PKV_ERR_RANGE, "slot %d of token %lld is outside the pool (%lld slots)", slots[t],
+                  (long long)t, (long long)cap);
+    live.push_back(slots[t]);
+  }
+  std::sort(live.begin(), live.end());
+  for (size_t i = 1; i < live.size(); ++i)
+    if (live[i] == live[i - 1]) return fail(PKV_ERR_RANGE, "slot %d is repeated", live[i]);
+  return ok();
+}
+
+pkv_status pkv_validate_decode_inputs(const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int32_t block_size) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || num_blocks < 0 || block_size <= 0)
+    return fail(PKV_ERR_SHAPE, "negative sizes or non-positive block_size");
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return fail(PKV_ERR_NULL, "NULL input");
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t n = context_lens[s];
+    if (n < 0 || n > (int64_t)max_blocks_per_seq * block_size)
+      return fail(PKV_ERR_RANGE, "context_lens[%d] = %lld outside [0, %lld]", s, (long long)n,
+                  (long long)max_blocks_per_seq * block_size);
+    const int64_t nb = (n + block_size - 1) / block_size;
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t b = block_tables[(int64_t)s * max_blocks_per_seq + j];
+      if (b < 0 || b >= num_blocks)
+        return fail(PKV_ERR_RANGE, "block_tables[%d][%lld] = %d outside [0, %lld)", s, (long long)j,
+                    b, (long long)num_blocks);
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

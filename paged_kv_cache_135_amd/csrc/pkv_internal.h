@@ -1,0 +1,56 @@
+// Internal declarations shared by the HIP translation units of libpagedkv.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+// One KV-cache write launch: T tokens x Hkv heads x D elements for K and V.
+struct WriteArgs {
+  const void* k;
+  const void* v;
+  const int32_t* slots;
+  void* kc;
+  void* vc;
+  int64_t num_tokens;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t in_dtype;     // PKV_F32 or PKV_BF16
+  int32_t cache_dtype;  // in_dtype or PKV_FP8_E4M3
+  float inv_k;          // 1.0f / k scale (E4M3 cache only)
+  float inv_v;
+};
+
+// One decode call (partition kernel + optional reduce).
+struct DecodeArgs {
+  const void* q;
+  void* out;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* ws_acc;        // [S][Hq][NP][D] unnormalised partial outputs
+  float* ws_ml;         // [S][Hq][NP][2] partial running max (log2 units) and sum
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;        // Hq / Hkv
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks;
+  int32_t part_tiles;   // 16-token tiles per partition (single pass: covers max_blocks)
+  int32_t num_parts;    // partitions per (sequence, KV head) = grid.x
+  int32_t waves;        // wavefronts per workgroup
+  int32_t cache_dtype;
+  float qk_scale;       // scale * log2(e) (* k scale for E4M3)
+  float v_scale;        // 1, or the V scale for E4M3
+};
+
+hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pkv

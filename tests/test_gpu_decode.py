@@ -1,0 +1,145 @@
+"""GPU parity of paged decode attention against the fp64 oracle.
+
+Small cases span several tiles, ragged tails, empty contexts, every group size
+class and both head dims, in single-pass and split-K launches with 1-8
+wavefronts per workgroup.  The named workloads run at full size: every row for
+the 4-, 64-, 256- and 512-sequence batches, sampled rows for the 131072-token
+sequences."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    gu.need_gpu()
+
+
+MODES = [(0, 1), (0, 4), (0, 8), (32, 1), (64, 2), (512, 4), (256, 8)]
+
+SMALL = {
+    # name: (context lengths, Hq, Hkv, D, block_size, cache dtype)
+    "g7_d128_bf16": ([1, 15, 16, 17, 31, 100, 255, 257, 600, 1100], 28, 4, 128, 16, "bf16"),
+    "g1_d64_bs32_bf16": ([3, 32, 33, 95, 500, 64], 4, 4, 64, 32, "bf16"),
+    "g16_d128_bs64_bf16": ([64, 65, 700, 1], 16, 1, 128, 64, "bf16"),
+    "g2_d64_f32": ([1, 17, 40, 100, 300], 4, 2, 64, 16, "f32"),
+    "g4_d128_f32": ([16, 90, 513], 8, 2, 128, 32, "f32"),
+    "g4_d128_e4m3": ([16, 17, 1000, 2048, 5], 32, 8, 128, 16, "fp8_e4m3"),
+    "g8_d64_e4m3": ([40, 300, 129], 16, 2, 64, 16, "fp8_e4m3"),
+    "empty_rows_bf16": ([0, 5, 0, 33, 0], 8, 2, 128, 16, "bf16"),
+}
+
+
+def _small(name, seed=7):
+    lens, Hq, Hkv, D, bs, dt = SMALL[name]
+    return workloads.build_case(name, seed=seed, context_lens=lens, num_q_heads=Hq,
+                                num_kv_heads=Hkv, head_dim=D, block_size=bs, cache_dtype=dt,
+                                std=0.5 if dt != "f32" else 1.0, scale=1.0 / math.sqrt(D))
+
+
+_cache = {}
+
+
+def _prepared(name):
+    if name not in _cache:
+        case = _small(name)
+        g = gu.GpuCase(case)
+        g.fill_and_step_writes()
+        kc, vc = gu.oracle_caches(case)
+        _cache[name] = (case, g, gu.oracle_decode(case, kc, vc))
+    return _cache[name]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: f"part{m[0]}_w{m[1]}")
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_cases(name, mode):
+    case, g, ref = _prepared(name)
+    part, waves = mode
+    got = gu.host(g.decode(partition_size=part, waves=waves))
+    gu.assert_close(got, ref, case.cache_dtype, f"{name} part={part} waves={waves}")
+    empty = case.context_lens == 0
+    if empty.any():
+        assert np.all(gu.as_f64(got[empty]) == 0.0)
+
+
+def test_single_token_contexts_return_the_value_row_exactly():
+    case = workloads.build_case("one", seed=3, context_lens=[1] * 9, num_q_heads=12,
+                                num_kv_heads=3, head_dim=128, block_size=16, cache_dtype="bf16",
+                                std=0.5, scale=0.08)
+    g = gu.GpuCase(case)
+    g.fill_and_step_writes()
+    kc, vc = gu.oracle_caches(case)
+    for part, waves in [(0, 1), (0, 4), (16, 2)]:
+        got = gu.host(g.decode(part, waves))
+        for s in range(9):
+            row = vc[case.block_tables[s, 0], :, 0, :]  # [Hkv, D] bf16 bits
+            assert np.array_equal(got[s], np.repeat(row, 4, axis=0))
+
+
+# ------------------------------------------------------------ full sizes
+def _full(name, builder, part, waves, row_mask=None, tokens_mask_fn=None):
+    case = builder()
+    g = gu.GpuCase(case)
+    g.fill_and_step_writes()
+    got = gu.host(g.decode(partition_size=part, waves=waves))
+    tm = tokens_mask_fn(case) if tokens_mask_fn else None
+    kc, vc = gu.oracle_caches(case, tokens_mask=tm)
+    rm = row_mask(case) if row_mask else None
+    ref = gu.oracle_decode(case, kc, vc, row_mask=rm)
+    return case, got, ref, rm
+
+
+def test_c1_tiny_f32_full():
+    for part, waves in [(0, 4), (32, 1)]:
+        case, got, ref, _ = _full("c1", workloads.c1_tiny_f32, part, waves)
+        gu.assert_close(got, ref, "f32", f"c1 part={part}")
+
+
+@pytest.mark.parametrize("part,waves", [(0, 4), (512, 4), (256, 1)])
+def test_c2_qwen_decode_full(part, waves):
+    case, got, ref, _ = _full("c2", workloads.c2_qwen_decode, part, waves)
+    gu.assert_close(got, ref, "bf16", f"c2 part={part}")
+
+
+def test_c3_shared_prefix_full():
+    case, got, ref, _ = _full("c3", workloads.c3_shared_prefix, 512, 4)
+    assert case.shared_blocks == 64
+    gu.assert_close(got, ref, "bf16", "c3")
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_c4_long_context_sampled_rows(bs):
+    def rows(case):
+        m = np.zeros((case.num_seqs, case.num_q_heads), bool)
+        m[[0, case.num_seqs - 1], :] = True
+        return m
+    case, got, ref, rm = _full(f"c4_bs{bs}", lambda: workloads.c4_long_context(block_size=bs),
+                               512, 4, row_mask=rows)
+    gu.assert_close(got, ref, "bf16", f"c4 bs{bs}", mask=rm)
+    assert np.all(np.isfinite(gu.as_f64(got)))
+
+
+def test_c5_e4m3_sampled_rows():
+    rng = np.random.default_rng(5)
+    pick = np.sort(rng.choice(512, size=32, replace=False))
+
+    def tokens(case):
+        starts = np.concatenate([[0], np.cumsum(case.context_lens)[:-1]])
+        mask = np.zeros(case.fill_slots.size, bool)
+        for s in pick:
+            mask[starts[s]:starts[s] + case.context_lens[s]] = True
+        return mask
+
+    def rows(case):
+        m = np.zeros((case.num_seqs, case.num_q_heads), bool)
+        m[pick, :] = True
+        return m
+    case, got, ref, rm = _full("c5", workloads.c5_fp8, 512, 4, row_mask=rows,
+                               tokens_mask_fn=tokens)
+    gu.assert_close(got, ref, "fp8_e4m3", "c5", mask=rm)
