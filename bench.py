@@ -3,7 +3,8 @@
 
 One step = one decode step of one attention layer over one batch: the
 slot-mapped KV write of every sequence's new token, then paged decode
-attention over the whole context (split-K with the partition reduce).  Inputs
+attention over the whole context (by default the balanced split: equal runs
+of tiles per wavefront, then the merge of split (sequence, KV head) pairs).  Inputs
 are seeded synthetic data resident in HBM before timing starts.  Steps rotate
 over several layer pools (each its own K/V tensors) so a pool is not still
 resident in the 256 MB last-level cache when it is read again.
@@ -32,8 +33,10 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c4bs32", "c5"])
-    p.add_argument("--partition", type=int, default=512, help="split-K tokens (0 = single pass)")
-    p.add_argument("--waves", type=int, default=4)
+    p.add_argument("--mode", default="balanced", choices=["single", "partitioned", "balanced"])
+    p.add_argument("--partition", type=int, default=512, help="tokens per partition (partitioned)")
+    p.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (0 = default)")
+    p.add_argument("--workers", type=int, default=0, help="balanced workers (0 = default)")
     p.add_argument("--layers", type=int, default=0, help="layer pools to rotate (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -129,18 +132,16 @@ def main():
     pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(layers - 1)]
     knew, vnew, slots = dev(case.k_new), dev(case.v_new), dev(case.slot_mapping)
     out = torch.empty_like(q)
-    ws = None
-    if args.partition:
-        nbytes = pkv.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
-                                            case.block_tables.shape[1], case.block_size,
-                                            args.partition)
-        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    nbytes = pkv.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                        case.head_dim, case.block_tables.shape[1],
+                                        case.block_size, args.mode, args.partition, args.workers)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     writes = [pkv.WriteLaunch(knew, vnew, slots, kc, vc, k_scale=case.k_scale,
                               v_scale=case.v_scale) for kc, vc in pools]
     decodes = [pkv.DecodeLaunch(out, q, kc, vc, tables, lens, case.scale, case.block_size,
-                                k_scale=case.k_scale, v_scale=case.v_scale,
+                                k_scale=case.k_scale, v_scale=case.v_scale, mode=args.mode,
                                 partition_size=args.partition, waves_per_group=args.waves,
-                                workspace=ws) for kc, vc in pools]
+                                num_workers=args.workers, workspace=ws) for kc, vc in pools]
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -221,8 +222,10 @@ def main():
             "head_dim": case.head_dim,
             "block_size": case.block_size,
             "context_tokens": int(case.context_lens.astype(np.int64).sum()),
-            "partition_size": args.partition,
-            "waves_per_group": args.waves,
+            "decode_mode": args.mode,
+            "partition_size": args.partition if args.mode == "partitioned" else None,
+            "waves_per_group": args.waves or None,
+            "num_workers": args.workers or None,
             "layer_pools": layers,
             "graph": bool(args.graph),
         },
@@ -232,8 +235,9 @@ def main():
         "decode_us": round(dec_s * 1e6, 2),
         "write_us": round(float(wr_ms.mean()) * 1e3, 2),
         "roofline": {
-            "kernel": "paged_attention_decode (partition + reduce)" if args.partition
-                      else "paged_attention_decode",
+            "kernel": {"single": "paged_attention_decode (single pass)",
+                       "partitioned": "paged_attention_decode (partitions + merge)",
+                       "balanced": "paged_attention_decode (balanced split + merge)"}[args.mode],
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,

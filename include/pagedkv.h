@@ -99,17 +99,31 @@ typedef enum {
   PKV_ERR_RANGE = 8        /* pkv_validate_*: an id, length or slot is out of range */
 } pkv_status;
 
+typedef enum {
+  /* one workgroup per (sequence, KV head) walks the whole context */
+  PKV_DECODE_SINGLE_PASS = 0,
+  /* split-K: one workgroup per (partition of partition_size tokens, KV head,
+     sequence); partial softmax states go to the workspace and a merge kernel
+     combines a sequence's partitions in partition order (sequences that fit
+     in one partition are finalised in place) */
+  PKV_DECODE_PARTITIONED = 1,
+  /* balanced split: the 16-token tiles of all (sequence, KV head) pairs are
+     flattened and num_workers wavefronts each take an equal contiguous run,
+     so all of them stream the same number of bytes whatever the spread of
+     context lengths; a pair covered by several runs is merged from the
+     workspace in run order */
+  PKV_DECODE_BALANCED = 2
+} pkv_decode_mode;
+
 typedef struct {
-  /* 0: one workgroup per (sequence, KV head) walks the whole context.
-     > 0: split-K; each workgroup covers `partition_size` tokens (a multiple of
-     16), writes its partial softmax state to the workspace, and a reduce kernel
-     merges the partitions in a fixed order.  Sequences that fit in one
-     partition skip the reduce. */
-  int32_t partition_size;
-  /* wavefronts per workgroup, each walking a disjoint subset of the tiles:
-     0 = library default, else 1, 2, 4 or 8 */
-  int32_t waves_per_group;
-  void* workspace;          /* device memory, >= paged_attention_decode_workspace_bytes() */
+  int32_t mode;             /* pkv_decode_mode */
+  int32_t partition_size;   /* PARTITIONED: tokens per partition, a positive multiple of 16 */
+  int32_t waves_per_group;  /* SINGLE_PASS / PARTITIONED: wavefronts per workgroup walking
+                               disjoint tiles: 0 = library default, else 1, 2, 4 or 8 */
+  int32_t num_workers;      /* BALANCED: wavefronts sharing the work; 0 = library default
+                               (4 per compute unit of the current device) */
+  void* workspace;          /* device memory, >= paged_attention_decode_workspace_bytes();
+                               not needed for SINGLE_PASS */
   size_t workspace_bytes;
 } pkv_decode_opts;
 
@@ -156,7 +170,7 @@ pkv_status paged_kv_write(const pkv_tensor* k, const pkv_tensor* v,
  *   K/V rows read through the table; len == 0 gives zeros.  Slots past len and
  *   blocks not listed may hold any bits, NaN included: they never reach out.
  * Supported: Hq % Hkv == 0 with Hq / Hkv <= 16, D in {64, 128}, block_size a
- * multiple of 16 up to 256, partition_size 0 or a positive multiple of 16.
+ * multiple of 16 up to 256.
  * Results are deterministic and do not depend on which physical blocks hold
  * the tokens.
  * Errors: PKV_ERR_NULL, PKV_ERR_DTYPE, PKV_ERR_SHAPE, PKV_ERR_LAYOUT,
@@ -169,11 +183,13 @@ pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q,
                                   int32_t block_size, const pkv_decode_opts* opts,
                                   void* hip_stream);
 
-/* Workspace bytes split-K needs for these sizes (0 when partition_size == 0).
- * Returns 0 as well for invalid arguments (negative sizes). */
+/* Workspace bytes paged_attention_decode needs with these sizes and options
+ * (0 when none is needed: single pass, or one partition per sequence).
+ * Returns 0 as well for invalid arguments. */
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                              int32_t head_dim, int32_t max_blocks_per_seq,
-                                              int32_t block_size, int32_t partition_size);
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              const pkv_decode_opts* opts);
 
 /*
  * Opt-in host-side checks of the caller contract, on HOST copies.

@@ -45,11 +45,29 @@ class PkvTensor(ctypes.Structure):
 
 class PkvDecodeOpts(ctypes.Structure):
     _fields_ = [
+        ("mode", ctypes.c_int32),
         ("partition_size", ctypes.c_int32),
         ("waves_per_group", ctypes.c_int32),
+        ("num_workers", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
+
+
+DECODE_MODES = {"single": 0, "partitioned": 1, "balanced": 2}
+
+
+def decode_opts(mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
+                num_workers: int = 0) -> PkvDecodeOpts:
+    """Options struct; mode None means "partitioned" if partition_size > 0 else "single"."""
+    if mode is None:
+        mode = "partitioned" if partition_size > 0 else "single"
+    o = PkvDecodeOpts()
+    o.mode = DECODE_MODES[mode]
+    o.partition_size = int(partition_size)
+    o.waves_per_group = int(waves_per_group)
+    o.num_workers = int(num_workers)
+    return o
 
 
 _lib = None
@@ -73,7 +91,8 @@ def load():
     lib.paged_attention_decode.argtypes = [T, T, T, T, T, T, ctypes.c_float, ctypes.c_int32,
                                            ctypes.POINTER(PkvDecodeOpts), P]
     lib.paged_attention_decode.restype = ctypes.c_int
-    lib.paged_attention_decode_workspace_bytes.argtypes = [ctypes.c_int32] * 6
+    lib.paged_attention_decode_workspace_bytes.argtypes = [ctypes.c_int32] * 6 + [
+        ctypes.POINTER(PkvDecodeOpts)]
     lib.paged_attention_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pkv_validate_slots.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
     lib.pkv_validate_slots.restype = ctypes.c_int
@@ -145,33 +164,42 @@ def paged_kv_write(k, v, slot_mapping, key_cache, value_cache, *, k_scale: float
                                  ctypes.byref(dkc), ctypes.byref(dvc), _stream(k, stream)))
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
-                           max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_blocks_per_seq: int, block_size: int, mode: str | None = None,
+                           partition_size: int = 0, num_workers: int = 0) -> int:
+    o = decode_opts(mode, partition_size, 0, num_workers)
     return int(load().paged_attention_decode_workspace_bytes(
-        num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size))
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+        ctypes.byref(o)))
+
+
+def _workspace_for(opts: PkvDecodeOpts, q, key_cache, block_tables, block_size, workspace):
+    import torch
+    need = int(load().paged_attention_decode_workspace_bytes(
+        q.shape[0], q.shape[1], key_cache.shape[1], q.shape[2], block_tables.shape[1],
+        block_size, ctypes.byref(opts)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel() * workspace.element_size()
+    return workspace
 
 
 def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context_lens,
                            scale: float, block_size: int, *, k_scale: float = 1.0,
-                           v_scale: float = 1.0, partition_size: int = 0,
-                           waves_per_group: int = 0, workspace=None, stream=None):
+                           v_scale: float = 1.0, mode: str | None = None, partition_size: int = 0,
+                           waves_per_group: int = 0, num_workers: int = 0, workspace=None,
+                           stream=None):
     """Decode attention over the paged pools into ``out`` [S, Hq, D].
 
-    partition_size > 0 selects split-K; ``workspace`` (a uint8 device tensor of
-    at least decode_workspace_bytes(...)) is allocated here when not given."""
-    import torch
+    mode: "single", "partitioned" (needs partition_size) or "balanced"; None
+    picks "partitioned" when partition_size > 0, else "single".  The split
+    modes need a workspace (a uint8 device tensor of at least
+    decode_workspace_bytes(...)); it is allocated here when not given."""
     _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
-    opts = PkvDecodeOpts()
-    opts.partition_size = int(partition_size)
-    opts.waves_per_group = int(waves_per_group)
-    if partition_size > 0:
-        need = decode_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], block_tables.shape[1],
-                                      block_size, partition_size)
-        if workspace is None and need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        if workspace is not None:
-            opts.workspace = workspace.data_ptr()
-            opts.workspace_bytes = workspace.numel() * workspace.element_size()
+    opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
+    ws = _workspace_for(opts, q, key_cache, block_tables, block_size, workspace)
     dout, dq = describe(out), describe(q)
     dkc, dvc = describe(key_cache, k_scale), describe(value_cache, v_scale)
     dt, dl = describe(block_tables), describe(context_lens)
@@ -179,6 +207,8 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
         ctypes.byref(dout), ctypes.byref(dq), ctypes.byref(dkc), ctypes.byref(dvc),
         ctypes.byref(dt), ctypes.byref(dl), float(scale), int(block_size), ctypes.byref(opts),
         _stream(q, stream)))
+    if ws is not None and workspace is None and stream is not None:
+        ws.record_stream(stream)
     return out
 
 
@@ -227,21 +257,12 @@ class DecodeLaunch:
 
     def __init__(self, out, q, key_cache, value_cache, block_tables, context_lens, scale: float,
                  block_size: int, *, k_scale: float = 1.0, v_scale: float = 1.0,
-                 partition_size: int = 0, waves_per_group: int = 0, workspace=None):
-        import torch
+                 mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
+                 num_workers: int = 0, workspace=None):
         _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
-        self._opts = PkvDecodeOpts()
-        self._opts.partition_size = int(partition_size)
-        self._opts.waves_per_group = int(waves_per_group)
-        if partition_size > 0:
-            need = decode_workspace_bytes(q.shape[0], q.shape[1], q.shape[2],
-                                          block_tables.shape[1], block_size, partition_size)
-            if workspace is None and need > 0:
-                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            if workspace is not None:
-                self._opts.workspace = workspace.data_ptr()
-                self._opts.workspace_bytes = workspace.numel() * workspace.element_size()
-        self.workspace = workspace
+        self._opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
+        self.workspace = _workspace_for(self._opts, q, key_cache, block_tables, block_size,
+                                        workspace)
         self._keep = (out, q, key_cache, value_cache, block_tables, context_lens)
         self._d = [describe(out), describe(q), describe(key_cache, k_scale),
                    describe(value_cache, v_scale), describe(block_tables), describe(context_lens)]

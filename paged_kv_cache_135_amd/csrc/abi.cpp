@@ -96,6 +96,78 @@ int64_t num_partitions(int64_t max_blocks, int64_t block_size, int64_t partition
   return np < 1 ? 1 : np;
 }
 
+// Default balanced worker count: 4 wavefronts per compute unit of the
+// current device (cached per device).
+int32_t default_workers() {
+  static int32_t cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = 4 * cus;
+  }
+  return cache[dev];
+}
+
+// Launch plan derived from the options and sizes.
+struct Plan {
+  int32_t mode = PKV_DECODE_SINGLE_PASS;
+  int64_t partitions = 1;   // PARTITIONED
+  int64_t part_tiles = 1;
+  int32_t waves = 4;
+  int32_t workers = 0;      // BALANCED
+  size_t workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D) const {
+    if (mode == PKV_DECODE_PARTITIONED && partitions > 1) return (size_t)(S * Hq * partitions * (D + 2));
+    if (mode == PKV_DECODE_BALANCED) return (size_t)((workers + S * Hkv) * (Hq / Hkv) * (D + 2));
+    return 0;
+  }
+  size_t meta_bytes(int64_t S, int64_t Hkv) const {
+    return mode == PKV_DECODE_BALANCED ? (size_t)(S * Hkv * 2 * 4) : 0;
+  }
+};
+
+pkv_status plan(const pkv_decode_opts* opts, int64_t S, int64_t Hq, int64_t Hkv, int64_t maxb,
+                int64_t bs, Plan* p) {
+  (void)Hq;
+  (void)Hkv;
+  const int32_t mode = opts ? opts->mode : PKV_DECODE_SINGLE_PASS;
+  const int32_t waves = opts ? opts->waves_per_group : 0;
+  p->mode = mode;
+  p->waves = waves == 0 ? 4 : waves;
+  if (p->waves != 1 && p->waves != 2 && p->waves != 4 && p->waves != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "waves_per_group %d: must be 0, 1, 2, 4 or 8", waves);
+  const int64_t max_tiles = (maxb * bs + 15) / 16;
+  switch (mode) {
+    case PKV_DECODE_SINGLE_PASS:
+      p->partitions = 1;
+      p->part_tiles = max_tiles > 0 ? max_tiles : 1;
+      return PKV_OK;
+    case PKV_DECODE_PARTITIONED: {
+      const int32_t part = opts->partition_size;
+      if (part <= 0 || part % 16 != 0)
+        return fail(PKV_ERR_UNSUPPORTED, "partition_size %d: must be a positive multiple of 16", part);
+      p->partitions = num_partitions(maxb, bs, part);
+      if (p->partitions > 65535 * 16384LL)
+        return fail(PKV_ERR_UNSUPPORTED, "too many partitions");
+      p->part_tiles = p->partitions > 1 ? part / 16 : (max_tiles > 0 ? max_tiles : 1);
+      return PKV_OK;
+    }
+    case PKV_DECODE_BALANCED: {
+      const int32_t wk = opts->num_workers;
+      if (wk < 0 || wk > (1 << 24))
+        return fail(PKV_ERR_UNSUPPORTED, "num_workers %d: must be in [0, 2^24]", wk);
+      p->workers = wk == 0 ? default_workers() : wk;
+      if (S * Hkv > INT32_MAX / 2) return fail(PKV_ERR_UNSUPPORTED, "too many (sequence, KV head) pairs");
+      return PKV_OK;
+    }
+    default:
+      return fail(PKV_ERR_UNSUPPORTED, "unknown decode mode %d", mode);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,14 +239,16 @@ pkv_status paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_te
 }
 
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                              int32_t head_dim, int32_t max_blocks_per_seq,
-                                              int32_t block_size, int32_t partition_size) {
-  if (num_seqs < 0 || num_q_heads < 0 || head_dim < 0 || max_blocks_per_seq < 0 ||
-      block_size < 0 || partition_size < 0)
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              const pkv_decode_opts* opts) {
+  if (num_seqs < 0 || num_q_heads < 0 || num_kv_heads <= 0 || head_dim < 0 ||
+      max_blocks_per_seq < 0 || block_size < 0 || num_q_heads % num_kv_heads != 0)
     return 0;
-  const int64_t np = num_partitions(max_blocks_per_seq, block_size, partition_size);
-  if (np <= 1) return 0;
-  return (size_t)num_seqs * (size_t)num_q_heads * (size_t)np * ((size_t)head_dim + 2) * 4u;
+  Plan p;
+  if (plan(opts, num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size, &p) != PKV_OK)
+    return 0;
+  return p.workspace_floats(num_seqs, num_q_heads, num_kv_heads, head_dim) * 4u + p.meta_bytes(num_seqs, num_kv_heads);
 }
 
 pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q, const pkv_tensor* key_cache,
@@ -232,29 +306,24 @@ pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q, const pk
   for (const pkv_tensor* t : inputs)
     if (overlap(out, t)) return fail(PKV_ERR_LAYOUT, "out overlaps an input");
 
-  int32_t part = opts ? opts->partition_size : 0;
-  int32_t waves = opts ? opts->waves_per_group : 0;
-  if (part < 0 || part % 16 != 0)
-    return fail(PKV_ERR_UNSUPPORTED, "partition_size %d: must be 0 or a positive multiple of 16", part);
-  if (waves == 0) waves = 4;
-  if (waves != 1 && waves != 2 && waves != 4 && waves != 8)
-    return fail(PKV_ERR_UNSUPPORTED, "waves_per_group %d: must be 0, 1, 2, 4 or 8", waves);
-
-  const int64_t max_tiles = (maxb * bs + 15) / 16;
-  const int64_t np = num_partitions(maxb, bs, part);
-  const int64_t part_tiles = np > 1 ? part / 16 : (max_tiles > 0 ? max_tiles : 1);
+  Plan p;
+  PKV_TRY(plan(opts, S, Hq, Hkv, maxb, bs, &p));
   pkv::DecodeArgs a{};
-  if (np > 1) {
-    const size_t need = paged_attention_decode_workspace_bytes((int32_t)S, (int32_t)Hq, (int32_t)D,
-                                                               (int32_t)maxb, (int32_t)bs, part);
+  const size_t need = p.workspace_floats(S, Hq, Hkv, D) * 4u + p.meta_bytes(S, Hkv);
+  if (need > 0) {
     if (!opts->workspace || opts->workspace_bytes < need)
-      return fail(PKV_ERR_WORKSPACE, "split-K needs a workspace of %zu bytes (got %zu)", need,
+      return fail(PKV_ERR_WORKSPACE, "this decode mode needs a workspace of %zu bytes (got %zu)", need,
                   opts->workspace ? opts->workspace_bytes : (size_t)0);
     if (reinterpret_cast<uintptr_t>(opts->workspace) % 16 != 0)
       return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-    if (np > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "too many partitions");
     a.ws_acc = static_cast<float*>(opts->workspace);
-    a.ws_ml = a.ws_acc + (size_t)S * Hq * np * D;
+    if (p.mode == PKV_DECODE_BALANCED) {
+      const size_t slots = (size_t)p.workers + (size_t)S * Hkv;
+      a.ws_ml = a.ws_acc + slots * (Hq / Hkv) * D;
+      a.ws_meta = reinterpret_cast<int32_t*>(a.ws_ml + slots * (Hq / Hkv) * 2);
+    } else {
+      a.ws_ml = a.ws_acc + (size_t)S * Hq * p.partitions * D;
+    }
   }
   if (S == 0) return ok();
 
@@ -271,9 +340,12 @@ pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q, const pk
   a.head_dim = (int32_t)D;
   a.block_size = (int32_t)bs;
   a.max_blocks = (int32_t)maxb;
-  a.part_tiles = (int32_t)part_tiles;
-  a.num_parts = (int32_t)np;
-  a.waves = waves;
+  a.part_tiles = (int32_t)p.part_tiles;
+  a.num_parts = (int32_t)p.partitions;
+  a.waves = p.waves;
+  a.mode = p.mode == PKV_DECODE_BALANCED ? pkv::kBalanced
+           : p.mode == PKV_DECODE_PARTITIONED ? pkv::kPartitioned : pkv::kSinglePass;
+  a.num_workers = p.workers;
   a.cache_dtype = ct;
   const double log2e = 1.4426950408889634;
   const double kscale = ct == PKV_FP8_E4M3 ? (double)key_cache->scale : 1.0;

@@ -45,7 +45,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+#ifndef PKV_DECODE_RING
+#define PKV_DECODE_RING 2
+#endif
+
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kChunkTiles = 1024;  // block ids staged in LDS per pass (4 KiB)
 constexpr uint32_t kSelLo = 0x05040100u;  // v_perm: low halves of two dwords
 constexpr uint32_t kSelHi = 0x07060302u;  // v_perm: high halves of two dwords
 
@@ -307,12 +312,61 @@ __device__ __forceinline__ void store_run(void* out, int64_t idx, const float* x
   }
 }
 
-template <int CT, int D, int NW>
+// Max over the four lanes l, l^16, l^32, l^48 (the lanes holding one head's
+// scores) with the gfx950 row-swap permutes: VALU only, no LDS round trip.
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Online-softmax state of one wavefront: per lane, head g = lane % 16.
+template <int VE>
+struct Softmax {
+  float m = kNegInf;  // running max (log2 units), identical in the 4 lane groups
+  float l = 0.f;      // this lane's share of the running sum
+  f32x4 acc[VE];
+};
+
+// One 16-token tile: scores, masking of tokens >= ctx, online-softmax update, P.V.
+template <int CT, int D>
+__device__ __forceinline__ void process_tile(Tile<CT, D>& t, const typename Tile<CT, D>::QFrag& qf,
+                                             Softmax<D / 16>& st, int t0, int ctx, float qk_scale,
+                                             int lane) {
+  constexpr int VE = D / 16;
+  const f32x4 sacc = t.scores(qf);
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * qk_scale;
+  if (t0 + 16 > ctx) {  // ragged last tile: drop tokens >= ctx by select
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ok[i] = t0 + 4 * (lane >> 4) + i < ctx;
+      sc[i] = ok[i] ? sc[i] : kNegInf;
+    }
+    t.mask_rows(ok);
+  }
+  const float bm = max_over_lane_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+  const float m_new = fmaxf(st.m, bm);  // finite: every tile holds >= 1 live token
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+#pragma unroll
+  for (int r = 0; r < VE; ++r) st.acc[r] *= alpha;
+  st.l = st.l * alpha + t.pv(p, st.acc);
+  st.m = m_new;
+}
+
+template <int CT, int D, int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a) {
   using T = Tile<CT, D>;
   constexpr int VE = T::VE;
   const int part = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int ctx = a.lens[s];
   const int ntiles = (ctx + 15) >> 4;
   const int tile_begin = part * a.part_tiles;
@@ -333,54 +387,45 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   const int64_t head_rows = (int64_t)hk * bs;  // row offset of this KV head inside a block
   const int64_t block_rows = (int64_t)a.num_kv_heads * bs;
 
-  float m_run = kNegInf, l_run = 0.f;
-  f32x4 acc[VE];
+  Softmax<VE> st;
 #pragma unroll
-  for (int r = 0; r < VE; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < VE; ++r) st.acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Software pipeline: the next tile's loads are in flight while this tile is
-  // computed.  Past the end the load repeats the wave's last tile (in bounds,
-  // result unused) so every iteration issues the same loads.
-  T cur, nxt;
-  int tile = tile_begin + wave;
-  auto row_of = [&](int t_idx) -> int64_t {
-    const int t0 = t_idx * 16;
-    const int32_t blk = table[t0 / bs];
-    return (int64_t)blk * block_rows + head_rows + (t0 % bs);
-  };
-  if (tile < tile_end) cur.load(a.kc, a.vc, row_of(tile), lane);
-  for (; tile < tile_end; tile += NW) {
-    const int nt = tile + NW < tile_end ? tile + NW : tile;
-    nxt.load(a.kc, a.vc, row_of(nt), lane);
-
-    const int t0 = tile * 16;
-    const f32x4 sacc = cur.scores(qf);
-    float sc[4];
+  // The partition's tiles are taken in chunks of up to kChunkTiles.  For each
+  // chunk the workgroup first copies the block id of every tile into LDS (one
+  // cooperative pass over the table), so inside the loop an address costs an
+  // LDS read, whose wait does not touch the in-flight K/V loads.  Wave w takes
+  // tiles c0 + w + NW*k.  Past the wave's last tile, indices clamp to it (in
+  // bounds, result unused), so every batch issues the same loads.
+  __shared__ int32_t sm_blk[kChunkTiles];
+  for (int c0 = tile_begin; c0 < tile_end; c0 += kChunkTiles) {
+    const int c1 = min(tile_end, c0 + kChunkTiles);
+    if (c0 > tile_begin) __syncthreads();  // every wave is done with the previous chunk
+    for (int i = threadIdx.x; i < c1 - c0; i += NW * 64) sm_blk[i] = table[((c0 + i) * 16) / bs];
+    __syncthreads();
+    const int first = c0 + wave;
+    const int n_my = first < c1 ? (c1 - first + NW - 1) / NW : 0;
+    auto tile_of = [&](int k) { return first + NW * min(k, n_my - 1); };
+    auto row_of = [&](int k) {
+      const int t = tile_of(k);
+      return (int64_t)sm_blk[t - c0] * block_rows + head_rows + ((t * 16) % bs);
+    };
+    // Batches of NBUF tiles: all their loads are issued back to back, then the
+    // tiles are computed in order, each waiting only for its own loads.  No
+    // load is in flight across the loop's back edge.
+    for (int k = 0; k < n_my; k += NBUF) {
+      T buf[NBUF];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * a.qk_scale;
-    if (t0 + 16 > ctx) {  // ragged last tile: drop tokens >= ctx by select
-      bool ok[4];
+      for (int j = 0; j < NBUF; ++j) buf[j].load(a.kc, a.vc, row_of(k + j), lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ok[i] = t0 + 4 * (lane >> 4) + i < ctx;
-        sc[i] = ok[i] ? sc[i] : kNegInf;
+      for (int j = 0; j < NBUF; ++j) {
+        if (k + j >= n_my) break;
+        process_tile<CT, D>(buf[j], qf, st, tile_of(k + j) * 16, ctx, a.qk_scale, lane);
       }
-      cur.mask_rows(ok);
     }
-    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);  // finite: every tile holds >= 1 live token
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
-#pragma unroll
-    for (int r = 0; r < VE; ++r) acc[r] *= alpha;
-    l_run = l_run * alpha + cur.pv(p, acc);
-    m_run = m_new;
-    cur = nxt;
   }
+  float m_run = st.m, l_run = st.l;
+  f32x4* acc = st.acc;
   // per-lane sums cover tokens 4*(lane/16)+i only; add the four lane groups
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -486,10 +531,276 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced split.  The work of one call is the flattened list of tiles of all
+// segments (sequence s, KV head h) in (s, h, tile) order.  num_workers
+// wavefronts each take an equal contiguous run of it, so every wavefront
+// streams the same number of bytes and they finish together, whatever the
+// spread of context lengths.  A run covers parts of one or more segments; a
+// segment covered by a single run is finalised in place, otherwise each run's
+// piece leaves its partial state in slot (worker + segment) and the merge
+// kernel combines the pieces in worker order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <int CT, int D>
+__device__ void write_zero_rows(const DecodeArgs& a, int s, int lane) {
+  constexpr int EB = CT == PKV_F32 ? 4 : 2;
+  char* o = static_cast<char*>(a.out) + (int64_t)s * a.num_q_heads * D * EB;
+  const int n16 = a.num_q_heads * D * EB / 16;
+  for (int i = lane; i < n16; i += 64) reinterpret_cast<u32x4*>(o)[i] = u32x4{0, 0, 0, 0};
+}
+
+template <int CT, int D, int NBUF>
+__global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void decode_balanced_kernel(DecodeArgs a) {
+  using T = Tile<CT, D>;
+  constexpr int VE = T::VE;
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = a.num_workers;
+  if (w >= W) return;
+  const int S = a.num_seqs, Hkv = a.num_kv_heads, G = a.group, bs = a.block_size;
+
+  // Tile counts of up to kScanRegs * 64 sequences stay in registers (lane l
+  // holds sequences l, l+64, ...); longer batches re-read the lengths.
+  // Sequences with no tokens have no tiles: worker s % W writes their zero rows.
+  constexpr int kScanRegs = 8;
+  uint32_t nreg[kScanRegs];
+  int64_t total = 0;
+  for (int c = 0, r = 0; c < S; c += 64, ++r) {
+    const int s = c + lane;
+    const int ctx = s < S ? a.lens[s] : 0;
+    const uint32_t n = (uint32_t)((ctx + 15) >> 4);
+    if (r < kScanRegs) nreg[r] = n;
+    total += wave_sum(n);
+    uint64_t zmask = __ballot(s < S && ctx == 0 && s % W == w);
+    while (zmask) {
+      const int l = __builtin_ctzll(zmask);
+      zmask &= zmask - 1;
+      write_zero_rows<CT, D>(a, c + l, lane);
+      if (lane < Hkv) {
+        a.ws_meta[2 * ((int64_t)(c + l) * Hkv + lane)] = -1;
+        a.ws_meta[2 * ((int64_t)(c + l) * Hkv + lane) + 1] = -1;
+      }
+      for (int h = 64; h < Hkv; ++h) {  // more than 64 KV heads: rest by lane 0
+        if (lane == 0) {
+          a.ws_meta[2 * ((int64_t)(c + l) * Hkv + h)] = -1;
+          a.ws_meta[2 * ((int64_t)(c + l) * Hkv + h) + 1] = -1;
+        }
+      }
+    }
+  }
+  total *= Hkv;
+  if (total == 0) return;
+  const int64_t chunk = (total + W - 1) / W;
+  const int64_t x0 = (int64_t)w * chunk;
+  const int64_t x1 = min(total, x0 + chunk);
+  if (x0 >= x1) return;
+
+  // Sequence holding tile x0, and the tiles before it.
+  int s_cur = 0;
+  int64_t p_cur = 0;
+  {
+    int64_t base = 0;
+    for (int c = 0, r = 0; c < S; c += 64, ++r) {
+      const int s = c + lane;
+      uint32_t n;
+      if (r < kScanRegs) n = nreg[r];
+      else n = s < S ? (uint32_t)((a.lens[s] + 15) >> 4) : 0u;
+      const uint32_t incl = wave_incl_scan(n, lane);
+      const int64_t tot = (int64_t)Hkv * __shfl(incl, 63);
+      if (x0 < base + tot) {
+        const uint64_t hit = __ballot(x0 < base + (int64_t)Hkv * incl);
+        const int l = __builtin_ctzll(hit);
+        s_cur = c + l;
+        p_cur = base + (int64_t)Hkv * __shfl(incl - n, l);
+        break;
+      }
+      base += tot;
+    }
+  }
+
+  const int g = lane & 15;
+  const bool g_ok = g < G;
+  int64_t x = x0;
+  int32_t carry = 0;      // first-batch block ids of the next piece, loaded ahead
+  bool has_carry = false;
+  while (x < x1 && s_cur < S) {
+    const int ctx = a.lens[s_cur];
+    const int n = (ctx + 15) >> 4;
+    if (n == 0) {
+      ++s_cur;
+      continue;
+    }
+    const int64_t rel = x - p_cur;
+    const int h = (int)(rel / n);
+    if (h >= Hkv) break;  // cannot happen: x lies inside sequence s_cur's tiles
+    const int tl = (int)(rel - (int64_t)h * n);
+    const int te = (int)min((int64_t)n, tl + (x1 - x));
+    const int seg = s_cur * Hkv + h;
+
+    const int qh = h * G + g;
+    const QElem<CT>* qrow = static_cast<const QElem<CT>*>(a.q) +
+                            ((int64_t)s_cur * a.num_q_heads + (g_ok ? qh : 0)) * D;
+    const typename T::QFrag qf = T::load_q(qrow, g_ok, lane);
+    const int32_t* table = a.tables + (int64_t)s_cur * a.max_blocks;
+    const int64_t head_rows = (int64_t)h * bs;
+    const int64_t block_rows = (int64_t)Hkv * bs;
+
+    Softmax<VE> st;
+#pragma unroll
+    for (int r = 0; r < VE; ++r) st.acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Block ids of the next batch arrive one batch ahead (lane j holds tile k+j);
+    // tiles past the piece clamp to its last tile (in bounds, result unused).
+    auto entry = [&](int t) { return table[(min(t, te - 1) * 16) / bs]; };
+    int32_t ent_next = has_carry ? carry : (lane < NBUF ? entry(tl + lane) : 0);
+    // When the run goes on with the next KV head of this sequence, that piece
+    // starts at tile 0 of the same table row: fetch its first block ids now.
+    const int64_t after = x + (te - tl);
+    has_carry = te == n && h + 1 < Hkv && after < x1;
+    const int te_next = has_carry ? (int)min((int64_t)n, x1 - after) : 1;
+    for (int k = tl; k < te; k += NBUF) {
+      const int32_t ent = ent_next;
+      ent_next = lane < NBUF ? entry(k + NBUF + lane) : 0;
+      if (has_carry && k == tl) carry = lane < NBUF ? table[(min(lane, te_next - 1) * 16) / bs] : 0;
+      T buf[NBUF];
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        const int t = min(k + j, te - 1);
+        const int32_t blk = __builtin_amdgcn_readlane(ent, j);
+        buf[j].load(a.kc, a.vc, (int64_t)blk * block_rows + head_rows + ((t * 16) % bs), lane);
+      }
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        if (k + j >= te) break;
+        process_tile<CT, D>(buf[j], qf, st, (k + j) * 16, ctx, a.qk_scale, lane);
+      }
+    }
+    float l_run = st.l;
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+
+    const bool whole = tl == 0 && te == n;
+    if (whole || te == n) {
+      // the segment's last piece records where its pieces are
+      if (lane == 0) {
+        const int64_t seg_start = p_cur + (int64_t)h * n;
+        a.ws_meta[2 * (int64_t)seg] = whole ? -1 : (int32_t)(seg_start / chunk);
+        a.ws_meta[2 * (int64_t)seg + 1] = whole ? -1 : w;
+      }
+    }
+    if (g_ok) {
+      if (whole) {
+        const int64_t row = (int64_t)s_cur * a.num_q_heads + qh;
+        const float inv = a.v_scale / l_run;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float xo[VE];
+#pragma unroll
+          for (int r = 0; r < VE; ++r) xo[r] = st.acc[r][i] * inv;
+          store_run<CT, VE>(a.out, row * D + VE * (4 * (lane >> 4) + i), xo);
+        }
+      } else {
+        const int64_t slot = (int64_t)w + seg;
+        float* o = a.ws_acc + (slot * G + g) * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q4 = 0; q4 < VE / 4; ++q4)
+            *reinterpret_cast<f32x4*>(o + VE * (4 * (lane >> 4) + i) + 4 * q4) =
+                f32x4{st.acc[4 * q4][i], st.acc[4 * q4 + 1][i], st.acc[4 * q4 + 2][i],
+                      st.acc[4 * q4 + 3][i]};
+        if (lane < 16) *reinterpret_cast<f32x2*>(a.ws_ml + (slot * G + g) * 2) = f32x2{st.m, l_run};
+      }
+    }
+    x += te - tl;
+    if (te == n && h == Hkv - 1) {
+      p_cur += (int64_t)Hkv * n;
+      ++s_cur;
+    }
+  }
+}
+
+// Merge the pieces of one segment (sequence, KV head) for one query head.
+// One wavefront: lanes first take the pieces' (max, sum) pairs (pieces
+// strided over lanes) for the common max M and the total L; then lane
+// (group p4 = lane / 16, column chunk c = lane % 16) sums pieces p4, p4+4, ...
+// over its D/16 columns, and the four groups are added in a fixed order.
+template <int CT, int D>
+__global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a) {
+  constexpr int VE = D / 16;
+  const int seg = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+  const int w0 = a.ws_meta[2 * (int64_t)seg], w1 = a.ws_meta[2 * (int64_t)seg + 1];
+  if (w0 < 0) return;
+  const int G = a.group;
+  const int np = w1 - w0 + 1;
+  const int64_t slot0 = (int64_t)w0 + seg;
+  auto ml = [&](int p) { return a.ws_ml + ((slot0 + p) * G + g) * 2; };
+
+  float M = kNegInf;
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml(p)[0]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float L = 0.f;
+  for (int p = lane; p < np; p += 64) L += __builtin_amdgcn_exp2f(ml(p)[0] - M) * ml(p)[1];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+
+  const int p4 = lane >> 4, c = lane & 15;
+  float o[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) o[e] = 0.f;
+  for (int p = p4; p < np; p += 4) {
+    const float f = __builtin_amdgcn_exp2f(ml(p)[0] - M);
+    const float* src = a.ws_acc + ((slot0 + p) * G + g) * D + VE * c;
+#pragma unroll
+    for (int q = 0; q < VE / 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q);
+      o[4 * q] += f * v[0];
+      o[4 * q + 1] += f * v[1];
+      o[4 * q + 2] += f * v[2];
+      o[4 * q + 3] += f * v[3];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    o[e] += __shfl_xor(o[e], 16);
+    o[e] += __shfl_xor(o[e], 32);
+  }
+  if (p4 != 0) return;
+  const float inv = a.v_scale / L;
+  const int s = seg / a.num_kv_heads, h = seg - s * a.num_kv_heads;
+  float x[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) x[e] = o[e] * inv;
+  store_run<CT, VE>(a.out, ((int64_t)s * a.num_q_heads + h * G + g) * D + VE * c, x);
+}
+
+// Tiles loaded per batch.  More tiles put more bytes in flight per wavefront
+// but cost VGPRs (32 per bf16 D=128 tile) and occupancy.
+template <int CT, int D>
+constexpr int ring_depth() {
+  return PKV_DECODE_RING;
+}
+
 template <int CT, int D, int NW>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW>), grid, dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, ring_depth<CT, D>()>), grid, dim3(NW * 64),
+                     0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_parts == 1) return e;
   const dim3 rgrid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
@@ -498,7 +809,20 @@ hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
 }
 
 template <int CT, int D>
+hipError_t launch_balanced(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.num_workers + 3) / 4));
+  hipLaunchKernelGGL((decode_balanced_kernel<CT, D, ring_depth<CT, D>()>), grid, dim3(256), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 mgrid((unsigned)(a.num_seqs * a.num_kv_heads), (unsigned)a.group);
+  hipLaunchKernelGGL((decode_balanced_merge_kernel<CT, D>), mgrid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int CT, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  if (a.mode == kBalanced) return launch_balanced<CT, D>(a, stream);
   switch (a.waves) {
     case 1: return launch_nw<CT, D, 1>(a, stream);
     case 2: return launch_nw<CT, D, 2>(a, stream);

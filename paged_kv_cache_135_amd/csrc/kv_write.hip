@@ -60,14 +60,15 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(WriteArgs a, int tok
     const int h = r2 / per_row;
     const int c = r2 - h * per_row;
     const int64_t t = tok0 + tl;
+    // the source chunk does not depend on the slot: both loads go out together
+    const int64_t src = (t * H + h) * (int64_t)D + (int64_t)c * kPerChunk;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(
+        static_cast<const char*>(is_v ? a.v : a.k) + src * kInBytes);
     const int32_t slot = a.slots[t];
     if (slot < 0) continue;
     const int32_t blk = slot / bs;
     const int32_t off = slot - blk * bs;
-    const int64_t src = (t * H + h) * (int64_t)D + (int64_t)c * kPerChunk;
     const int64_t dst = (((int64_t)blk * H + h) * bs + off) * (int64_t)D + (int64_t)c * kPerChunk;
-    const u32x4 x = *reinterpret_cast<const u32x4*>(
-        static_cast<const char*>(is_v ? a.v : a.k) + src * kInBytes);
     if constexpr (OUT == IN) {
       *reinterpret_cast<u32x4*>(static_cast<char*>(is_v ? a.vc : a.kc) + dst * kInBytes) = x;
     } else {

@@ -25,7 +25,9 @@ struct WriteArgs {
   float inv_v;
 };
 
-// One decode call (partition kernel + optional reduce).
+enum DecodeMode : int32_t { kSinglePass = 0, kPartitioned = 1, kBalanced = 2 };
+
+// One decode call (partition or balanced kernel + optional reduce).
 struct DecodeArgs {
   const void* q;
   void* out;
@@ -33,8 +35,12 @@ struct DecodeArgs {
   const void* vc;
   const int32_t* tables;
   const int32_t* lens;
-  float* ws_acc;        // [S][Hq][NP][D] unnormalised partial outputs
-  float* ws_ml;         // [S][Hq][NP][2] partial running max (log2 units) and sum
+  // split workspace.  Partitioned: [S][Hq][NP][D] and [S][Hq][NP][2].
+  // Balanced: slot = worker + segment, [slots][G][D] and [slots][G][2], plus
+  // per segment (sequence, KV head) the first and last worker of its partials.
+  float* ws_acc;        // unnormalised partial outputs
+  float* ws_ml;         // partial running max (log2 units) and sum
+  int32_t* ws_meta;     // balanced only: [S * Hkv][2]
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -45,6 +51,8 @@ struct DecodeArgs {
   int32_t part_tiles;   // 16-token tiles per partition (single pass: covers max_blocks)
   int32_t num_parts;    // partitions per (sequence, KV head) = grid.x
   int32_t waves;        // wavefronts per workgroup
+  int32_t mode;         // DecodeMode
+  int32_t num_workers;  // balanced: wavefronts sharing the flattened tiles
   int32_t cache_dtype;
   float qk_scale;       // scale * log2(e) (* k scale for E4M3)
   float v_scale;        // 1, or the V scale for E4M3

@@ -41,14 +41,24 @@ def test_abi_version_matches_header():
     assert B.load().pkv_abi_version() == int(m.group(1))
 
 
+def _opts(mode=0, part=0, waves=0, workers=0):
+    o = B.PkvDecodeOpts()
+    o.mode, o.partition_size, o.waves_per_group, o.num_workers = mode, part, waves, workers
+    return o
+
+
 def test_workspace_bytes():
     lib = B.load()
+    ws = lambda *a, **k: lib.paged_attention_decode_workspace_bytes(*a, ctypes.byref(_opts(**k)))
     # 8 sequences x 28 heads, 131072 tokens in 512-token partitions: 256 partitions
-    assert lib.paged_attention_decode_workspace_bytes(8, 28, 128, 8192, 16, 512) == \
-        8 * 28 * 256 * (128 + 2) * 4
-    assert lib.paged_attention_decode_workspace_bytes(8, 28, 128, 8192, 16, 0) == 0
-    assert lib.paged_attention_decode_workspace_bytes(8, 28, 128, 4, 16, 512) == 0  # one partition
-    assert lib.paged_attention_decode_workspace_bytes(-1, 28, 128, 4, 16, 512) == 0
+    assert ws(8, 28, 4, 128, 8192, 16, mode=1, part=512) == 8 * 28 * 256 * (128 + 2) * 4
+    assert ws(8, 28, 4, 128, 8192, 16, mode=0) == 0
+    assert ws(8, 28, 4, 128, 4, 16, mode=1, part=512) == 0  # one partition
+    assert ws(-1, 28, 4, 128, 4, 16, mode=1, part=512) == 0
+    assert ws(8, 28, 4, 128, 4, 16, mode=1, part=24) == 0  # invalid partition size
+    # balanced: (workers + sequences x KV heads) slots of G x (D + 2) floats, plus 2 ints per pair
+    assert ws(64, 28, 4, 128, 256, 16, mode=2, workers=2048) == (2048 + 256) * 7 * 130 * 4 + 256 * 8
+    assert lib.paged_attention_decode_workspace_bytes(64, 28, 4, 128, 256, 16, None) == 0
 
 
 # ------------------------------------------------------ descriptor validation
@@ -126,17 +136,22 @@ def test_decode_rejects_bad_block_size_and_head_dim():
 
 
 def test_decode_rejects_bad_partition_and_missing_workspace():
-    o = B.PkvDecodeOpts()
-    o.partition_size = 24
+    o = _opts(mode=1, part=24)
+    assert _decode(_decode_args(opts=o)) == 5
+    o.partition_size = 0
     assert _decode(_decode_args(opts=o)) == 5
     o.partition_size = 32  # 4 blocks * 16 = 64 tokens -> 2 partitions, workspace needed
     assert _decode(_decode_args(opts=o)) == 6
     o.workspace = FAKE + (6 << 20)
     o.workspace_bytes = 16
     assert _decode(_decode_args(opts=o)) == 6
-    o.partition_size = 0
-    o.waves_per_group = 3
-    assert _decode(_decode_args(opts=o)) == 5
+    o.workspace = FAKE + (6 << 20) + 4  # large enough but misaligned
+    o.workspace_bytes = 1 << 20
+    assert _decode(_decode_args(opts=o)) == 6
+    assert _decode(_decode_args(opts=_opts(mode=0, waves=3))) == 5
+    assert _decode(_decode_args(opts=_opts(mode=7))) == 5
+    assert _decode(_decode_args(opts=_opts(mode=2, workers=-1))) == 5
+    assert _decode(_decode_args(opts=_opts(mode=2, workers=64))) == 6  # balanced needs a workspace
 
 
 def test_decode_rejects_bad_e4m3_scale():

@@ -21,7 +21,14 @@ def _gpu():
     gu.need_gpu()
 
 
-MODES = [(0, 1), (0, 4), (0, 8), (32, 1), (64, 2), (512, 4), (256, 8)]
+MODES = [("single", 0, 1, 0), ("single", 0, 4, 0), ("single", 0, 8, 0),
+         ("partitioned", 32, 1, 0), ("partitioned", 64, 2, 0), ("partitioned", 512, 4, 0),
+         ("partitioned", 256, 8, 0), ("balanced", 0, 0, 0), ("balanced", 0, 0, 7),
+         ("balanced", 0, 0, 64), ("balanced", 0, 0, 1)]
+
+
+def _mid(m):
+    return f"{m[0]}_p{m[1]}_w{m[2]}_n{m[3]}"
 
 SMALL = {
     # name: (context lengths, Hq, Hkv, D, block_size, cache dtype)
@@ -56,13 +63,12 @@ def _prepared(name):
     return _cache[name]
 
 
-@pytest.mark.parametrize("mode", MODES, ids=lambda m: f"part{m[0]}_w{m[1]}")
+@pytest.mark.parametrize("mode", MODES, ids=_mid)
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_cases(name, mode):
     case, g, ref = _prepared(name)
-    part, waves = mode
-    got = gu.host(g.decode(partition_size=part, waves=waves))
-    gu.assert_close(got, ref, case.cache_dtype, f"{name} part={part} waves={waves}")
+    got = gu.host(g.decode_mode(mode))
+    gu.assert_close(got, ref, case.cache_dtype, f"{name} {_mid(mode)}")
     empty = case.context_lens == 0
     if empty.any():
         assert np.all(gu.as_f64(got[empty]) == 0.0)
@@ -75,19 +81,20 @@ def test_single_token_contexts_return_the_value_row_exactly():
     g = gu.GpuCase(case)
     g.fill_and_step_writes()
     kc, vc = gu.oracle_caches(case)
-    for part, waves in [(0, 1), (0, 4), (16, 2)]:
-        got = gu.host(g.decode(part, waves))
+    for m in [("single", 0, 1, 0), ("single", 0, 4, 0), ("partitioned", 16, 2, 0),
+              ("balanced", 0, 0, 5)]:
+        got = gu.host(g.decode_mode(m))
         for s in range(9):
             row = vc[case.block_tables[s, 0], :, 0, :]  # [Hkv, D] bf16 bits
             assert np.array_equal(got[s], np.repeat(row, 4, axis=0))
 
 
 # ------------------------------------------------------------ full sizes
-def _full(name, builder, part, waves, row_mask=None, tokens_mask_fn=None):
+def _full(name, builder, mode, row_mask=None, tokens_mask_fn=None):
     case = builder()
     g = gu.GpuCase(case)
     g.fill_and_step_writes()
-    got = gu.host(g.decode(partition_size=part, waves=waves))
+    got = gu.host(g.decode_mode(mode))
     tm = tokens_mask_fn(case) if tokens_mask_fn else None
     kc, vc = gu.oracle_caches(case, tokens_mask=tm)
     rm = row_mask(case) if row_mask else None
@@ -96,19 +103,22 @@ def _full(name, builder, part, waves, row_mask=None, tokens_mask_fn=None):
 
 
 def test_c1_tiny_f32_full():
-    for part, waves in [(0, 4), (32, 1)]:
-        case, got, ref, _ = _full("c1", workloads.c1_tiny_f32, part, waves)
-        gu.assert_close(got, ref, "f32", f"c1 part={part}")
+    for m in [("single", 0, 4, 0), ("partitioned", 32, 1, 0), ("balanced", 0, 0, 0),
+              ("balanced", 0, 0, 3)]:
+        case, got, ref, _ = _full("c1", workloads.c1_tiny_f32, m)
+        gu.assert_close(got, ref, "f32", f"c1 {_mid(m)}")
 
 
-@pytest.mark.parametrize("part,waves", [(0, 4), (512, 4), (256, 1)])
-def test_c2_qwen_decode_full(part, waves):
-    case, got, ref, _ = _full("c2", workloads.c2_qwen_decode, part, waves)
-    gu.assert_close(got, ref, "bf16", f"c2 part={part}")
+@pytest.mark.parametrize("mode", [("single", 0, 4, 0), ("partitioned", 512, 4, 0),
+                                  ("partitioned", 256, 1, 0), ("balanced", 0, 0, 0)], ids=_mid)
+def test_c2_qwen_decode_full(mode):
+    case, got, ref, _ = _full("c2", workloads.c2_qwen_decode, mode)
+    gu.assert_close(got, ref, "bf16", f"c2 {_mid(mode)}")
 
 
-def test_c3_shared_prefix_full():
-    case, got, ref, _ = _full("c3", workloads.c3_shared_prefix, 512, 4)
+@pytest.mark.parametrize("mode", [("partitioned", 512, 4, 0), ("balanced", 0, 0, 0)], ids=_mid)
+def test_c3_shared_prefix_full(mode):
+    case, got, ref, _ = _full("c3", workloads.c3_shared_prefix, mode)
     assert case.shared_blocks == 64
     gu.assert_close(got, ref, "bf16", "c3")
 
@@ -119,8 +129,9 @@ def test_c4_long_context_sampled_rows(bs):
         m = np.zeros((case.num_seqs, case.num_q_heads), bool)
         m[[0, case.num_seqs - 1], :] = True
         return m
+    mode = ("partitioned", 512, 4, 0) if bs == 16 else ("balanced", 0, 0, 0)
     case, got, ref, rm = _full(f"c4_bs{bs}", lambda: workloads.c4_long_context(block_size=bs),
-                               512, 4, row_mask=rows)
+                               mode, row_mask=rows)
     gu.assert_close(got, ref, "bf16", f"c4 bs{bs}", mask=rm)
     assert np.all(np.isfinite(gu.as_f64(got)))
 
@@ -140,6 +151,6 @@ def test_c5_e4m3_sampled_rows():
         m = np.zeros((case.num_seqs, case.num_q_heads), bool)
         m[pick, :] = True
         return m
-    case, got, ref, rm = _full("c5", workloads.c5_fp8, 512, 4, row_mask=rows,
+    case, got, ref, rm = _full("c5", workloads.c5_fp8, ("balanced", 0, 0, 0), row_mask=rows,
                                tokens_mask_fn=tokens)
     gu.assert_close(got, ref, "fp8_e4m3", "c5", mask=rm)

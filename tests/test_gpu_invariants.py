@@ -13,7 +13,8 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-MODES = [(0, 4), (64, 2), (512, 4)]
+MODES = [("single", 0, 4, 0), ("partitioned", 64, 2, 0), ("partitioned", 512, 4, 0),
+         ("balanced", 0, 0, 0), ("balanced", 0, 0, 13)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -40,10 +41,10 @@ def test_physical_block_permutation_is_bit_identical(dtype):
     g2 = gu.GpuCase(case)
     g2.kc, g2.vc = gu.dev(kc2), gu.dev(vc2)
     g2.tables = gu.dev(pi[case.block_tables])
-    for part, waves in MODES:
-        a = gu.host(g.decode(part, waves)).copy()
-        b = gu.host(g2.decode(part, waves))
-        assert np.array_equal(a, b), (part, waves)
+    for m in MODES:
+        a = gu.host(g.decode_mode(m)).copy()
+        b = gu.host(g2.decode_mode(m))
+        assert np.array_equal(a, b), m
 
 
 def test_poisoned_tails_and_free_blocks_do_not_change_bits():
@@ -51,20 +52,20 @@ def test_poisoned_tails_and_free_blocks_do_not_change_bits():
     clean = gu.GpuCase(_case(poison=False))
     poisoned.fill_and_step_writes()
     clean.fill_and_step_writes()
-    for part, waves in MODES:
-        a = gu.host(poisoned.decode(part, waves)).copy()
-        b = gu.host(clean.decode(part, waves))
-        assert np.array_equal(a, b), (part, waves)
+    for m in MODES:
+        a = gu.host(poisoned.decode_mode(m)).copy()
+        b = gu.host(clean.decode_mode(m))
+        assert np.array_equal(a, b), m
         assert np.all(np.isfinite(gu.as_f64(a)))
 
 
 def test_repeated_launches_are_deterministic():
     g = gu.GpuCase(_case())
     g.fill_and_step_writes()
-    for part, waves in MODES:
-        first = gu.host(g.decode(part, waves)).copy()
+    for m in MODES:
+        first = gu.host(g.decode_mode(m)).copy()
         for _ in range(3):
-            assert np.array_equal(gu.host(g.decode(part, waves)), first)
+            assert np.array_equal(gu.host(g.decode_mode(m)), first)
 
 
 def test_contiguous_table_gives_the_same_bits():
@@ -81,5 +82,5 @@ def test_contiguous_table_gives_the_same_bits():
         c += nbs[s]
     g2 = gu.GpuCase(case)
     g2.kc, g2.vc, g2.tables = gu.dev(kc[order]), gu.dev(vc[order]), gu.dev(t2)
-    for part, waves in MODES:
-        assert np.array_equal(gu.host(g.decode(part, waves)).copy(), gu.host(g2.decode(part, waves)))
+    for m in MODES:
+        assert np.array_equal(gu.host(g.decode_mode(m)).copy(), gu.host(g2.decode_mode(m)))
