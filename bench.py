@@ -33,7 +33,7 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c4bs32", "c5"])
-    p.add_argument("--mode", default="balanced", choices=["single", "partitioned", "balanced"])
+    p.add_argument("--mode", default="auto", choices=["single", "partitioned", "balanced", "auto"])
     p.add_argument("--partition", type=int, default=512, help="tokens per partition (partitioned)")
     p.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (0 = default)")
     p.add_argument("--workers", type=int, default=0, help="balanced workers (0 = default)")
@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="run one plain device copy of this many MiB first (scales PMC byte counters)")
     return p.parse_args()
 
 
@@ -55,6 +57,28 @@ def build_workload(name):
     if name == "c4bs32":
         return workloads.c4_long_context(block_size=32)
     return workloads.c5_fp8()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant decode kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary for this workload, or None when the
+    kernel source changed since the counters were taken."""
+    import glob
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    src = os.path.join(here, "paged_kv_cache_135_amd", "csrc", "decode.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(here, "profiles", "*_pmc_traffic.md"))):
+        fields = {}
+        with open(path) as f:
+            first = f.readline()
+            for line in f:
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if workload in first and fields.get("decode.hip sha256") == sha:
+            return int(fields["traffic_bytes_per_launch"]), fields.get("kernel", "")
+    return None, None
 
 
 def cpu_baseline(case, seconds):
@@ -158,6 +182,13 @@ def main():
             if ev is not None:
                 ev[i][2].record(stream)
 
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=q.device)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] warmup {args.warmup} steps, {layers} layer pools", file=sys.stderr, flush=True)
     run_steps(args.warmup)
     torch.cuda.synchronize()
@@ -195,6 +226,7 @@ def main():
     dec_s = float(dec_ms.mean()) / 1e3
 
     kv = case.kv_bytes()
+    traffic, traffic_kernel = measured_traffic(case.name)
     value = kv / (ms_per_step / 1e3) / 1e9
     achieved = kv / dec_s / 1e9
     print(f"[bench] decode {dec_ms.mean()*1e3:.1f} us (p10 {np.percentile(dec_ms,10)*1e3:.1f}, "
@@ -237,13 +269,14 @@ def main():
         "roofline": {
             "kernel": {"single": "paged_attention_decode (single pass)",
                        "partitioned": "paged_attention_decode (partitions + merge)",
-                       "balanced": "paged_attention_decode (balanced split + merge)"}[args.mode],
+                       "balanced": "paged_attention_decode (balanced split + merge)",
+                       "auto": "paged_attention_decode (auto mode)"}[args.mode],
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
         },
     }
     if case.cache_dtype != "bf16" or case.shared_blocks:

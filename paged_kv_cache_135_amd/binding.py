@@ -54,14 +54,14 @@ class PkvDecodeOpts(ctypes.Structure):
     ]
 
 
-DECODE_MODES = {"single": 0, "partitioned": 1, "balanced": 2}
+DECODE_MODES = {"single": 0, "partitioned": 1, "balanced": 2, "auto": 3}
 
 
 def decode_opts(mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
                 num_workers: int = 0) -> PkvDecodeOpts:
-    """Options struct; mode None means "partitioned" if partition_size > 0 else "single"."""
+    """Options struct; mode None means "partitioned" if partition_size > 0, else "auto"."""
     if mode is None:
-        mode = "partitioned" if partition_size > 0 else "single"
+        mode = "partitioned" if partition_size > 0 else "auto"
     o = PkvDecodeOpts()
     o.mode = DECODE_MODES[mode]
     o.partition_size = int(partition_size)
@@ -193,8 +193,8 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
                            stream=None):
     """Decode attention over the paged pools into ``out`` [S, Hq, D].
 
-    mode: "single", "partitioned" (needs partition_size) or "balanced"; None
-    picks "partitioned" when partition_size > 0, else "single".  The split
+    mode: "single", "partitioned" (needs partition_size), "balanced" or "auto";
+    None picks "partitioned" when partition_size > 0, else "auto".  The split
     modes need a workspace (a uint8 device tensor of at least
     decode_workspace_bytes(...)); it is allocated here when not given."""
     _same_device(out, q, key_cache, value_cache, block_tables, context_lens)

@@ -96,21 +96,23 @@ int64_t num_partitions(int64_t max_blocks, int64_t block_size, int64_t partition
   return np < 1 ? 1 : np;
 }
 
-// Default balanced worker count: 4 wavefronts per compute unit of the
-// current device (cached per device).
-int32_t default_workers() {
+// Compute units of the current device (cached per device; 256 if unknown).
+int32_t device_cus() {
   static int32_t cache[64] = {0};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (cache[dev] == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cache[dev] = 4 * cus;
+    cache[dev] = cus;
   }
   return cache[dev];
 }
+
+// Default balanced worker count: 4 wavefronts per compute unit.
+int32_t default_workers() { return 4 * device_cus(); }
 
 // Launch plan derived from the options and sizes.
 struct Plan {
@@ -132,9 +134,21 @@ struct Plan {
 pkv_status plan(const pkv_decode_opts* opts, int64_t S, int64_t Hq, int64_t Hkv, int64_t maxb,
                 int64_t bs, Plan* p) {
   (void)Hq;
-  (void)Hkv;
-  const int32_t mode = opts ? opts->mode : PKV_DECODE_SINGLE_PASS;
-  const int32_t waves = opts ? opts->waves_per_group : 0;
+  int32_t mode = opts ? opts->mode : PKV_DECODE_SINGLE_PASS;
+  int32_t waves = opts ? opts->waves_per_group : 0;
+  int32_t auto_workers = 0;
+  if (mode == PKV_DECODE_AUTO) {
+    // measured on MI355X: many short (sequence, KV head) pairs stream best one
+    // workgroup each; few or long ones need the balanced split
+    const int64_t pairs = S * Hkv, cus = device_cus();
+    if (pairs >= 16 * cus) {
+      mode = PKV_DECODE_SINGLE_PASS;
+      if (waves == 0) waves = 8;
+    } else {
+      mode = PKV_DECODE_BALANCED;
+      auto_workers = (int32_t)((pairs >= 8 * cus ? 8 : 4) * cus);
+    }
+  }
   p->mode = mode;
   p->waves = waves == 0 ? 4 : waves;
   if (p->waves != 1 && p->waves != 2 && p->waves != 4 && p->waves != 8)
@@ -159,7 +173,7 @@ pkv_status plan(const pkv_decode_opts* opts, int64_t S, int64_t Hq, int64_t Hkv,
       const int32_t wk = opts->num_workers;
       if (wk < 0 || wk > (1 << 24))
         return fail(PKV_ERR_UNSUPPORTED, "num_workers %d: must be in [0, 2^24]", wk);
-      p->workers = wk == 0 ? default_workers() : wk;
+      p->workers = wk != 0 ? wk : auto_workers != 0 ? auto_workers : default_workers();
       if (S * Hkv > INT32_MAX / 2) return fail(PKV_ERR_UNSUPPORTED, "too many (sequence, KV head) pairs");
       return PKV_OK;
     }

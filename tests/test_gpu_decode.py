@@ -21,7 +21,7 @@ def _gpu():
     gu.need_gpu()
 
 
-MODES = [("single", 0, 1, 0), ("single", 0, 4, 0), ("single", 0, 8, 0),
+MODES = [("single", 0, 1, 0), ("single", 0, 4, 0), ("single", 0, 8, 0), ("auto", 0, 0, 0),
          ("partitioned", 32, 1, 0), ("partitioned", 64, 2, 0), ("partitioned", 512, 4, 0),
          ("partitioned", 256, 8, 0), ("balanced", 0, 0, 0), ("balanced", 0, 0, 7),
          ("balanced", 0, 0, 64), ("balanced", 0, 0, 1)]
