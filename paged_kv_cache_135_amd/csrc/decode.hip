@@ -51,6 +51,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kChunkTiles = 1024;  // block ids staged in LDS per pass (4 KiB)
+// Balanced split: work units charged for starting a piece, in tiles.  A piece
+// start (q rows, block ids, the partial write) costs about two bf16 tile times
+// on MI355X; an E4M3 tile streams in half the time, so the same start costs
+// about four of them.
+template <int CT>
+constexpr int piece_cost() {
+  return CT == PKV_FP8_E4M3 ? 4 : CT == PKV_BF16 ? 2 : 1;
+}
 constexpr uint32_t kSelLo = 0x05040100u;  // v_perm: low halves of two dwords
 constexpr uint32_t kSelHi = 0x07060302u;  // v_perm: high halves of two dwords
 
@@ -574,10 +582,16 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
   if (w >= W) return;
   const int S = a.num_seqs, Hkv = a.num_kv_heads, G = a.group, bs = a.block_size;
 
+  // The split is made in work units: a (sequence, KV head) pair with n tiles
+  // costs n + kPieceCost units, the first kPieceCost standing for the fixed
+  // cost of starting a piece (its q rows, block ids and partial state), so a
+  // run that crosses into a new pair gets fewer tiles.
   // Tile counts of up to kScanRegs * 64 sequences stay in registers (lane l
   // holds sequences l, l+64, ...); longer batches re-read the lengths.
   // Sequences with no tokens have no tiles: worker s % W writes their zero rows.
   constexpr int kScanRegs = 8;
+  constexpr int kPieceCost = piece_cost<CT>();
+  auto units = [](uint32_t n) { return n ? n + (uint32_t)kPieceCost : 0u; };
   uint32_t nreg[kScanRegs];
   int64_t total = 0;
   for (int c = 0, r = 0; c < S; c += 64, ++r) {
@@ -585,7 +599,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
     const int ctx = s < S ? a.lens[s] : 0;
     const uint32_t n = (uint32_t)((ctx + 15) >> 4);
     if (r < kScanRegs) nreg[r] = n;
-    total += wave_sum(n);
+    total += wave_sum(units(n));
     uint64_t zmask = __ballot(s < S && ctx == 0 && s % W == w);
     while (zmask) {
       const int l = __builtin_ctzll(zmask);
@@ -610,7 +624,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
   const int64_t x1 = min(total, x0 + chunk);
   if (x0 >= x1) return;
 
-  // Sequence holding tile x0, and the tiles before it.
+  // Sequence holding unit x0, and the units before it.
   int s_cur = 0;
   int64_t p_cur = 0;
   {
@@ -620,13 +634,14 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
       uint32_t n;
       if (r < kScanRegs) n = nreg[r];
       else n = s < S ? (uint32_t)((a.lens[s] + 15) >> 4) : 0u;
-      const uint32_t incl = wave_incl_scan(n, lane);
+      const uint32_t u = units(n);
+      const uint32_t incl = wave_incl_scan(u, lane);
       const int64_t tot = (int64_t)Hkv * __shfl(incl, 63);
       if (x0 < base + tot) {
         const uint64_t hit = __ballot(x0 < base + (int64_t)Hkv * incl);
         const int l = __builtin_ctzll(hit);
         s_cur = c + l;
-        p_cur = base + (int64_t)Hkv * __shfl(incl - n, l);
+        p_cur = base + (int64_t)Hkv * __shfl(incl - u, l);
         break;
       }
       base += tot;
@@ -645,12 +660,23 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
       ++s_cur;
       continue;
     }
+    const int u = n + kPieceCost;
     const int64_t rel = x - p_cur;
-    const int h = (int)(rel / n);
-    if (h >= Hkv) break;  // cannot happen: x lies inside sequence s_cur's tiles
-    const int tl = (int)(rel - (int64_t)h * n);
-    const int te = (int)min((int64_t)n, tl + (x1 - x));
+    const int h = (int)(rel / u);
+    if (h >= Hkv) break;  // cannot happen: x lies inside sequence s_cur's units
+    const int vt = (int)(rel - (int64_t)h * u);          // unit range of this run
+    const int ve = (int)min((int64_t)u, vt + (x1 - x));  // inside the pair: [vt, ve)
+    const int tl = max(0, vt - kPieceCost);               // its tiles: [tl, te)
+    const int te = max(0, ve - kPieceCost);
     const int seg = s_cur * Hkv + h;
+    if (te <= tl) {  // the run holds only the pair's start-up units: no tiles here
+      x += ve - vt;
+      if (ve == u && h == Hkv - 1) {
+        p_cur += (int64_t)Hkv * u;
+        ++s_cur;
+      }
+      continue;
+    }
 
     const int qh = h * G + g;
     const QElem<CT>* qrow = static_cast<const QElem<CT>*>(a.q) +
@@ -669,9 +695,9 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
     int32_t ent_next = has_carry ? carry : (lane < NBUF ? entry(tl + lane) : 0);
     // When the run goes on with the next KV head of this sequence, that piece
     // starts at tile 0 of the same table row: fetch its first block ids now.
-    const int64_t after = x + (te - tl);
-    has_carry = te == n && h + 1 < Hkv && after < x1;
-    const int te_next = has_carry ? (int)min((int64_t)n, x1 - after) : 1;
+    const int64_t after = x + (ve - vt);
+    has_carry = ve == u && h + 1 < Hkv && x1 - after > kPieceCost;
+    const int te_next = has_carry ? (int)min((int64_t)n, x1 - after - kPieceCost) : 1;
     for (int k = tl; k < te; k += NBUF) {
       const int32_t ent = ent_next;
       ent_next = lane < NBUF ? entry(k + NBUF + lane) : 0;
@@ -697,8 +723,8 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
     if (whole || te == n) {
       // the segment's last piece records where its pieces are
       if (lane == 0) {
-        const int64_t seg_start = p_cur + (int64_t)h * n;
-        a.ws_meta[2 * (int64_t)seg] = whole ? -1 : (int32_t)(seg_start / chunk);
+        const int64_t first_tile_unit = p_cur + (int64_t)h * u + kPieceCost;
+        a.ws_meta[2 * (int64_t)seg] = whole ? -1 : (int32_t)(first_tile_unit / chunk);
         a.ws_meta[2 * (int64_t)seg + 1] = whole ? -1 : w;
       }
     }
@@ -726,9 +752,9 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
         if (lane < 16) *reinterpret_cast<f32x2*>(a.ws_ml + (slot * G + g) * 2) = f32x2{st.m, l_run};
       }
     }
-    x += te - tl;
-    if (te == n && h == Hkv - 1) {
-      p_cur += (int64_t)Hkv * n;
+    x += ve - vt;
+    if (ve == u && h == Hkv - 1) {
+      p_cur += (int64_t)Hkv * u;
       ++s_cur;
     }
   }
