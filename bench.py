@@ -32,7 +32,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
-    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c4bs32", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c4bs32", "c5", "cow"],
+                   help="cow: copy-on-write block copies of the Qwen-shaped pool (its own metric)")
     p.add_argument("--mode", default="auto", choices=["single", "partitioned", "balanced", "auto"])
     p.add_argument("--partition", type=int, default=512, help="tokens per partition (partitioned)")
     p.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (0 = default)")
@@ -119,6 +120,67 @@ def cpu_baseline(case, seconds):
     }
 
 
+def bench_copy_blocks(args):
+    """Copy-on-write block copies: 4096 (src, dst) pairs over the Qwen-shaped
+    bf16 pool (4 KV heads x 16 slots x 128 dims: 16 KiB per block per pool).
+    Algorithmic bytes per call: pairs x 2 pools x block bytes, read and written."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_135_amd as pkv
+    import workloads
+    NB, H, bs, D, P = 20000, 4, 16, 128, 4096
+    rng = np.random.default_rng(1005)
+    kc = torch.empty((NB, H, bs, D), dtype=torch.bfloat16, device="cuda").normal_()
+    vc = torch.empty_like(kc).normal_()
+    perm = rng.permutation(NB).astype(np.int32)
+    pairs_np = np.stack([perm[:P], perm[P:2 * P]], axis=1)
+    pairs = torch.from_numpy(pairs_np).cuda()
+    pkv.validate_block_pairs(pairs_np, NB)
+    block_bytes = H * bs * D * 2
+    moved = P * 2 * block_bytes * 2
+    for _ in range(args.warmup):
+        pkv.paged_kv_copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        pkv.paged_kv_copy_blocks(kc, vc, pairs)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    res = {
+        "metric": "copy-on-write block copy: GB/s moved (read + write)",
+        "value": round(moved / (us / 1e6) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "cow_block_copy", "pairs": P, "block_bytes_per_pool": block_bytes,
+                   "num_blocks": NB},
+        "roofline": {"kernel": "copy_blocks_kernel", "bound": "hbm",
+                     "achieved": round(moved / (us / 1e6) / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(moved / (us / 1e6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        kh = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.copy_blocks(kh, vh, pairs_np)
+            reps += 1
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(moved * reps / el / 1e9, 3), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"the same {P} pair copies, {reps} times in {el:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -141,6 +203,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         return 1
     pkv.load()
+    if args.workload == "cow":
+        return bench_copy_blocks(args)
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
     case = build_workload(args.workload)
     pool_bytes = case.key_cache.nbytes * 2

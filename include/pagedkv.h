@@ -188,6 +188,25 @@ pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q,
                                   int32_t block_size, const pkv_decode_opts* opts,
                                   void* hip_stream);
 
+/*
+ * Copy-on-write block copies.  A physical block listed by several block tables
+ * is copied to a fresh block before one branch writes into it ("PagedAttention
+ * Memory Management", section "Complex Topologies and Memory Sharing"; "What
+ * problem does PagedAttention solve...", section "Sharing, the second
+ * dividend").
+ *   key_cache,
+ *   value_cache   [NB, Hkv, bs, D], same shape and element type
+ *   block_pairs   [P, 2] int32 rows (src, dst): block dst of both pools becomes a
+ *                 byte copy of block src; a row with a negative id, or src == dst,
+ *                 is skipped
+ * Caller contract (checked on host copies by pkv_validate_block_pairs): ids
+ * < NB, destinations distinct, and no destination is also a source, so the
+ * result does not depend on the order of the copies.
+ * Errors: PKV_ERR_NULL, PKV_ERR_DTYPE, PKV_ERR_SHAPE, PKV_ERR_LAYOUT, PKV_ERR_HIP.
+ */
+pkv_status paged_kv_copy_blocks(pkv_tensor* key_cache, pkv_tensor* value_cache,
+                                const pkv_tensor* block_pairs, void* hip_stream);
+
 /* Workspace bytes paged_attention_decode needs with these sizes and options
  * (0 when none is needed: single pass, or one partition per sequence).
  * Returns 0 as well for invalid arguments. */
@@ -209,6 +228,10 @@ pkv_status pkv_validate_slots(const int32_t* slots, int64_t num_tokens, int64_t 
 pkv_status pkv_validate_decode_inputs(const int32_t* block_tables, const int32_t* context_lens,
                                       int32_t num_seqs, int32_t max_blocks_per_seq,
                                       int64_t num_blocks, int32_t block_size);
+/* pkv_validate_block_pairs: rows with both ids >= 0 name blocks < num_blocks,
+ * their destinations are distinct and none is also a source. */
+pkv_status pkv_validate_block_pairs(const int32_t* block_pairs, int64_t num_pairs,
+                                    int64_t num_blocks);
 
 #ifdef __cplusplus
 }

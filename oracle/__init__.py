@@ -15,7 +15,8 @@ Sources, by page and section:
     "Calculating Physical Block Sizes", the block-size formula.
   * pool_capacity: same section, the worked sizing of the pool from the memory
     left after weights and the runtime reserve.
-  * paged_kv_write / paged_attention_decode / the E4M3 codec: see oracle.c.
+  * paged_kv_write / paged_attention_decode / copy_blocks / the E4M3 codec:
+    see oracle.c.
 """
 from __future__ import annotations
 
@@ -65,6 +66,8 @@ def _load():
     lib.orc_paged_attention_decode.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, P, P, i32, i32,
                                                i32, i32, i64, i32, i32, f32, f32, f32, P, P]
     lib.orc_paged_attention_decode.restype = ctypes.c_int
+    lib.orc_copy_blocks.argtypes = [P, P, i64, i64, P, i64]
+    lib.orc_copy_blocks.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -170,3 +173,20 @@ def paged_attention_decode(q: np.ndarray, key_cache: np.ndarray, value_cache: np
         _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, NB, bs,
         block_tables.shape[1], float(scale), float(k_scale), float(v_scale), mask_arg, _ptr(out)))
     return out
+
+
+def copy_blocks(key_cache: np.ndarray, value_cache: np.ndarray, pairs: np.ndarray) -> None:
+    """Copy-on-write block copies in place: for each (src, dst) row of the int32
+    [P, 2] array, block dst of both pools becomes a copy of block src."""
+    if key_cache.shape != value_cache.shape or key_cache.dtype != value_cache.dtype:
+        raise ValueError("pools differ")
+    for a in (key_cache, value_cache, pairs):
+        if not a.flags.c_contiguous:
+            raise ValueError("oracle arrays must be C-contiguous")
+    pr = np.ascontiguousarray(pairs, dtype=np.int32)
+    if pr.ndim != 2 or pr.shape[1] != 2:
+        raise ValueError("pairs must be [P, 2]")
+    nb = key_cache.shape[0]
+    bb = key_cache[0].nbytes if nb else 0
+    _check(_load().orc_copy_blocks(_ptr(key_cache), _ptr(value_cache), nb, bb, _ptr(pr),
+                                   pr.shape[0]))

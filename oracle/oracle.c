@@ -284,4 +284,35 @@ int orc_paged_attention_decode(const void* q, int q_dtype, const void* kc, const
   return status;
 }
 
+/* ------------------------------------------------------ block copy (CoW) */
+
+/*
+ * Copy-on-write support: before a branch writes into a physical block that
+ * other sequences still list, the block's contents are copied to a fresh block
+ * ("PagedAttention Memory Management", section "Complex Topologies and Memory
+ * Sharing"; "What problem does PagedAttention solve...", section "Sharing, the
+ * second dividend").  For every pair (src, dst) with both ids >= 0, block dst of
+ * the K pool and of the V pool becomes a byte copy of block src; pairs with a
+ * negative id are skipped.  block_bytes is the size of one block of one pool.
+ */
+int orc_copy_blocks(void* kc, void* vc, int64_t num_blocks, int64_t block_bytes,
+                    const int32_t* pairs, int64_t num_pairs) {
+  int64_t i;
+  if (num_blocks < 0 || block_bytes < 0 || num_pairs < 0) return ORC_ERR_ARG;
+  for (i = 0; i < num_pairs; ++i) {
+    int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || dst < 0) continue;
+    if (src >= num_blocks || dst >= num_blocks) return ORC_ERR_RANGE;
+  }
+  for (i = 0; i < num_pairs; ++i) {
+    int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || dst < 0 || src == dst) continue;
+    memcpy((char*)kc + (int64_t)dst * block_bytes, (const char*)kc + (int64_t)src * block_bytes,
+           (size_t)block_bytes);
+    memcpy((char*)vc + (int64_t)dst * block_bytes, (const char*)vc + (int64_t)src * block_bytes,
+           (size_t)block_bytes);
+  }
+  return ORC_OK;
+}
+
 int orc_abi_version(void) { return 1; }

@@ -22,7 +22,8 @@ STATUS_NAMES = {
 }
 EXPORTED = (
     "pkv_abi_version", "pkv_last_error", "paged_kv_write", "paged_attention_decode",
-    "paged_attention_decode_workspace_bytes", "pkv_validate_slots", "pkv_validate_decode_inputs",
+    "paged_attention_decode_workspace_bytes", "paged_kv_copy_blocks", "pkv_validate_slots",
+    "pkv_validate_decode_inputs", "pkv_validate_block_pairs",
 )
 
 
@@ -99,6 +100,10 @@ def load():
     lib.pkv_validate_decode_inputs.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int64, ctypes.c_int32]
     lib.pkv_validate_decode_inputs.restype = ctypes.c_int
+    lib.paged_kv_copy_blocks.argtypes = [T, T, T, P]
+    lib.paged_kv_copy_blocks.restype = ctypes.c_int
+    lib.pkv_validate_block_pairs.argtypes = [P, ctypes.c_int64, ctypes.c_int64]
+    lib.pkv_validate_block_pairs.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -210,6 +215,23 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
     if ws is not None and workspace is None and stream is not None:
         ws.record_stream(stream)
     return out
+
+
+def paged_kv_copy_blocks(key_cache, value_cache, block_pairs, *, stream=None) -> None:
+    """Copy-on-write: for each int32 row (src, dst) of ``block_pairs`` [P, 2],
+    block dst of both pools becomes a copy of block src (see include/pagedkv.h)."""
+    _same_device(key_cache, value_cache, block_pairs)
+    dk, dv, dp = describe(key_cache), describe(value_cache), describe(block_pairs)
+    _check(load().paged_kv_copy_blocks(ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(dp),
+                                       _stream(key_cache, stream)))
+
+
+def validate_block_pairs(pairs: np.ndarray, num_blocks: int) -> None:
+    """Host check of copy-on-write pairs (range, distinct destinations, no
+    destination used as a source); raises PagedKVError."""
+    p = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    _check(load().pkv_validate_block_pairs(p.ctypes.data_as(ctypes.c_void_p), p.shape[0],
+                                           num_blocks))
 
 
 def validate_slots(slots: np.ndarray, num_blocks: int, block_size: int) -> None:

@@ -252,6 +252,44 @@ pkv_status paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_te
   return ok();
 }
 
+pkv_status paged_kv_copy_blocks(pkv_tensor* key_cache, pkv_tensor* value_cache,
+                                const pkv_tensor* block_pairs, void* hip_stream) {
+  PKV_TRY(check_tensor(key_cache, "key_cache", 4));
+  PKV_TRY(check_tensor(value_cache, "value_cache", 4));
+  PKV_TRY(check_tensor(block_pairs, "block_pairs", 2));
+  if (value_cache->dtype != key_cache->dtype)
+    return fail(PKV_ERR_DTYPE, "value_cache: dtype differs from key_cache");
+  if (key_cache->dtype != PKV_F32 && key_cache->dtype != PKV_BF16 && key_cache->dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_DTYPE, "key_cache: must be f32, bf16 or E4M3");
+  if (block_pairs->dtype != PKV_I32) return fail(PKV_ERR_DTYPE, "block_pairs: must be int32");
+  for (int i = 0; i < 4; ++i)
+    if (value_cache->shape[i] != key_cache->shape[i])
+      return fail(PKV_ERR_SHAPE, "value_cache: shape differs from key_cache");
+  if (block_pairs->shape[1] != 2) return fail(PKV_ERR_SHAPE, "block_pairs: expected [P, 2]");
+  const int64_t P = block_pairs->shape[0];
+  const int64_t block_bytes = key_cache->shape[1] * key_cache->shape[2] * key_cache->shape[3] *
+                              elem_bytes(key_cache->dtype);
+  if (block_bytes % 16 != 0)
+    return fail(PKV_ERR_LAYOUT, "one block must be a multiple of 16 bytes (got %lld)", (long long)block_bytes);
+  if (P > INT32_MAX / 2) return fail(PKV_ERR_SHAPE, "too many pairs");
+  PKV_TRY(check_align(key_cache, "key_cache", 16));
+  PKV_TRY(check_align(value_cache, "value_cache", 16));
+  PKV_TRY(check_align(block_pairs, "block_pairs", 4));
+  if (overlap(key_cache, value_cache)) return fail(PKV_ERR_LAYOUT, "key_cache and value_cache overlap");
+  if (overlap(block_pairs, key_cache) || overlap(block_pairs, value_cache))
+    return fail(PKV_ERR_LAYOUT, "block_pairs overlaps a cache");
+  if (P == 0) return ok();
+  pkv::CopyArgs a{};
+  a.kc = key_cache->data;
+  a.vc = value_cache->data;
+  a.pairs = static_cast<const int32_t*>(block_pairs->data);
+  a.num_pairs = P;
+  a.block_bytes = block_bytes;
+  const hipError_t e = pkv::launch_copy_blocks(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "paged_kv_copy_blocks launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim,
                                               int32_t max_blocks_per_seq, int32_t block_size,
@@ -410,6 +448,29 @@ pkv_status pkv_validate_decode_inputs(const int32_t* block_tables, const int32_t
                     b, (long long)num_blocks);
     }
   }
+  return ok();
+}
+
+pkv_status pkv_validate_block_pairs(const int32_t* block_pairs, int64_t num_pairs,
+                                    int64_t num_blocks) {
+  if (num_pairs < 0 || num_blocks < 0) return fail(PKV_ERR_SHAPE, "negative sizes");
+  if (num_pairs > 0 && !block_pairs) return fail(PKV_ERR_NULL, "block_pairs is NULL");
+  std::vector<int32_t> srcs, dsts;
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    const int32_t s = block_pairs[2 * i], d = block_pairs[2 * i + 1];
+    if (s < 0 || d < 0 || s == d) continue;
+    if (s >= num_blocks || d >= num_blocks)
+      return fail(PKV_ERR_RANGE, "pair %lld (%d, %d) outside the pool of %lld blocks", (long long)i,
+                  s, d, (long long)num_blocks);
+    srcs.push_back(s);
+    dsts.push_back(d);
+  }
+  std::sort(dsts.begin(), dsts.end());
+  for (size_t i = 1; i < dsts.size(); ++i)
+    if (dsts[i] == dsts[i - 1]) return fail(PKV_ERR_RANGE, "destination block %d repeated", dsts[i]);
+  for (int32_t s : srcs)
+    if (std::binary_search(dsts.begin(), dsts.end(), s))
+      return fail(PKV_ERR_RANGE, "block %d is both a source and a destination", s);
   return ok();
 }
 

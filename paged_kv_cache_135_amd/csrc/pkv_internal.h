@@ -58,7 +58,18 @@ struct DecodeArgs {
   float v_scale;        // 1, or the V scale for E4M3
 };
 
+// Copy-on-write block copies: for each (src, dst) pair, both pools' block dst
+// becomes a copy of block src.
+struct CopyArgs {
+  void* kc;
+  void* vc;
+  const int32_t* pairs;  // [num_pairs][2]
+  int64_t num_pairs;
+  int64_t block_bytes;   // one block of one pool
+};
+
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -207,3 +207,27 @@ def test_host_validators():
         B.validate_decode_inputs(tables, np.array([40, 17], np.int32), 4, 16)  # reads entry 9
     with pytest.raises(B.PagedKVError):
         B.validate_decode_inputs(tables, np.array([49, 0], np.int32), 4, 16)  # > 3 blocks
+
+
+def test_copy_blocks_rejects_bad_descriptors():
+    lib = B.load()
+    kc = desc([8, 2, 16, 64], B.PKV_BF16, FAKE)
+    vc = desc([8, 2, 16, 64], B.PKV_BF16, FAKE + (1 << 20))
+    pr = desc([3, 2], B.PKV_I32, FAKE + (2 << 20))
+    call = lambda a, b, c: lib.paged_kv_copy_blocks(*(ctypes.byref(x) if x is not None else None
+                                                      for x in (a, b, c)), None)
+    assert call(None, vc, pr) == 1
+    assert call(kc, desc([8, 2, 16, 64], B.PKV_F32, FAKE + (1 << 20)), pr) == 2
+    assert call(kc, vc, desc([3, 2], B.PKV_BF16, FAKE + (2 << 20))) == 2
+    assert call(kc, vc, desc([3, 3], B.PKV_I32, FAKE + (2 << 20))) == 3
+    assert call(kc, desc([9, 2, 16, 64], B.PKV_BF16, FAKE + (1 << 20)), pr) == 3
+    assert call(kc, desc([8, 2, 16, 64], B.PKV_BF16, FAKE + 4096), pr) == 4  # pools overlap
+    assert call(kc, vc, desc([0, 2], B.PKV_I32, 0)) == 0  # nothing to copy
+
+
+def test_block_pair_validator():
+    B.validate_block_pairs(np.array([[1, 5], [2, 6], [-1, 3], [4, 4]], np.int32), 8)
+    for bad in ([[1, 8]], [[1, 5], [2, 5]], [[1, 5], [5, 6]]):
+        with pytest.raises(B.PagedKVError) as e:
+            B.validate_block_pairs(np.array(bad, np.int32), 8)
+        assert e.value.status == 8
