@@ -4,14 +4,19 @@
 One step = one decode step of one attention layer over one batch: the
 slot-mapped KV write of every sequence's new token, then paged decode
 attention over the whole context (by default the balanced split: equal runs
-of tiles per wavefront, then the merge of split (sequence, KV head) pairs).  Inputs
-are seeded synthetic data resident in HBM before timing starts.  Steps rotate
-over several layer pools (each its own K/V tensors) so a pool is not still
-resident in the 256 MB last-level cache when it is read again.
+of tiles per wavefront, then the merge of split (sequence, KV head) pairs).
+When the step's writes are one new token per sequence at position len-1, the
+step is one call (paged_attention_decode_append, the write folded into the
+decode launch); otherwise (a prefill chunk into free slots) it is the KV write
+followed by the decode.  Inputs are seeded synthetic data resident in HBM
+before timing starts.  Steps rotate over several layer pools (each its own K/V
+tensors) so a pool is not still resident in the 256 MB last-level cache when
+it is read again.
 
 Prints ONE JSON line:
   value  = KV bytes read per step / wall time per step (GB/s, decimal)
-  roofline = the decode call's KV bytes / its event-timed duration vs 8 TB/s
+  roofline = KV bytes / the event-timed duration of the streaming decode
+             kernel alone (its merge kernel timed apart) vs 8 TB/s
   cpu_baseline = the fp64 oracle timed on this host on the same workload
 """
 from __future__ import annotations
@@ -42,6 +47,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    p.add_argument("--step", default="auto", choices=["auto", "append", "split"],
+                   help="append: one call per step; split: KV write then decode; auto: append "
+                        "when the step writes one token per sequence at position len-1")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (scales PMC byte counters)")
     return p.parse_args()
@@ -224,27 +232,51 @@ def main():
                                         case.head_dim, case.block_tables.shape[1],
                                         case.block_size, args.mode, args.partition, args.workers)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    step = args.step
+    if step == "auto":
+        step = "split"
+        if case.slot_mapping.shape[0] == case.num_seqs:
+            try:
+                pkv.validate_append_slots(case.slot_mapping, case.block_tables, case.context_lens,
+                                          case.key_cache.shape[0], case.block_size)
+                step = "append"
+            except pkv.PagedKVError:
+                pass
+    append = step == "append"
+    dkw = dict(k_scale=case.k_scale, v_scale=case.v_scale, mode=args.mode,
+               partition_size=args.partition, waves_per_group=args.waves,
+               num_workers=args.workers, workspace=ws)
+
+    def decode_launch(kc, vc, defer):
+        return pkv.DecodeLaunch(out, q, kc, vc, tables, lens, case.scale, case.block_size,
+                                append=(knew, vnew, slots) if append else None,
+                                defer_merge=defer, **dkw)
+
     writes = [pkv.WriteLaunch(knew, vnew, slots, kc, vc, k_scale=case.k_scale,
                               v_scale=case.v_scale) for kc, vc in pools]
-    decodes = [pkv.DecodeLaunch(out, q, kc, vc, tables, lens, case.scale, case.block_size,
-                                k_scale=case.k_scale, v_scale=case.v_scale, mode=args.mode,
-                                partition_size=args.partition, waves_per_group=args.waves,
-                                num_workers=args.workers, workspace=ws) for kc, vc in pools]
+    decodes = [decode_launch(kc, vc, False) for kc, vc in pools]
+    split_decodes = [decode_launch(kc, vc, True) for kc, vc in pools]
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
 
     def run_steps(n, ev=None):
+        # ev[i]: events before the write, before the streaming kernel, before
+        # the merge kernel and after it (the decode is split only when timed)
         for i in range(n):
             li = i % layers
             if ev is not None:
                 ev[i][0].record(stream)
-            writes[li]()
-            if ev is not None:
-                ev[i][1].record(stream)
-            decodes[li]()
-            if ev is not None:
-                ev[i][2].record(stream)
+            if not append:
+                writes[li]()
+            if ev is None:
+                decodes[li]()
+                continue
+            ev[i][1].record(stream)
+            split_decodes[li]()
+            ev[i][2].record(stream)
+            split_decodes[li].merge()
+            ev[i][3].record(stream)
 
     if args.copy_calibration_mib:
         src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=q.device)
@@ -280,22 +312,26 @@ def main():
         wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
 
-    # timed region 2: per-launch HIP events on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # timed region 2: per-launch HIP events on the launch stream; the decode
+    # call is made in its two halves so the streaming kernel is timed alone
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     run_steps(K, ev)
     torch.cuda.synchronize()
-    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
     wr_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
-    dec_s = float(dec_ms.mean()) / 1e3
+    main_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    merge_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])
+    main_s = float(main_ms.mean()) / 1e3
+    dec_s = float((main_ms + merge_ms).mean()) / 1e3
 
     kv = case.kv_bytes()
     traffic, traffic_kernel = measured_traffic(case.name)
     value = kv / (ms_per_step / 1e3) / 1e9
-    achieved = kv / dec_s / 1e9
-    print(f"[bench] decode {dec_ms.mean()*1e3:.1f} us (p10 {np.percentile(dec_ms,10)*1e3:.1f}, "
-          f"p90 {np.percentile(dec_ms,90)*1e3:.1f}), write {wr_ms.mean()*1e3:.1f} us, "
-          f"step {ms_per_step*1e3:.1f} us", file=sys.stderr, flush=True)
+    achieved = kv / main_s / 1e9
+    print(f"[bench] step {step}: streaming kernel {main_ms.mean()*1e3:.1f} us "
+          f"(p10 {np.percentile(main_ms,10)*1e3:.1f}, p90 {np.percentile(main_ms,90)*1e3:.1f}), "
+          f"merge {merge_ms.mean()*1e3:.1f} us, write {wr_ms.mean()*1e3:.1f} us, "
+          f"wall step {ms_per_step*1e3:.1f} us", file=sys.stderr, flush=True)
 
     res = {
         "metric": "paged decode attn: KV GB/s read (% of MI355X HBM peak) + decode tokens/s per layer",
@@ -324,17 +360,20 @@ def main():
             "num_workers": args.workers or None,
             "layer_pools": layers,
             "graph": bool(args.graph),
+            "step": step,
         },
         "kv_bytes_per_step": kv,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s_per_layer": round(case.num_seqs / (ms_per_step / 1e3), 1),
         "decode_us": round(dec_s * 1e6, 2),
-        "write_us": round(float(wr_ms.mean()) * 1e3, 2),
+        "streaming_kernel_us": round(main_s * 1e6, 2),
+        "merge_us": round(float(merge_ms.mean()) * 1e3, 2),
+        "write_us": round(float(wr_ms.mean()) * 1e3, 2) if not append else 0.0,
         "roofline": {
-            "kernel": {"single": "paged_attention_decode (single pass)",
-                       "partitioned": "paged_attention_decode (partitions + merge)",
-                       "balanced": "paged_attention_decode (balanced split + merge)",
-                       "auto": "paged_attention_decode (auto mode)"}[args.mode],
+            "kernel": "streaming decode kernel (" + (
+                "append, " if append else "") + {
+                "single": "single pass", "partitioned": "partitions",
+                "balanced": "balanced split", "auto": "auto mode"}[args.mode] + ")",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 #define PKV_MAX_DIMS 4
 
 typedef enum {
@@ -130,7 +130,15 @@ typedef struct {
   void* workspace;          /* device memory, >= paged_attention_decode_workspace_bytes();
                                not needed for SINGLE_PASS */
   size_t workspace_bytes;
+  int32_t flags;            /* PKV_DECODE_* flags below, or 0 */
 } pkv_decode_opts;
+
+/* opts->flags: launch only the streaming kernel and leave its partial states
+ * in the workspace; the caller then calls paged_attention_decode_merge with
+ * the same arguments on the same stream before reading `out` or reusing the
+ * workspace.  Lets a caller time or schedule the two kernels apart.  Modes
+ * without a merge (single pass, one partition) finish in the first call. */
+#define PKV_DECODE_DEFER_MERGE 1
 
 /* Version of this header the library was built from (PKV_ABI_VERSION). */
 int32_t pkv_abi_version(void);
@@ -189,6 +197,51 @@ pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q,
                                   void* hip_stream);
 
 /*
+ * Second half of a call made with PKV_DECODE_DEFER_MERGE: merges the partial
+ * states the streaming kernel left in the workspace into `out`.  Arguments and
+ * errors as for paged_attention_decode (all of them as in the first call);
+ * launches nothing when the mode has no merge.
+ */
+pkv_status paged_attention_decode_merge(pkv_tensor* out, const pkv_tensor* q,
+                                        const pkv_tensor* key_cache,
+                                        const pkv_tensor* value_cache,
+                                        const pkv_tensor* block_tables,
+                                        const pkv_tensor* context_lens, float scale,
+                                        int32_t block_size, const pkv_decode_opts* opts,
+                                        void* hip_stream);
+
+/*
+ * One decode step in one call: the KV write of each sequence's new token (the
+ * token the step attends last) followed by decode attention, with the write
+ * folded into the decode launch.  Same sources as the two operations: the new
+ * token is written first, then attended with the rest of its context.
+ *   k, v          [S, Hkv, D], q's element type: sequence s's new K/V rows
+ *                 (bf16 for an E4M3 cache, quantized as paged_kv_write does)
+ *   slot_mapping  [S] int32: slot of sequence s's new token; negative = no write
+ *   the rest      as for paged_attention_decode
+ * Result: the same cache bytes and, bit for bit, the same `out` as
+ * paged_kv_write(k, v, slot_mapping, ...) followed by paged_attention_decode
+ * with the same options, provided each non-negative slot is position
+ * len - 1 of its own sequence (table entry (len-1) / bs, offset (len-1) % bs)
+ * and its block is read by no other sequence in the call
+ * (pkv_validate_append_slots checks host copies).  Then the row is read from
+ * k / v by the kernel that attends it and stored to its slot from registers.
+ * A slot that is not position len - 1 is still written, and the attention
+ * reads that position from the pool; if any sequence of the call reads the
+ * written slot, its result is undefined (the read races the write).
+ * Errors: as paged_attention_decode, and PKV_ERR_NULL / PKV_ERR_DTYPE /
+ * PKV_ERR_SHAPE / PKV_ERR_LAYOUT for k, v and slot_mapping.
+ */
+pkv_status paged_attention_decode_append(pkv_tensor* out, const pkv_tensor* q,
+                                         const pkv_tensor* k, const pkv_tensor* v,
+                                         const pkv_tensor* slot_mapping, pkv_tensor* key_cache,
+                                         pkv_tensor* value_cache,
+                                         const pkv_tensor* block_tables,
+                                         const pkv_tensor* context_lens, float scale,
+                                         int32_t block_size, const pkv_decode_opts* opts,
+                                         void* hip_stream);
+
+/*
  * Copy-on-write block copies.  A physical block listed by several block tables
  * is copied to a fresh block before one branch writes into it ("PagedAttention
  * Memory Management", section "Complex Topologies and Memory Sharing"; "What
@@ -228,6 +281,13 @@ pkv_status pkv_validate_slots(const int32_t* slots, int64_t num_tokens, int64_t 
 pkv_status pkv_validate_decode_inputs(const int32_t* block_tables, const int32_t* context_lens,
                                       int32_t num_seqs, int32_t max_blocks_per_seq,
                                       int64_t num_blocks, int32_t block_size);
+/* pkv_validate_append_slots: the decode inputs as above, and every slot >= 0
+ * is position len - 1 of its sequence (so len > 0) in a block that no other
+ * sequence reads. */
+pkv_status pkv_validate_append_slots(const int32_t* slots, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t max_blocks_per_seq, int64_t num_blocks,
+                                     int32_t block_size);
 /* pkv_validate_block_pairs: rows with both ids >= 0 name blocks < num_blocks,
  * their destinations are distinct and none is also a source. */
 pkv_status pkv_validate_block_pairs(const int32_t* block_pairs, int64_t num_pairs,

@@ -22,9 +22,12 @@ STATUS_NAMES = {
 }
 EXPORTED = (
     "pkv_abi_version", "pkv_last_error", "paged_kv_write", "paged_attention_decode",
+    "paged_attention_decode_merge", "paged_attention_decode_append",
     "paged_attention_decode_workspace_bytes", "paged_kv_copy_blocks", "pkv_validate_slots",
-    "pkv_validate_decode_inputs", "pkv_validate_block_pairs",
+    "pkv_validate_decode_inputs", "pkv_validate_append_slots", "pkv_validate_block_pairs",
 )
+ABI_VERSION = 2
+DECODE_DEFER_MERGE = 1
 
 
 class PagedKVError(RuntimeError):
@@ -52,6 +55,7 @@ class PkvDecodeOpts(ctypes.Structure):
         ("num_workers", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -59,7 +63,7 @@ DECODE_MODES = {"single": 0, "partitioned": 1, "balanced": 2, "auto": 3}
 
 
 def decode_opts(mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
-                num_workers: int = 0) -> PkvDecodeOpts:
+                num_workers: int = 0, defer_merge: bool = False) -> PkvDecodeOpts:
     """Options struct; mode None means "partitioned" if partition_size > 0, else "auto"."""
     if mode is None:
         mode = "partitioned" if partition_size > 0 else "auto"
@@ -68,6 +72,7 @@ def decode_opts(mode: str | None = None, partition_size: int = 0, waves_per_grou
     o.partition_size = int(partition_size)
     o.waves_per_group = int(waves_per_group)
     o.num_workers = int(num_workers)
+    o.flags = DECODE_DEFER_MERGE if defer_merge else 0
     return o
 
 
@@ -86,12 +91,23 @@ def load():
     P = ctypes.c_void_p
     T = ctypes.POINTER(PkvTensor)
     lib.pkv_abi_version.restype = ctypes.c_int32
+    if lib.pkv_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.pkv_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild it")
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.paged_kv_write.argtypes = [T, T, T, T, T, P]
     lib.paged_kv_write.restype = ctypes.c_int
     lib.paged_attention_decode.argtypes = [T, T, T, T, T, T, ctypes.c_float, ctypes.c_int32,
                                            ctypes.POINTER(PkvDecodeOpts), P]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode_merge.argtypes = lib.paged_attention_decode.argtypes
+    lib.paged_attention_decode_merge.restype = ctypes.c_int
+    lib.paged_attention_decode_append.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_float,
+                                                  ctypes.c_int32, ctypes.POINTER(PkvDecodeOpts), P]
+    lib.paged_attention_decode_append.restype = ctypes.c_int
+    lib.pkv_validate_append_slots.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int64, ctypes.c_int32]
+    lib.pkv_validate_append_slots.restype = ctypes.c_int
     lib.paged_attention_decode_workspace_bytes.argtypes = [ctypes.c_int32] * 6 + [
         ctypes.POINTER(PkvDecodeOpts)]
     lib.paged_attention_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -217,6 +233,30 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
     return out
 
 
+def paged_attention_decode_append(out, q, k, v, slot_mapping, key_cache, value_cache,
+                                  block_tables, context_lens, scale: float, block_size: int, *,
+                                  k_scale: float = 1.0, v_scale: float = 1.0,
+                                  mode: str | None = None, partition_size: int = 0,
+                                  waves_per_group: int = 0, num_workers: int = 0, workspace=None,
+                                  stream=None):
+    """One decode step in one call: write each sequence's new token (k, v
+    [S, Hkv, D] at slot_mapping [S]) and attend (see include/pagedkv.h).
+    Equal to paged_kv_write followed by paged_attention_decode when every
+    slot is position context_lens[s]-1 of its own sequence."""
+    _same_device(out, q, k, v, slot_mapping, key_cache, value_cache, block_tables, context_lens)
+    opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
+    ws = _workspace_for(opts, q, key_cache, block_tables, block_size, workspace)
+    d = [describe(out), describe(q), describe(k), describe(v), describe(slot_mapping),
+         describe(key_cache, k_scale), describe(value_cache, v_scale), describe(block_tables),
+         describe(context_lens)]
+    _check(load().paged_attention_decode_append(*[ctypes.byref(x) for x in d], float(scale),
+                                                int(block_size), ctypes.byref(opts),
+                                                _stream(q, stream)))
+    if ws is not None and workspace is None and stream is not None:
+        ws.record_stream(stream)
+    return out
+
+
 def paged_kv_copy_blocks(key_cache, value_cache, block_pairs, *, stream=None) -> None:
     """Copy-on-write: for each int32 row (src, dst) of ``block_pairs`` [P, 2],
     block dst of both pools becomes a copy of block src (see include/pagedkv.h)."""
@@ -253,6 +293,21 @@ def validate_decode_inputs(block_tables: np.ndarray, context_lens: np.ndarray, n
                                              t.shape[1], num_blocks, block_size))
 
 
+def validate_append_slots(slots: np.ndarray, block_tables: np.ndarray, context_lens: np.ndarray,
+                          num_blocks: int, block_size: int) -> None:
+    """Host check of an append call's slots: each is -1 or position len-1 of its
+    own sequence, in a block no other sequence reads; raises PagedKVError."""
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    t = np.ascontiguousarray(block_tables, dtype=np.int32)
+    n = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if t.ndim != 2 or n.shape != (t.shape[0],) or sl.shape != (t.shape[0],):
+        raise ValueError("block_tables must be [S, max_blocks], context_lens and slots [S]")
+    _check(load().pkv_validate_append_slots(sl.ctypes.data_as(ctypes.c_void_p),
+                                            t.ctypes.data_as(ctypes.c_void_p),
+                                            n.ctypes.data_as(ctypes.c_void_p), t.shape[0],
+                                            t.shape[1], num_blocks, block_size))
+
+
 class WriteLaunch:
     """A KV write with its descriptors built once (for tight loops and graph
     capture).  Holds references to the tensors; call to launch on the current
@@ -275,28 +330,54 @@ class WriteLaunch:
 
 
 class DecodeLaunch:
-    """A decode call with descriptors, options and workspace prepared once."""
+    """A decode call with descriptors, options and workspace prepared once.
+
+    append=(k, v, slot_mapping) makes it the one-call decode step
+    (paged_attention_decode_append).  defer_merge=True launches only the
+    streaming kernel; call merge() next on the same stream."""
 
     def __init__(self, out, q, key_cache, value_cache, block_tables, context_lens, scale: float,
                  block_size: int, *, k_scale: float = 1.0, v_scale: float = 1.0,
                  mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
-                 num_workers: int = 0, workspace=None):
+                 num_workers: int = 0, workspace=None, append=None, defer_merge: bool = False):
         _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
-        self._opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
+        self._opts = decode_opts(mode, partition_size, waves_per_group, num_workers, defer_merge)
+        self._merge_opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
         self.workspace = _workspace_for(self._opts, q, key_cache, block_tables, block_size,
                                         workspace)
-        self._keep = (out, q, key_cache, value_cache, block_tables, context_lens)
+        _workspace_for(self._merge_opts, q, key_cache, block_tables, block_size, self.workspace)
+        self._keep = (out, q, key_cache, value_cache, block_tables, context_lens, append)
         self._d = [describe(out), describe(q), describe(key_cache, k_scale),
                    describe(value_cache, v_scale), describe(block_tables), describe(context_lens)]
         self._refs = [ctypes.byref(d) for d in self._d]
+        self._app_refs = None
+        if append is not None:
+            k, v, slots = append
+            _same_device(q, k, v, slots)
+            self._da = [describe(k), describe(v), describe(slots)]
+            r = self._refs
+            self._app_refs = [r[0], r[1]] + [ctypes.byref(d) for d in self._da] + r[2:]
         self._scale = float(scale)
         self._bs = int(block_size)
         self._lib = load()
         self._device = q.device
 
-    def __call__(self, stream=None):
+    def _s(self, stream):
         import torch
         s = stream if stream is not None else torch.cuda.current_stream(self._device)
-        _check(self._lib.paged_attention_decode(*self._refs, self._scale, self._bs,
-                                                ctypes.byref(self._opts),
-                                                ctypes.c_void_p(s.cuda_stream)))
+        return ctypes.c_void_p(s.cuda_stream)
+
+    def __call__(self, stream=None):
+        if self._app_refs is not None:
+            _check(self._lib.paged_attention_decode_append(*self._app_refs, self._scale, self._bs,
+                                                           ctypes.byref(self._opts),
+                                                           self._s(stream)))
+        else:
+            _check(self._lib.paged_attention_decode(*self._refs, self._scale, self._bs,
+                                                    ctypes.byref(self._opts), self._s(stream)))
+
+    def merge(self, stream=None):
+        """Second half of a deferred-merge call (no-op for modes without a merge)."""
+        _check(self._lib.paged_attention_decode_merge(*self._refs, self._scale, self._bs,
+                                                      ctypes.byref(self._merge_opts),
+                                                      self._s(stream)))

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "pkv_internal.h"
@@ -303,10 +304,22 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
   return p.workspace_floats(num_seqs, num_q_heads, num_kv_heads, head_dim) * 4u + p.meta_bytes(num_seqs, num_kv_heads);
 }
 
-pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q, const pkv_tensor* key_cache,
-                                  const pkv_tensor* value_cache, const pkv_tensor* block_tables,
-                                  const pkv_tensor* context_lens, float scale, int32_t block_size,
-                                  const pkv_decode_opts* opts, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The new tokens of an append call: one per sequence.
+struct AppendIn {
+  const pkv_tensor* k;
+  const pkv_tensor* v;
+  const pkv_tensor* slots;
+};
+
+pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
+                       const pkv_tensor* key_cache, const pkv_tensor* value_cache,
+                       const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
+                       int32_t block_size, const pkv_decode_opts* opts, const AppendIn* app,
+                       int32_t phase, void* hip_stream) {
   PKV_TRY(check_tensor(out, "out", 3));
   PKV_TRY(check_tensor(q, "q", 3));
   PKV_TRY(check_tensor(key_cache, "key_cache", 4));
@@ -357,6 +370,29 @@ pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q, const pk
   const pkv_tensor* inputs[] = {q, key_cache, value_cache, block_tables, context_lens};
   for (const pkv_tensor* t : inputs)
     if (overlap(out, t)) return fail(PKV_ERR_LAYOUT, "out overlaps an input");
+  if (app) {
+    PKV_TRY(check_tensor(app->k, "k", 3));
+    PKV_TRY(check_tensor(app->v, "v", 3));
+    PKV_TRY(check_tensor(app->slots, "slot_mapping", 1));
+    if (app->k->dtype != q->dtype || app->v->dtype != q->dtype)
+      return fail(PKV_ERR_DTYPE, "k, v: must have q's dtype");
+    if (app->slots->dtype != PKV_I32) return fail(PKV_ERR_DTYPE, "slot_mapping: must be int32");
+    for (const pkv_tensor* t : {app->k, app->v})
+      if (t->shape[0] != S || t->shape[1] != Hkv || t->shape[2] != D)
+        return fail(PKV_ERR_SHAPE, "k, v: expected [num_seqs, num_kv_heads, head_dim] = [%lld, %lld, %lld]",
+                    (long long)S, (long long)Hkv, (long long)D);
+    if (app->slots->shape[0] != S) return fail(PKV_ERR_SHAPE, "slot_mapping: expected [num_seqs]");
+    if (key_cache->shape[0] * bs > INT32_MAX)
+      return fail(PKV_ERR_UNSUPPORTED, "pool has more than 2^31-1 slots");
+    PKV_TRY(check_align(app->k, "k", 16));
+    PKV_TRY(check_align(app->v, "v", 16));
+    PKV_TRY(check_align(app->slots, "slot_mapping", 4));
+    const pkv_tensor* news[] = {app->k, app->v, app->slots};
+    for (const pkv_tensor* t : news)
+      if (overlap(t, key_cache) || overlap(t, value_cache) || overlap(t, out))
+        return fail(PKV_ERR_LAYOUT, "k, v or slot_mapping overlaps a cache or out");
+    if (overlap(key_cache, value_cache)) return fail(PKV_ERR_LAYOUT, "key_cache and value_cache overlap");
+  }
 
   Plan p;
   PKV_TRY(plan(opts, S, Hq, Hkv, maxb, bs, &p));
@@ -403,9 +439,57 @@ pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q, const pk
   const double kscale = ct == PKV_FP8_E4M3 ? (double)key_cache->scale : 1.0;
   a.qk_scale = (float)((double)scale * log2e * kscale);
   a.v_scale = ct == PKV_FP8_E4M3 ? value_cache->scale : 1.0f;
+  a.phase = phase;
+  if (app) {
+    a.append = 1;
+    a.kn = app->k->data;
+    a.vn = app->v->data;
+    a.slots = static_cast<const int32_t*>(app->slots->data);
+    a.inv_k = ct == PKV_FP8_E4M3 ? 1.0f / key_cache->scale : 1.0f;
+    a.inv_v = ct == PKV_FP8_E4M3 ? 1.0f / value_cache->scale : 1.0f;
+  }
   const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(hip_stream));
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "paged_attention_decode launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+int32_t phase_of(const pkv_decode_opts* opts) {
+  return opts && (opts->flags & PKV_DECODE_DEFER_MERGE) ? pkv::kSplitPhase : pkv::kBothPhases;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q, const pkv_tensor* key_cache,
+                                  const pkv_tensor* value_cache, const pkv_tensor* block_tables,
+                                  const pkv_tensor* context_lens, float scale, int32_t block_size,
+                                  const pkv_decode_opts* opts, void* hip_stream) {
+  return decode_impl("paged_attention_decode", out, q, key_cache, value_cache, block_tables,
+                     context_lens, scale, block_size, opts, nullptr, phase_of(opts), hip_stream);
+}
+
+pkv_status paged_attention_decode_merge(pkv_tensor* out, const pkv_tensor* q,
+                                        const pkv_tensor* key_cache, const pkv_tensor* value_cache,
+                                        const pkv_tensor* block_tables,
+                                        const pkv_tensor* context_lens, float scale,
+                                        int32_t block_size, const pkv_decode_opts* opts,
+                                        void* hip_stream) {
+  return decode_impl("paged_attention_decode_merge", out, q, key_cache, value_cache, block_tables,
+                     context_lens, scale, block_size, opts, nullptr, pkv::kMergePhase, hip_stream);
+}
+
+pkv_status paged_attention_decode_append(pkv_tensor* out, const pkv_tensor* q, const pkv_tensor* k,
+                                         const pkv_tensor* v, const pkv_tensor* slot_mapping,
+                                         pkv_tensor* key_cache, pkv_tensor* value_cache,
+                                         const pkv_tensor* block_tables,
+                                         const pkv_tensor* context_lens, float scale,
+                                         int32_t block_size, const pkv_decode_opts* opts,
+                                         void* hip_stream) {
+  if (!k || !v || !slot_mapping) return fail(PKV_ERR_NULL, "k, v and slot_mapping must not be NULL");
+  const AppendIn app{k, v, slot_mapping};
+  return decode_impl("paged_attention_decode_append", out, q, key_cache, value_cache, block_tables,
+                     context_lens, scale, block_size, opts, &app, phase_of(opts), hip_stream);
 }
 
 pkv_status pkv_validate_slots(const int32_t* slots, int64_t num_tokens, int64_t num_blocks,
@@ -446,6 +530,41 @@ pkv_status pkv_validate_decode_inputs(const int32_t* block_tables, const int32_t
       if (b < 0 || b >= num_blocks)
         return fail(PKV_ERR_RANGE, "block_tables[%d][%lld] = %d outside [0, %lld)", s, (long long)j,
                     b, (long long)num_blocks);
+    }
+  }
+  return ok();
+}
+
+pkv_status pkv_validate_append_slots(const int32_t* slots, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t max_blocks_per_seq, int64_t num_blocks,
+                                     int32_t block_size) {
+  PKV_TRY(pkv_validate_decode_inputs(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                     num_blocks, block_size));
+  if (num_seqs > 0 && !slots) return fail(PKV_ERR_NULL, "slots is NULL");
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (slots[s] < 0) continue;
+    const int64_t n = context_lens[s];
+    if (n == 0) return fail(PKV_ERR_RANGE, "sequence %d has no tokens but slot %d", s, slots[s]);
+    const int64_t pos = n - 1;
+    const int64_t want = (int64_t)block_tables[(int64_t)s * max_blocks_per_seq + pos / block_size] *
+                             block_size + pos % block_size;
+    if (slots[s] != want)
+      return fail(PKV_ERR_RANGE, "slot %d of sequence %d is not position %lld (slot %lld)", slots[s],
+                  s, (long long)pos, (long long)want);
+  }
+  // a block written by one sequence must not be read by another in the same
+  // call (a block still shared has to be copied before the write)
+  std::unordered_map<int32_t, int32_t> writer;
+  for (int32_t s = 0; s < num_seqs; ++s)
+    if (slots[s] >= 0) writer.emplace(slots[s] / block_size, s);
+  for (int32_t s = 0; s < num_seqs && !writer.empty(); ++s) {
+    const int64_t nb = ((int64_t)context_lens[s] + block_size - 1) / block_size;
+    for (int64_t j = 0; j < nb; ++j) {
+      const auto it = writer.find(block_tables[(int64_t)s * max_blocks_per_seq + j]);
+      if (it != writer.end() && it->second != s)
+        return fail(PKV_ERR_RANGE, "block %d is written by sequence %d and read by sequence %d",
+                    it->first, it->second, s);
     }
   }
   return ok();

@@ -32,6 +32,11 @@
 // * Wavefront partials merge through LDS in a fixed order; split-K partials
 //   merge in a second kernel in a fixed order: results are deterministic and
 //   independent of physical block placement.
+// * Append (the step's KV write folded into the decode): the wavefront that
+//   holds a (sequence, KV head) pair's last tile reads the new token's rows
+//   from k / v instead of the pool (a per-lane address choice, no extra
+//   latency) and also stores them to their slot.
+#include "e4m3.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -118,6 +123,21 @@ struct Tile<PKV_BF16, D> {
     for (int j = 0; j < 4; ++j)
       v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * D + VE * (lane & 15));
   }
+  // load() with token r of the tile read from the rows kn / vn instead (r < 0: none)
+  __device__ __forceinline__ void load_sub(const void* kc, const void* vc, int64_t row0, int lane,
+                                           int r, const void* kn, const void* vn, float, float) {
+    const uint16_t* kb = static_cast<const uint16_t*>(kc) + row0 * D;
+    const uint16_t* vb = static_cast<const uint16_t*>(vc) + row0 * D;
+    const uint16_t* kr = (lane & 15) == r ? static_cast<const uint16_t*>(kn) : kb + (lane & 15) * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) k[c] = *reinterpret_cast<const u32x4*>(kr + c * 32 + (lane >> 4) * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * (lane >> 4) + j;
+      const uint16_t* vr = t == r ? static_cast<const uint16_t*>(vn) : vb + t * D;
+      v[j] = *reinterpret_cast<const VRow*>(vr + VE * (lane & 15));
+    }
+  }
   // B operand of the q.K MFMAs: Q row g = lane % 16 with the same d mapping as k[]
   struct QFrag {
     u32x4 q[KC];
@@ -175,6 +195,38 @@ struct Tile<PKV_FP8_E4M3, D> {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * D + VE * (lane & 15));
+  }
+  // load() with token r replaced by the bf16 rows kn / vn, quantized as the
+  // KV write quantizes them (the conversion waits for those loads); r < 0: none
+  __device__ __forceinline__ void load_sub(const void* kc, const void* vc, int64_t row0, int lane,
+                                           int r, const void* kn, const void* vn, float inv_k,
+                                           float inv_v) {
+    load(kc, vc, row0, lane);
+    if (r < 0) return;
+    if ((lane & 15) == r) {
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const uint16_t* src = static_cast<const uint16_t*>(kn) + 16 * ((lane >> 4) + 4 * c);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 8);
+        k[c] = u32x4{e4m3x4_from_bf16x4(lo[0], lo[1], inv_k), e4m3x4_from_bf16x4(lo[2], lo[3], inv_k),
+                     e4m3x4_from_bf16x4(hi[0], hi[1], inv_k), e4m3x4_from_bf16x4(hi[2], hi[3], inv_k)};
+      }
+    }
+    if ((lane >> 4) == (r >> 2)) {
+      const uint16_t* src = static_cast<const uint16_t*>(vn) + VE * (lane & 15);
+      VRow x;
+      if constexpr (VE == 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+        x = VRow{e4m3x4_from_bf16x4(w[0], w[1], inv_v), e4m3x4_from_bf16x4(w[2], w[3], inv_v)};
+      } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(src);
+        x = e4m3x4_from_bf16x4(w[0], w[1], inv_v);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == (r & 3)) v[j] = x;
+    }
   }
   struct QFrag {
     u32x4 q[2 * KC];
@@ -262,6 +314,22 @@ struct Tile<PKV_F32, D> {
       for (int w = 0; w < VE / 4; ++w)
         v[j][w] = *reinterpret_cast<const f32x4*>(vb + (4 * (lane >> 4) + j) * D + VE * (lane & 15) + 4 * w);
   }
+  __device__ __forceinline__ void load_sub(const void* kc, const void* vc, int64_t row0, int lane,
+                                           int r, const void* kn, const void* vn, float, float) {
+    const float* kb = static_cast<const float*>(kc) + row0 * D;
+    const float* vb = static_cast<const float*>(vc) + row0 * D;
+    const float* kr = (lane & 15) == r ? static_cast<const float*>(kn) : kb + (lane & 15) * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) k[c] = *reinterpret_cast<const f32x4*>(kr + 4 * (4 * c + (lane >> 4)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * (lane >> 4) + j;
+      const float* vr = t == r ? static_cast<const float*>(vn) : vb + t * D;
+#pragma unroll
+      for (int w = 0; w < VE / 4; ++w)
+        v[j][w] = *reinterpret_cast<const f32x4*>(vr + VE * (lane & 15) + 4 * w);
+    }
+  }
   struct QFrag {
     f32x4 q[KC];
   };
@@ -337,6 +405,51 @@ struct Softmax {
   f32x4 acc[VE];
 };
 
+// The new token's K and V rows of one KV head, one 16-byte chunk per lane
+// (lanes [0, CH) carry K, [CH, 2 CH) carry V): the KV write of one row, split
+// into its load and its store so the load can be issued early.
+template <int CT, int D>
+struct NewRow {
+  static constexpr int IB = CT == PKV_F32 ? 4 : 2;  // new rows: f32 for f32 pools, else bf16
+  static constexpr int CH = D * IB / 16;            // 16-byte chunks per row, <= 32
+  u32x4 x;
+
+  __device__ __forceinline__ void load(const DecodeArgs& a, int s, int h, int lane) {
+    const int64_t src = (int64_t)s * a.num_kv_heads + h;
+    const int is_v = lane >= CH;
+    const int c = lane - is_v * CH;
+    if (lane < 2 * CH)
+      x = *reinterpret_cast<const u32x4*>(static_cast<const char*>(is_v ? a.vn : a.kn) +
+                                          src * D * IB + c * 16);
+  }
+  __device__ __forceinline__ void store(const DecodeArgs& a, int32_t slot, int h, int lane) const {
+    const int64_t blk = slot / a.block_size;
+    const int64_t dst = (blk * a.num_kv_heads + h) * a.block_size + (slot - blk * a.block_size);
+    const int is_v = lane >= CH;
+    const int c = lane - is_v * CH;
+    if (lane >= 2 * CH) return;
+    char* pool = static_cast<char*>(const_cast<void*>(is_v ? a.vc : a.kc));
+    if constexpr (CT == PKV_FP8_E4M3) {
+      const float inv = is_v ? a.inv_v : a.inv_k;
+      *reinterpret_cast<u32x2*>(pool + dst * D + c * 8) =
+          u32x2{e4m3x4_from_bf16x4(x[0], x[1], inv), e4m3x4_from_bf16x4(x[2], x[3], inv)};
+    } else {
+      *reinterpret_cast<u32x4*>(pool + dst * D * IB + c * 16) = x;
+    }
+  }
+};
+
+// The KV write of sequence s's new token, KV head h, when nothing attends it
+// in this call (an empty sequence).
+template <int CT, int D>
+__device__ __forceinline__ void append_row(const DecodeArgs& a, int s, int h, int lane) {
+  const int32_t slot = a.slots[s];
+  if (slot < 0) return;
+  NewRow<CT, D> r;
+  r.load(a, s, h, lane);
+  r.store(a, slot, h, lane);
+}
+
 // One 16-token tile: scores, masking of tokens >= ctx, online-softmax update, P.V.
 template <int CT, int D>
 __device__ __forceinline__ void process_tile(Tile<CT, D>& t, const typename Tile<CT, D>::QFrag& qf,
@@ -368,7 +481,7 @@ __device__ __forceinline__ void process_tile(Tile<CT, D>& t, const typename Tile
   st.m = m_new;
 }
 
-template <int CT, int D, int NW, int NBUF>
+template <int CT, int D, int NW, int NBUF, bool APPEND>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a) {
   using T = Tile<CT, D>;
   constexpr int VE = T::VE;
@@ -399,6 +512,19 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
 #pragma unroll
   for (int r = 0; r < VE; ++r) st.acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Append: the wavefront holding tile ntiles-1 writes the new token's rows to
+  // their slot (loaded now, stored at the end) and, when that slot is position
+  // ctx-1 (found through the tile's block id), reads the rows from k / v.
+  const int32_t slot_new = APPEND && tile_end == ntiles && ntiles > 0 ? a.slots[s] : -1;
+  const bool owns_last = slot_new >= 0 && wave == ((ntiles - 1 - tile_begin) % kChunkTiles) % NW;
+  const int r_new = (ctx - 1) & 15;
+  const int64_t off_new = ctx > 0 ? (ctx - 1) % bs : 0;
+  const int64_t new_row = (int64_t)s * a.num_kv_heads + hk;
+  const void* kn = static_cast<const QElem<CT>*>(a.kn) + new_row * D;
+  const void* vn = static_cast<const QElem<CT>*>(a.vn) + new_row * D;
+  NewRow<CT, D> nrow;
+  if (owns_last) nrow.load(a, s, hk, lane);
+
   // The partition's tiles are taken in chunks of up to kChunkTiles.  For each
   // chunk the workgroup first copies the block id of every tile into LDS (one
   // cooperative pass over the table), so inside the loop an address costs an
@@ -414,17 +540,20 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
     const int first = c0 + wave;
     const int n_my = first < c1 ? (c1 - first + NW - 1) / NW : 0;
     auto tile_of = [&](int k) { return first + NW * min(k, n_my - 1); };
-    auto row_of = [&](int k) {
-      const int t = tile_of(k);
-      return (int64_t)sm_blk[t - c0] * block_rows + head_rows + ((t * 16) % bs);
-    };
     // Batches of NBUF tiles: all their loads are issued back to back, then the
     // tiles are computed in order, each waiting only for its own loads.  No
     // load is in flight across the loop's back edge.
     for (int k = 0; k < n_my; k += NBUF) {
       T buf[NBUF];
 #pragma unroll
-      for (int j = 0; j < NBUF; ++j) buf[j].load(a.kc, a.vc, row_of(k + j), lane);
+      for (int j = 0; j < NBUF; ++j) {
+        const int t = tile_of(k + j);
+        const int32_t blk = sm_blk[t - c0];
+        const int64_t row = (int64_t)blk * block_rows + head_rows + ((t * 16) % bs);
+        const int rsub = owns_last && k + j < n_my && t == ntiles - 1 &&
+                                 (int64_t)blk * bs + off_new == slot_new ? r_new : -1;
+        buf[j].load_sub(a.kc, a.vc, row, lane, rsub, kn, vn, a.inv_k, a.inv_v);
+      }
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
         if (k + j >= n_my) break;
@@ -432,6 +561,8 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
       }
     }
   }
+  if (owns_last) nrow.store(a, slot_new, hk, lane);
+  if (APPEND && ntiles == 0 && part == 0 && wave == 0) append_row<CT, D>(a, s, hk, lane);
   float m_run = st.m, l_run = st.l;
   f32x4* acc = st.acc;
   // per-lane sums cover tokens 4*(lane/16)+i only; add the four lane groups
@@ -572,8 +703,8 @@ __device__ void write_zero_rows(const DecodeArgs& a, int s, int lane) {
   for (int i = lane; i < n16; i += 64) reinterpret_cast<u32x4*>(o)[i] = u32x4{0, 0, 0, 0};
 }
 
-template <int CT, int D, int NBUF>
-__global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void decode_balanced_kernel(DecodeArgs a) {
+template <int CT, int D, int NBUF, bool APPEND>
+__global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3) void decode_balanced_kernel(DecodeArgs a) {
   using T = Tile<CT, D>;
   constexpr int VE = T::VE;
   const int lane = threadIdx.x & 63;
@@ -605,6 +736,8 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
       const int l = __builtin_ctzll(zmask);
       zmask &= zmask - 1;
       write_zero_rows<CT, D>(a, c + l, lane);
+      if constexpr (APPEND)
+        for (int h = 0; h < Hkv; ++h) append_row<CT, D>(a, c + l, h, lane);
       if (lane < Hkv) {
         a.ws_meta[2 * ((int64_t)(c + l) * Hkv + lane)] = -1;
         a.ws_meta[2 * ((int64_t)(c + l) * Hkv + lane) + 1] = -1;
@@ -689,6 +822,17 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
     Softmax<VE> st;
 #pragma unroll
     for (int r = 0; r < VE; ++r) st.acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Append: the piece holding the pair's last tile writes the new token's rows
+    // to their slot (loaded now, stored at the end) and, when that slot is
+    // position ctx-1, reads them from k / v.
+    const int32_t slot_new = APPEND && te == n ? a.slots[s_cur] : -1;
+    const int r_new = (ctx - 1) & 15;
+    const int64_t off_new = (ctx - 1) % bs;
+    const int64_t new_row = (int64_t)s_cur * Hkv + h;
+    const void* kn = static_cast<const QElem<CT>*>(a.kn) + new_row * D;
+    const void* vn = static_cast<const QElem<CT>*>(a.vn) + new_row * D;
+    NewRow<CT, D> nrow;
+    if (slot_new >= 0) nrow.load(a, s_cur, h, lane);
     // Block ids of the next batch arrive one batch ahead (lane j holds tile k+j);
     // tiles past the piece clamp to its last tile (in bounds, result unused).
     auto entry = [&](int t) { return table[(min(t, te - 1) * 16) / bs]; };
@@ -707,7 +851,10 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
       for (int j = 0; j < NBUF; ++j) {
         const int t = min(k + j, te - 1);
         const int32_t blk = __builtin_amdgcn_readlane(ent, j);
-        buf[j].load(a.kc, a.vc, (int64_t)blk * block_rows + head_rows + ((t * 16) % bs), lane);
+        const int64_t row = (int64_t)blk * block_rows + head_rows + ((t * 16) % bs);
+        const int rsub =
+            slot_new >= 0 && k + j == n - 1 && (int64_t)blk * bs + off_new == slot_new ? r_new : -1;
+        buf[j].load_sub(a.kc, a.vc, row, lane, rsub, kn, vn, a.inv_k, a.inv_v);
       }
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
@@ -715,6 +862,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2) ? 2 : 3) void deco
         process_tile<CT, D>(buf[j], qf, st, (k + j) * 16, ctx, a.qk_scale, lane);
       }
     }
+    if (slot_new >= 0) nrow.store(a, slot_new, h, lane);
     float l_run = st.l;
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
@@ -824,11 +972,18 @@ constexpr int ring_depth() {
 
 template <int CT, int D, int NW>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, ring_depth<CT, D>()>), grid, dim3(NW * 64),
-                     0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_parts == 1) return e;
+  if (a.phase != kMergePhase) {
+    const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+    if (a.append)
+      hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, ring_depth<CT, D>(), true>), grid,
+                         dim3(NW * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, ring_depth<CT, D>(), false>), grid,
+                         dim3(NW * 64), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.phase == kSplitPhase || a.num_parts == 1) return hipSuccess;
   const dim3 rgrid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
   hipLaunchKernelGGL((decode_reduce_kernel<CT, D>), rgrid, dim3(64), 0, stream, a);
   return hipGetLastError();
@@ -836,11 +991,18 @@ hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
 
 template <int CT, int D>
 hipError_t launch_balanced(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.num_workers + 3) / 4));
-  hipLaunchKernelGGL((decode_balanced_kernel<CT, D, ring_depth<CT, D>()>), grid, dim3(256), 0,
-                     stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (a.phase != kMergePhase) {
+    const dim3 grid((unsigned)((a.num_workers + 3) / 4));
+    if (a.append)
+      hipLaunchKernelGGL((decode_balanced_kernel<CT, D, ring_depth<CT, D>(), true>), grid,
+                         dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_balanced_kernel<CT, D, ring_depth<CT, D>(), false>), grid,
+                         dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.phase == kSplitPhase) return hipSuccess;
   const dim3 mgrid((unsigned)(a.num_seqs * a.num_kv_heads), (unsigned)a.group);
   hipLaunchKernelGGL((decode_balanced_merge_kernel<CT, D>), mgrid, dim3(64), 0, stream, a);
   return hipGetLastError();

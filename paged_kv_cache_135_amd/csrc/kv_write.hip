@@ -11,6 +11,7 @@
 // token's K row for all heads is contiguous in the source, so adjacent threads
 // read adjacent 16 bytes; each (head, chunk) lands in a D-element row of the
 // pool.  The work is pure HBM traffic, so there is no LDS staging.
+#include "e4m3.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -20,23 +21,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-
-// f32 -> E4M3 (OCP, "FN" variant): round to nearest, ties to even; |y| >= 448
-// and infinities saturate to +-448; NaN gives 0x7F.
-__device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu;             // NaN
-  if (a >= 0x43e00000u) return sign | 0x7eu;     // >= 448 or inf
-  if (a < 0x3c800000u) {                         // < 2^-6: multiples of 2^-9
-    const float f = __uint_as_float(a) * 512.0f; // exact power-of-two scaling
-    return sign | (uint32_t)__builtin_rintf(f);  // 8 rounds up to the smallest normal
-  }
-  // keep 3 mantissa bits, ties to even, carry into the exponent
-  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
-  return sign | ((r >> 20) - (120u << 3));       // rebias 127 -> 7
-}
 
 __device__ __forceinline__ float f32_from_bf16_bits(uint32_t b) { return __uint_as_float(b << 16); }
 

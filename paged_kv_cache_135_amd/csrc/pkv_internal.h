@@ -27,6 +27,10 @@ struct WriteArgs {
 
 enum DecodeMode : int32_t { kSinglePass = 0, kPartitioned = 1, kBalanced = 2 };
 
+// Which kernels of a decode call to launch: the streaming kernel and its merge
+// (or reduce) kernel, only the first, or only the second.
+enum DecodePhase : int32_t { kBothPhases = 0, kSplitPhase = 1, kMergePhase = 2 };
+
 // One decode call (partition or balanced kernel + optional reduce).
 struct DecodeArgs {
   const void* q;
@@ -56,6 +60,16 @@ struct DecodeArgs {
   int32_t cache_dtype;
   float qk_scale;       // scale * log2(e) (* k scale for E4M3)
   float v_scale;        // 1, or the V scale for E4M3
+  int32_t phase;        // DecodePhase
+  // Append (write folded into the decode): sequence s's new token, rows
+  // [S][Hkv][D] of q's element type, goes to slots[s]; when that slot is
+  // position len-1 of the sequence, the attention takes the row from kn/vn.
+  int32_t append;
+  const void* kn;
+  const void* vn;
+  const int32_t* slots;
+  float inv_k;          // 1.0f / k scale (E4M3 cache only)
+  float inv_v;
 };
 
 // Copy-on-write block copies: for each (src, dst) pair, both pools' block dst

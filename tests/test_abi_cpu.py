@@ -231,3 +231,70 @@ def test_block_pair_validator():
         with pytest.raises(B.PagedKVError) as e:
             B.validate_block_pairs(np.array(bad, np.int32), 8)
         assert e.value.status == 8
+
+
+# ------------------------------------------------------------ append + merge
+def _append(a, k, v, slots):
+    lib = B.load()
+    opts = ctypes.byref(a["opts"]) if a["opts"] is not None else None
+    ref = lambda d: ctypes.byref(d) if d is not None else None
+    return lib.paged_attention_decode_append(ref(a["out"]), ref(a["q"]), ref(k), ref(v), ref(slots),
+                                             ref(a["kc"]), ref(a["vc"]), ref(a["tables"]),
+                                             ref(a["lens"]), a["scale"], a["bs"], opts, None)
+
+
+def _new_rows(dtype=B.PKV_BF16, S=2, H=2, D=128, slot_dtype=B.PKV_I32, k_at=6 << 20):
+    return (desc([S, H, D], dtype, FAKE + k_at), desc([S, H, D], dtype, FAKE + (7 << 20)),
+            desc([S], slot_dtype, FAKE + (8 << 20)))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=B.PKV_F32), 2),         # not q's dtype
+    (dict(S=3), 3),                     # not one row per sequence
+    (dict(H=1), 3),                     # not the pool's KV heads
+    (dict(D=64), 3),
+    (dict(slot_dtype=B.PKV_BF16), 2),
+    (dict(k_at=2 << 20), 4),            # k inside the key pool
+])
+def test_append_rejects_bad_new_rows(kw, status):
+    k, v, s = _new_rows(**kw)
+    assert _append(_decode_args(), k, v, s) == status
+    assert B.load().pkv_last_error()
+
+
+def test_append_rejects_null_rows_and_merge_validates_like_decode():
+    k, v, s = _new_rows()
+    assert _append(_decode_args(), None, v, s) == 1
+    lib = B.load()
+    a = _decode_args(q=desc([2, 8, 128], B.PKV_F32, FAKE + (1 << 20)))
+    ref = lambda d: ctypes.byref(d) if d is not None else None
+    st = lib.paged_attention_decode_merge(ref(a["out"]), ref(a["q"]), ref(a["kc"]), ref(a["vc"]),
+                                          ref(a["tables"]), ref(a["lens"]), a["scale"], a["bs"],
+                                          None, None)
+    assert st == 2
+
+
+def test_append_slot_validator():
+    bs = 16
+    tables = np.array([[3, 1, 0], [2, 5, 9], [4, 6, 7]], np.int32)
+    lens = np.array([40, 17, 0], np.int32)
+    # position len-1: seq 0 -> block 0 (entry 2) offset 7; seq 1 -> block 5 offset 0
+    good = np.array([0 * bs + 7, 5 * bs + 0, -1], np.int32)
+    B.validate_append_slots(good, tables, lens, 10, bs)
+    B.validate_append_slots(np.array([-1, -1, -1], np.int32), tables, lens, 10, bs)
+    bad = [
+        [0 * bs + 6, 5 * bs, -1],    # not position len-1
+        [0 * bs + 7, 5 * bs, 4 * bs],  # empty sequence with a slot
+        [3 * bs + 7, 5 * bs, -1],    # right offset, wrong block
+    ]
+    for b in bad:
+        with pytest.raises(B.PagedKVError) as e:
+            B.validate_append_slots(np.array(b, np.int32), tables, lens, 10, bs)
+        assert e.value.status == 8
+    # a written block that another sequence also reads (a shared block not yet copied)
+    shared = np.array([[3, 1, 0], [2, 0, 9], [4, 6, 7]], np.int32)
+    with pytest.raises(B.PagedKVError):
+        B.validate_append_slots(np.array([7, -1, -1], np.int32), shared, np.array([40, 20, 0], np.int32), 10, bs)
+    # tables themselves are checked too
+    with pytest.raises(B.PagedKVError):
+        B.validate_append_slots(good, tables, np.array([40, 17, 49], np.int32), 10, bs)
