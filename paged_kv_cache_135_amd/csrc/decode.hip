@@ -923,6 +923,20 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
   const int np = w1 - w0 + 1;
   const int64_t slot0 = (int64_t)w0 + seg;
   auto ml = [&](int p) { return a.ws_ml + ((slot0 + p) * G + g) * 2; };
+  // Lane (p4 = lane / 16, c = lane % 16) sums pieces p4, p4 + 4, ... over
+  // columns [VE c, VE c + VE).  Its first two pieces' columns are loaded now,
+  // together with the (max, sum) pairs below, so the two latencies overlap.
+  const int p4 = lane >> 4, c = lane & 15;
+  f32x4 v0[VE / 4], v1[VE / 4];
+  {
+    const float* src0 = a.ws_acc + ((slot0 + p4) * G + g) * D + VE * c;
+    const float* src1 = src0 + 4 * (int64_t)G * D;
+#pragma unroll
+    for (int q = 0; q < VE / 4; ++q) {
+      v0[q] = p4 < np ? *reinterpret_cast<const f32x4*>(src0 + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v1[q] = p4 + 4 < np ? *reinterpret_cast<const f32x4*>(src1 + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
 
   float M = kNegInf;
   for (int p = lane; p < np; p += 64) M = fmaxf(M, ml(p)[0]);
@@ -933,21 +947,27 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
 
-  const int p4 = lane >> 4, c = lane & 15;
   float o[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) o[e] = 0.f;
-  for (int p = p4; p < np; p += 4) {
-    const float f = __builtin_amdgcn_exp2f(ml(p)[0] - M);
-    const float* src = a.ws_acc + ((slot0 + p) * G + g) * D + VE * c;
+  auto add = [&](float f, const f32x4* v) {
 #pragma unroll
     for (int q = 0; q < VE / 4; ++q) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q);
-      o[4 * q] += f * v[0];
-      o[4 * q + 1] += f * v[1];
-      o[4 * q + 2] += f * v[2];
-      o[4 * q + 3] += f * v[3];
+      o[4 * q] += f * v[q][0];
+      o[4 * q + 1] += f * v[q][1];
+      o[4 * q + 2] += f * v[q][2];
+      o[4 * q + 3] += f * v[q][3];
     }
+  };
+  // pieces p4, p4 + 4, ... in order; the first two were loaded up front
+  if (p4 < np) add(__builtin_amdgcn_exp2f(ml(p4)[0] - M), v0);
+  if (p4 + 4 < np) add(__builtin_amdgcn_exp2f(ml(p4 + 4)[0] - M), v1);
+  for (int p = p4 + 8; p < np; p += 4) {
+    const float* src = a.ws_acc + ((slot0 + p) * G + g) * D + VE * c;
+    f32x4 v[VE / 4];
+#pragma unroll
+    for (int q = 0; q < VE / 4; ++q) v[q] = *reinterpret_cast<const f32x4*>(src + 4 * q);
+    add(__builtin_amdgcn_exp2f(ml(p)[0] - M), v);
   }
 #pragma unroll
   for (int e = 0; e < VE; ++e) {
