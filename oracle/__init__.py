@@ -15,8 +15,8 @@ Sources, by page and section:
     "Calculating Physical Block Sizes", the block-size formula.
   * pool_capacity: same section, the worked sizing of the pool from the memory
     left after weights and the runtime reserve.
-  * paged_kv_write / paged_attention_decode / copy_blocks / the E4M3 codec:
-    see oracle.c.
+  * paged_kv_write / paged_attention_decode / paged_attention_prefill /
+    copy_blocks / the E4M3 codec: see oracle.c.
 """
 from __future__ import annotations
 
@@ -68,6 +68,9 @@ def _load():
     lib.orc_paged_attention_decode.restype = ctypes.c_int
     lib.orc_copy_blocks.argtypes = [P, P, i64, i64, P, i64]
     lib.orc_copy_blocks.restype = ctypes.c_int
+    lib.orc_paged_attention_prefill.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, P, P, P, i32,
+                                                i32, i32, i32, i64, i32, i32, f32, f32, f32, P]
+    lib.orc_paged_attention_prefill.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -190,3 +193,31 @@ def copy_blocks(key_cache: np.ndarray, value_cache: np.ndarray, pairs: np.ndarra
     bb = key_cache[0].nbytes if nb else 0
     _check(_load().orc_copy_blocks(_ptr(key_cache), _ptr(value_cache), nb, bb, _ptr(pr),
                                    pr.shape[0]))
+
+
+def paged_attention_prefill(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+                            block_tables: np.ndarray, context_lens: np.ndarray,
+                            query_start: np.ndarray, scale: float, block_size: int,
+                            k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """fp64 chunked-prefill attention; q is [T, Hq, D] with sequence s's queries
+    in rows query_start[s] .. query_start[s+1]-1, at the last positions of its
+    context.  Returns [T, Hq, D] float64."""
+    for a in (q, key_cache, value_cache, block_tables, context_lens, query_start):
+        if not a.flags.c_contiguous:
+            raise ValueError("oracle arrays must be C-contiguous")
+    T, Hq, D = q.shape
+    NB, Hkv, bs, Dc = key_cache.shape
+    S = context_lens.shape[0]
+    if bs != block_size or Dc != D or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if (block_tables.dtype != np.int32 or context_lens.dtype != np.int32
+            or query_start.dtype != np.int32):
+        raise ValueError("tables, lengths and query starts must be int32")
+    if block_tables.shape[0] != S or query_start.shape != (S + 1,) or query_start[-1] != T:
+        raise ValueError("tables must be [S, max_blocks], query_start [S+1] ending at T")
+    out = np.full((T, Hq, D), np.nan, dtype=np.float64)
+    _check(_load().orc_paged_attention_prefill(
+        _ptr(q), _tag(q), _ptr(key_cache), _ptr(value_cache), _tag(key_cache),
+        _ptr(block_tables), _ptr(context_lens), _ptr(query_start), S, Hq, Hkv, D, NB, bs,
+        block_tables.shape[1], float(scale), float(k_scale), float(v_scale), _ptr(out)))
+    return out

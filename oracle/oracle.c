@@ -34,6 +34,17 @@
  *    largest finite 448, smallest subnormal 2^-9.  Encoding rounds to nearest,
  *    ties to even, and saturates finite overflow and infinities to +-448.
  *
+ *  - Chunked-prefill attention (orc_paged_attention_prefill).  "What problem
+ *    does PagedAttention solve for the KV cache in vLLM?" (katajob), section
+ *    "Sharing, the second dividend": blocks that already hold a prompt
+ *    prefix's K/V are reused and that part of prefill is skipped, so the
+ *    remaining prompt tokens attend over the cached prefix through the block
+ *    table; foundry, section "Effect": the boundary between reused and freshly
+ *    prefilled blocks only changes how the reduction is tiled.  Each new query
+ *    token sits at the end of its sequence's context (the chunk's own K/V are
+ *    written first) and attends, causally, to every position up to its own:
+ *    the same softmax(scale * q.K^T) . V as decode, over a shorter prefix.
+ *
  * Everything is plain loops in double precision; no blocking, fusion or
  * reordering.  OpenMP only splits independent (sequence, KV head) pairs.
  */
@@ -316,3 +327,103 @@ int orc_copy_blocks(void* kc, void* vc, int64_t num_blocks, int64_t block_bytes,
 }
 
 int orc_abi_version(void) { return 1; }
+
+/* ---------------------------------------------------------- chunked prefill */
+
+/*
+ * q:                [T][Hq][D], q_dtype (f32 or bf16); rows of sequence s are
+ *                   query_start[s] .. query_start[s+1]-1
+ * query_start:      [S+1], non-decreasing, query_start[0] = 0
+ * context_lens:     [S]; the n_s = query_start[s+1] - query_start[s] queries
+ *                   of sequence s are its positions context_lens[s] - n_s ..
+ *                   context_lens[s] - 1 (n_s <= context_lens[s])
+ * the rest:         as orc_paged_attention_decode
+ * out:              [T][Hq][D] fp64; query i of sequence s, head h, at position
+ *                   p = context_lens[s] - n_s + i:
+ *                   out = sum_{t <= p} softmax_t(scale q.K_t) V_t
+ */
+int orc_paged_attention_prefill(const void* q, int q_dtype, const void* kc, const void* vc,
+                                int cache_dtype, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start,
+                                int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t NB,
+                                int32_t bs, int32_t max_blocks, float scale, float k_scale,
+                                float v_scale, double* out) {
+  int32_t G;
+  int64_t pair;
+  int status = ORC_OK;
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0) return ORC_ERR_ARG;
+  if (Hq % Hkv != 0) return ORC_ERR_ARG;
+  if (q_dtype != ORC_F32 && q_dtype != ORC_BF16) return ORC_ERR_ARG;
+  if (cache_dtype != ORC_F32 && cache_dtype != ORC_BF16 && cache_dtype != ORC_FP8_E4M3)
+    return ORC_ERR_ARG;
+  if (query_start[0] != 0) return ORC_ERR_ARG;
+  G = Hq / Hkv;
+
+  for (int32_t s = 0; s < S; ++s) {
+    int64_t n = context_lens[s];
+    int64_t nq = (int64_t)query_start[s + 1] - query_start[s];
+    if (nq < 0 || nq > n) return ORC_ERR_RANGE;
+    if (n < 0 || (n + bs - 1) / bs > max_blocks) return ORC_ERR_RANGE;
+    for (int64_t j = 0; j < (n + bs - 1) / bs; ++j) {
+      int32_t pb = block_tables[(int64_t)s * max_blocks + j];
+      if (pb < 0 || pb >= NB) return ORC_ERR_RANGE;
+    }
+  }
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (pair = 0; pair < (int64_t)S * Hkv; ++pair) {
+    int32_t s = (int32_t)(pair / Hkv), hk = (int32_t)(pair % Hkv);
+    int64_t n = context_lens[s], t, i;
+    int64_t q0 = query_start[s], nq = (int64_t)query_start[s + 1] - query_start[s];
+    int32_t g, d;
+    double *Kc, *Vc, *z;
+    if (nq == 0) continue;
+    Kc = (double*)malloc(sizeof(double) * (size_t)(n * D));
+    Vc = (double*)malloc(sizeof(double) * (size_t)(n * D));
+    z = (double*)malloc(sizeof(double) * (size_t)n);
+    if (!Kc || !Vc || !z) {
+      free(Kc);
+      free(Vc);
+      free(z);
+#pragma omp atomic write
+      status = ORC_ERR_NOMEM;
+      continue;
+    }
+    /* this KV head's contiguous K and V, through the block table */
+    for (t = 0; t < n; ++t) {
+      int64_t pb = block_tables[(int64_t)s * max_blocks + t / bs];
+      int64_t off = t % bs;
+      for (d = 0; d < D; ++d) {
+        int64_t idx = ((pb * Hkv + hk) * bs + off) * D + d;
+        Kc[t * D + d] = load_elem(kc, idx, cache_dtype, (double)k_scale);
+        Vc[t * D + d] = load_elem(vc, idx, cache_dtype, (double)v_scale);
+      }
+    }
+    for (i = 0; i < nq; ++i) {
+      int64_t row = q0 + i;
+      int64_t pos = n - nq + i; /* keys 0 .. pos are visible */
+      for (g = 0; g < G; ++g) {
+        int32_t h = hk * G + g;
+        double* o = out + (row * Hq + h) * D;
+        double zmax = -INFINITY, wsum = 0.0;
+        for (d = 0; d < D; ++d) o[d] = 0.0;
+        for (t = 0; t <= pos; ++t) {
+          double dot = 0.0;
+          for (d = 0; d < D; ++d) dot += load_elem(q, (row * Hq + h) * D + d, q_dtype, 1.0) * Kc[t * D + d];
+          z[t] = (double)scale * dot;
+          if (z[t] > zmax) zmax = z[t];
+        }
+        for (t = 0; t <= pos; ++t) {
+          double w = exp(z[t] - zmax);
+          wsum += w;
+          for (d = 0; d < D; ++d) o[d] += w * Vc[t * D + d];
+        }
+        for (d = 0; d < D; ++d) o[d] /= wsum;
+      }
+    }
+    free(Kc);
+    free(Vc);
+    free(z);
+  }
+  return status;
+}

@@ -33,7 +33,8 @@ BF16_NAN = np.uint16(0x7FC0)
 FP8_NAN = np.uint8(0x7F)
 F32_NAN_BITS = np.uint32(0x7FC00000)
 
-_STREAM_TABLES, _STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_NEWK, _STREAM_NEWV, _STREAM_CHUNK = range(7)
+_STREAM_TABLES, _STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_NEWK, _STREAM_NEWV, _STREAM_CHUNK, \
+    _STREAM_PREFILL = range(8)
 _CHUNK = 1 << 22
 
 
@@ -121,11 +122,12 @@ class PagedCase:
     slot_mapping: np.ndarray | None = None
     free_blocks: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
     shared_blocks: int = 0
+    query_start: np.ndarray | None = None  # prefill: int32 [S+1] row offsets of q's sequences
     meta: dict = field(default_factory=dict)
 
     @property
     def num_seqs(self) -> int:
-        return int(self.q.shape[0])
+        return int(self.context_lens.shape[0])
 
     @property
     def num_q_heads(self) -> int:
@@ -148,6 +150,26 @@ class PagedCase:
         K and V row for every KV head (block-tail padding not counted)."""
         elem = self.key_cache.dtype.itemsize
         return int(self.context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * \
+            self.head_dim * elem
+
+    def prefill_flops(self) -> int:
+        """Algorithmic flops of one chunked-prefill call: q.K and P.V (2 flops
+        per multiply-add each) for every query head and every key a query
+        sees (keys up to and including its own position)."""
+        qs = self.query_start.astype(np.int64)
+        ctx = self.context_lens.astype(np.int64)
+        nq = qs[1:] - qs[:-1]
+        # queries sit at positions ctx-nq .. ctx-1 and see pos + 1 keys each
+        keys = (nq * (ctx - nq) + nq * (nq + 1) // 2).sum()
+        return int(keys) * self.num_q_heads * self.head_dim * 4
+
+    def prefill_kv_bytes(self) -> int:
+        """K/V bytes a chunked-prefill call must read at least once: every
+        context token of every sequence with queries, each KV head."""
+        qs = self.query_start.astype(np.int64)
+        live = (qs[1:] - qs[:-1]) > 0
+        elem = self.key_cache.dtype.itemsize
+        return int(self.context_lens.astype(np.int64)[live].sum()) * 2 * self.num_kv_heads * \
             self.head_dim * elem
 
     def unique_kv_bytes(self) -> int:
@@ -288,6 +310,32 @@ def build_case(name: str, *, seed: int, context_lens, num_q_heads: int, num_kv_h
     return case
 
 
+def build_prefill_case(name: str, *, seed: int, prefix_lens, chunk_lens, num_q_heads: int,
+                       num_kv_heads: int, head_dim: int, block_size: int, cache_dtype: str,
+                       std: float, scale: float, **kw) -> PagedCase:
+    """A chunked-prefill batch: sequence s already holds ``prefix_lens[s]``
+    tokens and gets ``chunk_lens[s]`` new ones.  The pool (built as in
+    ``build_case``) holds all ``prefix + chunk`` tokens, the chunk's K/V
+    included (they are written before the attention runs).  ``q`` is the packed
+    [sum(chunk), Hq, D] block of the chunks' queries; ``query_start`` [S+1]
+    gives each sequence's first row."""
+    pre = np.asarray(prefix_lens, dtype=np.int64)
+    chk = np.asarray(chunk_lens, dtype=np.int64)
+    if pre.shape != chk.shape or np.any(pre < 0) or np.any(chk < 0):
+        raise ValueError("prefix and chunk lengths must be non-negative and of equal count")
+    case = build_case(name, seed=seed, context_lens=pre + chk, num_q_heads=num_q_heads,
+                      num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                      cache_dtype=cache_dtype, std=std, scale=scale, new_token_step=False, **kw)
+    qs = np.zeros(chk.size + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(chk)
+    in_elem = "f32" if cache_dtype == "f32" else "bf16"
+    q = np.empty((int(qs[-1]), num_q_heads, head_dim), dtype=_np_dtype(in_elem))
+    fill_normal(q, std, seed, _STREAM_PREFILL)
+    case.q = q
+    case.query_start = qs
+    return case
+
+
 # ----------------------------------------------------------- named workloads
 def c1_tiny_f32() -> PagedCase:
     """4 sequences (lengths 1, 17, 40, 100), 4 q / 2 KV heads, head dim 64,
@@ -347,3 +395,17 @@ WORKLOADS = {
     "c4": c4_long_context,
     "c5": c5_fp8,
 }
+
+
+def p1_chunked_prefill(seed: int = 1005, num_seqs: int = 8, chunk: int = 512,
+                       max_prefix: int = 3584) -> PagedCase:
+    """Chunked prefill in the Qwen2.5-7B shape (28 q / 4 KV heads, head dim
+    128, bf16, block size 16): 8 sequences, each with a cached prefix of
+    U[0, 3584] tokens read through its block table and a 512-token chunk of
+    new queries, 4,096 query tokens in all."""
+    rng = np.random.default_rng([seed, _STREAM_TABLES + 100])
+    prefix = rng.integers(0, max_prefix + 1, size=num_seqs)
+    return build_prefill_case("p1_chunked_prefill", seed=seed, prefix_lens=prefix,
+                              chunk_lens=[chunk] * num_seqs, num_q_heads=28, num_kv_heads=4,
+                              head_dim=128, block_size=16, cache_dtype="bf16", std=0.5,
+                              scale=1.0 / math.sqrt(128))
