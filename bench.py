@@ -30,6 +30,7 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MALL_BYTES = 256 * 2 ** 20
 
 
@@ -38,8 +39,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
-    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c4bs32", "c5", "cow"],
-                   help="cow: copy-on-write block copies of the Qwen-shaped pool (its own metric)")
+    p.add_argument("--workload", default="c2",
+                   choices=["c2", "c3", "c4", "c4bs32", "c5", "cow", "p1"],
+                   help="cow: copy-on-write block copies of the Qwen-shaped pool; p1: chunked "
+                        "prefill of 8 x 512 tokens over cached prefixes (each its own metric)")
+    p.add_argument("--prefill-rows", type=int, default=0,
+                   help="p1: (query, head) rows per wavefront (0 = library default)")
     p.add_argument("--mode", default="auto", choices=["single", "partitioned", "balanced", "auto"])
     p.add_argument("--partition", type=int, default=512, help="tokens per partition (partitioned)")
     p.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (0 = default)")
@@ -190,6 +195,99 @@ def bench_copy_blocks(args):
     return 0
 
 
+def bench_prefill(args):
+    """Chunked prefill (p1): one call attends 4,096 new query tokens (8 sequences
+    x 512) causally over their cached prefixes and chunks.  It is a dense
+    contraction, so it is measured in TFLOP/s against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_135_amd as pkv
+    import workloads
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    print("[bench] building workload p1", file=sys.stderr, flush=True)
+    case = workloads.p1_chunked_prefill()
+    flops = case.prefill_flops()
+    kvb = case.prefill_kv_bytes()
+    q, tables, lens, qs = dev(case.q), dev(case.block_tables), dev(case.context_lens), dev(case.query_start)
+    layers = 2
+    pools = [(dev(case.key_cache), dev(case.value_cache))]
+    pools += [(pools[0][0].clone(), pools[0][1].clone()) for _ in range(layers - 1)]
+    out = torch.empty_like(q)
+    mql = int(np.diff(case.query_start).max())
+    calls = [pkv.PrefillLaunch(out, q, kc, vc, tables, lens, qs, mql, case.scale, case.block_size,
+                               rows_per_wave=args.prefill_rows) for kc, vc in pools]
+    for i in range(args.warmup):
+        calls[i % layers]()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for i in range(K):
+        calls[i % layers]()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / K
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        calls[i % layers]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / 1e3 / K
+    achieved = flops / per / 1e12
+    print(f"[bench] prefill: {per*1e6:.1f} us per launch, {achieved:.1f} TFLOP/s, "
+          f"wall {wall*1e6:.1f} us", file=sys.stderr, flush=True)
+    res = {
+        "metric": "chunked prefill paged attention: TFLOP/s (causal, algorithmic flops)",
+        "value": round(flops / wall / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": case.name, "num_seqs": case.num_seqs, "query_tokens": int(q.shape[0]),
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "block_size": case.block_size,
+                   "context_tokens": int(case.context_lens.astype(np.int64).sum()),
+                   "rows_per_wave": args.prefill_rows or None, "layer_pools": layers},
+        "flops_per_step": flops, "kv_bytes_per_step": kvb,
+        "kv_gbps": round(kvb / per / 1e9, 2), "prefill_kernel_us": round(per * 1e6, 2),
+        "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        # bounded sample: the oracle on whole sequences (shortest first) for ~cpu-seconds
+        order = np.argsort(case.context_lens)
+        done_flops, el, used = 0, 0.0, []
+        for s_ in order:
+            a, b = int(case.query_start[s_]), int(case.query_start[s_ + 1])
+            t1 = time.perf_counter()
+            oracle.paged_attention_prefill(
+                np.ascontiguousarray(case.q[a:b]), case.key_cache, case.value_cache,
+                np.ascontiguousarray(case.block_tables[s_:s_ + 1]),
+                np.ascontiguousarray(case.context_lens[s_:s_ + 1]), np.array([0, b - a], np.int32),
+                case.scale, case.block_size)
+            el += time.perf_counter() - t1
+            n, c = int(case.context_lens[s_]), b - a
+            done_flops += (c * (n - c) + c * (c + 1) // 2) * case.num_q_heads * case.head_dim * 4
+            used.append(int(s_))
+            if el >= args.cpu_seconds:
+                break
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        # the oracle splits (sequence, KV head) pairs over threads: one sequence
+        # at a time keeps at most num_kv_heads of them busy
+        res["cpu_baseline"] = {"value": round(done_flops / el / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": min(threads, case.num_kv_heads), "kind": "oracle",
+                               "sample": f"fp64 oracle on sequences {used} of the batch "
+                                         f"({len(used)} of {case.num_seqs}), {el:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -214,6 +312,8 @@ def main():
     pkv.load()
     if args.workload == "cow":
         return bench_copy_blocks(args)
+    if args.workload == "p1":
+        return bench_prefill(args)
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
     case = build_workload(args.workload)
     pool_bytes = case.key_cache.nbytes * 2

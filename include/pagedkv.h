@@ -2,7 +2,8 @@
  * pagedkv.h -- C ABI of libpagedkv.so: the paged KV cache hot path on AMD
  * Instinct MI355X (gfx950).
  *
- * Two device operations:
+ * Device operations (the first two are the hot path; the others build on the
+ * same kernels and pool layout):
  *
  *   paged_kv_write          the slot-mapped KV-cache write.  Each new token's
  *                           key and value rows land in one slot (physical
@@ -26,6 +27,13 @@
  *                           indirection; output is identical given the same
  *                           reduction order) and "Concept" (attention is a
  *                           weighted sum over logically ordered positions).
+ *
+ *   paged_attention_decode_append   the two above in one launch for one new
+ *                           token per sequence.
+ *   paged_attention_prefill chunked prefill: many new query tokens per
+ *                           sequence, causal, the cached prefix read through
+ *                           the block table.
+ *   paged_kv_copy_blocks    copy-on-write copies of whole blocks.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -66,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 #define PKV_MAX_DIMS 4
 
 typedef enum {
@@ -241,6 +249,45 @@ pkv_status paged_attention_decode_append(pkv_tensor* out, const pkv_tensor* q,
                                          int32_t block_size, const pkv_decode_opts* opts,
                                          void* hip_stream);
 
+typedef struct {
+  int32_t rows_per_wave;  /* (query token, query head) rows per wavefront: 0 = library
+                             default (32), 16, 32, or 64 (not for f32) */
+} pkv_prefill_opts;
+
+/*
+ * Chunked-prefill attention over the paged cache: several new query tokens
+ * per sequence, each attending causally to the sequence's cached prefix (read
+ * through the block table) and to the chunk's earlier tokens.  Source: "What
+ * problem does PagedAttention solve for the KV cache in vLLM?", section
+ * "Sharing, the second dividend" (reused prefix blocks skip that part of
+ * prefill; the rest of the prompt attends over them through the table), and
+ * "pipe-paged-block-allocation-kv-cache", section "Effect".
+ *   out              [T, Hq, D], q's element type
+ *   q                [T, Hq, D]; rows query_start_loc[s] .. query_start_loc[s+1]-1
+ *                    are sequence s's chunk of n_s tokens
+ *   query_start_loc  [S + 1] int32, non-decreasing, [0] = 0, [S] = T
+ *   context_lens     [S] int32; the chunk is the last n_s <= len positions: its
+ *                    K/V must already be in the pool (paged_kv_write first)
+ *   max_query_len    >= every n_s; sizes the launch (a longer chunk is still
+ *                    computed correctly, with fewer workgroups than it could use)
+ *   key_cache, value_cache, block_tables, scale, block_size: as for
+ *                    paged_attention_decode
+ *   opts             NULL = defaults
+ * For sequence s, query i at position p = len - n_s + i and query head h:
+ *   out[row,h,:] = sum_{t <= p} softmax_t(scale * q[row,h,:].K[t,:]) V[t,:].
+ * Slots past len and blocks not listed may hold any bits; they never reach out.
+ * Results are deterministic and do not depend on which physical blocks hold
+ * the tokens.  No workspace is needed.
+ * Errors: PKV_ERR_NULL, PKV_ERR_DTYPE, PKV_ERR_SHAPE, PKV_ERR_LAYOUT,
+ * PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ */
+pkv_status paged_attention_prefill(pkv_tensor* out, const pkv_tensor* q,
+                                   const pkv_tensor* key_cache, const pkv_tensor* value_cache,
+                                   const pkv_tensor* block_tables, const pkv_tensor* context_lens,
+                                   const pkv_tensor* query_start_loc, int32_t max_query_len,
+                                   float scale, int32_t block_size, const pkv_prefill_opts* opts,
+                                   void* hip_stream);
+
 /*
  * Copy-on-write block copies.  A physical block listed by several block tables
  * is copied to a fresh block before one branch writes into it ("PagedAttention
@@ -288,6 +335,14 @@ pkv_status pkv_validate_append_slots(const int32_t* slots, const int32_t* block_
                                      const int32_t* context_lens, int32_t num_seqs,
                                      int32_t max_blocks_per_seq, int64_t num_blocks,
                                      int32_t block_size);
+/* pkv_validate_prefill_inputs: the decode inputs as above, query_start_loc
+ * starts at 0, never decreases and ends at num_query_rows, and every chunk is
+ * at most its context length and at most max_query_len. */
+pkv_status pkv_validate_prefill_inputs(const int32_t* query_start_loc, const int32_t* block_tables,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t max_blocks_per_seq, int64_t num_blocks,
+                                       int32_t block_size, int64_t num_query_rows,
+                                       int32_t max_query_len);
 /* pkv_validate_block_pairs: rows with both ids >= 0 name blocks < num_blocks,
  * their destinations are distinct and none is also a source. */
 pkv_status pkv_validate_block_pairs(const int32_t* block_pairs, int64_t num_pairs,

@@ -1,19 +1,21 @@
 """Paged KV cache hot path for AMD Instinct MI355X (gfx950).
 
 * ``paged_kv_write`` / ``paged_attention_decode`` / ``paged_attention_decode_append`` /
-  ``paged_kv_copy_blocks``: HIP kernels behind the C ABI of ``libpagedkv.so`` (declared in
+  ``paged_attention_prefill`` / ``paged_kv_copy_blocks``: HIP kernels behind the C ABI of ``libpagedkv.so`` (declared in
   include/pagedkv.h), called with torch tensors.
 * ``BlockPool``: host-side allocator producing block tables and slot mappings.
 """
-from .binding import (DecodeLaunch, PagedKVError, WriteLaunch, decode_workspace_bytes, load,
-                      paged_attention_decode, paged_attention_decode_append, paged_kv_copy_blocks,
+from .binding import (DecodeLaunch, PagedKVError, PrefillLaunch, WriteLaunch,
+                      decode_workspace_bytes, load, paged_attention_decode,
+                      paged_attention_decode_append, paged_attention_prefill, paged_kv_copy_blocks,
                       paged_kv_write, validate_append_slots, validate_block_pairs,
-                      validate_decode_inputs, validate_slots)
+                      validate_decode_inputs, validate_prefill_inputs, validate_slots)
 from .block_pool import BlockPool, OutOfBlocks, block_bytes, blocks_for_memory
 
 __all__ = [
-    "DecodeLaunch", "WriteLaunch", "PagedKVError", "BlockPool", "OutOfBlocks", "block_bytes",
+    "DecodeLaunch", "PrefillLaunch", "WriteLaunch", "PagedKVError", "BlockPool", "OutOfBlocks", "block_bytes",
     "blocks_for_memory", "decode_workspace_bytes", "load", "paged_attention_decode",
-    "paged_attention_decode_append", "paged_kv_copy_blocks", "paged_kv_write",
-    "validate_append_slots", "validate_block_pairs", "validate_decode_inputs", "validate_slots",
+    "paged_attention_decode_append", "paged_attention_prefill", "paged_kv_copy_blocks",
+    "paged_kv_write", "validate_append_slots", "validate_block_pairs", "validate_decode_inputs",
+    "validate_prefill_inputs", "validate_slots",
 ]

@@ -22,11 +22,12 @@ STATUS_NAMES = {
 }
 EXPORTED = (
     "pkv_abi_version", "pkv_last_error", "paged_kv_write", "paged_attention_decode",
-    "paged_attention_decode_merge", "paged_attention_decode_append",
+    "paged_attention_decode_merge", "paged_attention_decode_append", "paged_attention_prefill",
     "paged_attention_decode_workspace_bytes", "paged_kv_copy_blocks", "pkv_validate_slots",
-    "pkv_validate_decode_inputs", "pkv_validate_append_slots", "pkv_validate_block_pairs",
+    "pkv_validate_decode_inputs", "pkv_validate_append_slots", "pkv_validate_prefill_inputs",
+    "pkv_validate_block_pairs",
 )
-ABI_VERSION = 2
+ABI_VERSION = 3
 DECODE_DEFER_MERGE = 1
 
 
@@ -57,6 +58,10 @@ class PkvDecodeOpts(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("flags", ctypes.c_int32),
     ]
+
+
+class PkvPrefillOpts(ctypes.Structure):
+    _fields_ = [("rows_per_wave", ctypes.c_int32)]
 
 
 DECODE_MODES = {"single": 0, "partitioned": 1, "balanced": 2, "auto": 3}
@@ -108,6 +113,13 @@ def load():
     lib.pkv_validate_append_slots.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int64, ctypes.c_int32]
     lib.pkv_validate_append_slots.restype = ctypes.c_int
+    lib.paged_attention_prefill.argtypes = [T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float,
+                                            ctypes.c_int32, ctypes.POINTER(PkvPrefillOpts), P]
+    lib.paged_attention_prefill.restype = ctypes.c_int
+    lib.pkv_validate_prefill_inputs.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_int32]
+    lib.pkv_validate_prefill_inputs.restype = ctypes.c_int
     lib.paged_attention_decode_workspace_bytes.argtypes = [ctypes.c_int32] * 6 + [
         ctypes.POINTER(PkvDecodeOpts)]
     lib.paged_attention_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -257,6 +269,24 @@ def paged_attention_decode_append(out, q, k, v, slot_mapping, key_cache, value_c
     return out
 
 
+def paged_attention_prefill(out, q, key_cache, value_cache, block_tables, context_lens,
+                            query_start_loc, max_query_len: int, scale: float, block_size: int, *,
+                            k_scale: float = 1.0, v_scale: float = 1.0, rows_per_wave: int = 0,
+                            stream=None):
+    """Chunked-prefill attention into ``out`` [T, Hq, D]: sequence s's queries
+    are rows query_start_loc[s] .. query_start_loc[s+1]-1 of q, at the last
+    positions of its context, attending causally (see include/pagedkv.h)."""
+    _same_device(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc)
+    o = PkvPrefillOpts()
+    o.rows_per_wave = int(rows_per_wave)
+    d = [describe(out), describe(q), describe(key_cache, k_scale), describe(value_cache, v_scale),
+         describe(block_tables), describe(context_lens), describe(query_start_loc)]
+    _check(load().paged_attention_prefill(*[ctypes.byref(x) for x in d], int(max_query_len),
+                                          float(scale), int(block_size), ctypes.byref(o),
+                                          _stream(q, stream)))
+    return out
+
+
 def paged_kv_copy_blocks(key_cache, value_cache, block_pairs, *, stream=None) -> None:
     """Copy-on-write: for each int32 row (src, dst) of ``block_pairs`` [P, 2],
     block dst of both pools becomes a copy of block src (see include/pagedkv.h)."""
@@ -306,6 +336,50 @@ def validate_append_slots(slots: np.ndarray, block_tables: np.ndarray, context_l
                                             t.ctypes.data_as(ctypes.c_void_p),
                                             n.ctypes.data_as(ctypes.c_void_p), t.shape[0],
                                             t.shape[1], num_blocks, block_size))
+
+
+def validate_prefill_inputs(query_start_loc: np.ndarray, block_tables: np.ndarray,
+                            context_lens: np.ndarray, num_blocks: int, block_size: int,
+                            num_query_rows: int, max_query_len: int) -> None:
+    """Host check of a chunked-prefill call's query layout, tables and lengths;
+    raises PagedKVError."""
+    qs = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    t = np.ascontiguousarray(block_tables, dtype=np.int32)
+    n = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if t.ndim != 2 or n.shape != (t.shape[0],) or qs.shape != (t.shape[0] + 1,):
+        raise ValueError("block_tables must be [S, max_blocks], context_lens [S], "
+                         "query_start_loc [S + 1]")
+    _check(load().pkv_validate_prefill_inputs(qs.ctypes.data_as(ctypes.c_void_p),
+                                              t.ctypes.data_as(ctypes.c_void_p),
+                                              n.ctypes.data_as(ctypes.c_void_p), t.shape[0],
+                                              t.shape[1], num_blocks, block_size, num_query_rows,
+                                              max_query_len))
+
+
+class PrefillLaunch:
+    """A chunked-prefill call with its descriptors built once."""
+
+    def __init__(self, out, q, key_cache, value_cache, block_tables, context_lens,
+                 query_start_loc, max_query_len: int, scale: float, block_size: int, *,
+                 k_scale: float = 1.0, v_scale: float = 1.0, rows_per_wave: int = 0):
+        _same_device(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc)
+        self._keep = (out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc)
+        self._d = [describe(out), describe(q), describe(key_cache, k_scale),
+                   describe(value_cache, v_scale), describe(block_tables), describe(context_lens),
+                   describe(query_start_loc)]
+        self._refs = [ctypes.byref(d) for d in self._d]
+        self._opts = PkvPrefillOpts()
+        self._opts.rows_per_wave = int(rows_per_wave)
+        self._mql, self._scale, self._bs = int(max_query_len), float(scale), int(block_size)
+        self._lib = load()
+        self._device = q.device
+
+    def __call__(self, stream=None):
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self._device)
+        _check(self._lib.paged_attention_prefill(*self._refs, self._mql, self._scale, self._bs,
+                                                 ctypes.byref(self._opts),
+                                                 ctypes.c_void_p(s.cuda_stream)))
 
 
 class WriteLaunch:

@@ -253,6 +253,98 @@ pkv_status paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_te
   return ok();
 }
 
+pkv_status paged_attention_prefill(pkv_tensor* out, const pkv_tensor* q,
+                                   const pkv_tensor* key_cache, const pkv_tensor* value_cache,
+                                   const pkv_tensor* block_tables, const pkv_tensor* context_lens,
+                                   const pkv_tensor* query_start_loc, int32_t max_query_len,
+                                   float scale, int32_t block_size, const pkv_prefill_opts* opts,
+                                   void* hip_stream) {
+  PKV_TRY(check_tensor(out, "out", 3));
+  PKV_TRY(check_tensor(q, "q", 3));
+  PKV_TRY(check_tensor(key_cache, "key_cache", 4));
+  PKV_TRY(check_tensor(value_cache, "value_cache", 4));
+  PKV_TRY(check_tensor(block_tables, "block_tables", 2));
+  PKV_TRY(check_tensor(context_lens, "context_lens", 1));
+  PKV_TRY(check_tensor(query_start_loc, "query_start_loc", 1));
+  if (q->dtype != PKV_F32 && q->dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "q: must be f32 or bf16");
+  if (out->dtype != q->dtype) return fail(PKV_ERR_DTYPE, "out: dtype differs from q");
+  if (value_cache->dtype != key_cache->dtype)
+    return fail(PKV_ERR_DTYPE, "value_cache: dtype differs from key_cache");
+  const int32_t ct = key_cache->dtype;
+  if (!((ct == PKV_F32 && q->dtype == PKV_F32) || (ct == PKV_BF16 && q->dtype == PKV_BF16) ||
+        (ct == PKV_FP8_E4M3 && q->dtype == PKV_BF16)))
+    return fail(PKV_ERR_DTYPE, "cache/q dtypes: supported are f32/f32, bf16/bf16, e4m3/bf16");
+  if (block_tables->dtype != PKV_I32 || context_lens->dtype != PKV_I32 ||
+      query_start_loc->dtype != PKV_I32)
+    return fail(PKV_ERR_DTYPE, "block_tables, context_lens and query_start_loc must be int32");
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(PKV_ERR_SHAPE, "out: shape differs from q");
+  for (int i = 0; i < 4; ++i)
+    if (value_cache->shape[i] != key_cache->shape[i])
+      return fail(PKV_ERR_SHAPE, "value_cache: shape differs from key_cache");
+  const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  const int64_t S = context_lens->shape[0];
+  const int64_t Hkv = key_cache->shape[1], bs = key_cache->shape[2];
+  const int64_t maxb = block_tables->shape[1];
+  if (key_cache->shape[3] != D) return fail(PKV_ERR_SHAPE, "key_cache: head_dim differs from q");
+  if (block_tables->shape[0] != S || query_start_loc->shape[0] != S + 1)
+    return fail(PKV_ERR_SHAPE, "block_tables must be [S, max_blocks] and query_start_loc [S + 1]");
+  if (bs != block_size) return fail(PKV_ERR_SHAPE, "block_size %d != key_cache.shape[2] %lld",
+                                    block_size, (long long)bs);
+  if (bs < 16 || bs > 256 || bs % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %lld: must be a multiple of 16 in [16, 256]", (long long)bs);
+  if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %lld: must be 64 or 128", (long long)D);
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0)
+    return fail(PKV_ERR_SHAPE, "num_q_heads %lld must be a positive multiple of num_kv_heads %lld",
+                (long long)Hq, (long long)Hkv);
+  if (S > 65535 || Hkv > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 sequences or KV heads");
+  if (S > 0 && maxb <= 0) return fail(PKV_ERR_SHAPE, "block_tables: needs at least one column");
+  if (maxb * bs > INT32_MAX / 2) return fail(PKV_ERR_UNSUPPORTED, "max_blocks * block_size too large");
+  if (T > INT32_MAX / 2 || T * (Hq / Hkv) > INT32_MAX / 2)
+    return fail(PKV_ERR_UNSUPPORTED, "too many query rows");
+  if (max_query_len < 0 || max_query_len > T)
+    return fail(PKV_ERR_SHAPE, "max_query_len %d outside [0, %lld]", max_query_len, (long long)T);
+  const int32_t rpw = opts && opts->rows_per_wave ? opts->rows_per_wave : 32;
+  if (rpw != 16 && rpw != 32 && (rpw != 64 || ct == PKV_F32))
+    return fail(PKV_ERR_UNSUPPORTED, "rows_per_wave %d: must be 0, 16, 32 or (not f32) 64", rpw);
+  PKV_TRY(check_scale(key_cache, "key_cache"));
+  PKV_TRY(check_scale(value_cache, "value_cache"));
+  PKV_TRY(check_align(out, "out", 16));
+  PKV_TRY(check_align(q, "q", 16));
+  PKV_TRY(check_align(key_cache, "key_cache", 16));
+  PKV_TRY(check_align(value_cache, "value_cache", 16));
+  const pkv_tensor* inputs[] = {q, key_cache, value_cache, block_tables, context_lens, query_start_loc};
+  for (const pkv_tensor* t : inputs)
+    if (overlap(out, t)) return fail(PKV_ERR_LAYOUT, "out overlaps an input");
+  if (S == 0 || T == 0) return ok();
+
+  pkv::PrefillArgs a{};
+  a.q = q->data;
+  a.out = out->data;
+  a.kc = key_cache->data;
+  a.vc = value_cache->data;
+  a.tables = static_cast<const int32_t*>(block_tables->data);
+  a.lens = static_cast<const int32_t*>(context_lens->data);
+  a.qstart = static_cast<const int32_t*>(query_start_loc->data);
+  a.num_seqs = (int32_t)S;
+  a.num_q_heads = (int32_t)Hq;
+  a.num_kv_heads = (int32_t)Hkv;
+  a.group = (int32_t)(Hq / Hkv);
+  a.head_dim = (int32_t)D;
+  a.block_size = (int32_t)bs;
+  a.max_blocks = (int32_t)maxb;
+  a.max_query_len = max_query_len;
+  a.rows_per_wave = rpw;
+  a.cache_dtype = ct;
+  const double log2e = 1.4426950408889634;
+  const double kscale = ct == PKV_FP8_E4M3 ? (double)key_cache->scale : 1.0;
+  a.qk_scale = (float)((double)scale * log2e * kscale);
+  a.v_scale = ct == PKV_FP8_E4M3 ? value_cache->scale : 1.0f;
+  const hipError_t e = pkv::launch_prefill(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "paged_attention_prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 pkv_status paged_kv_copy_blocks(pkv_tensor* key_cache, pkv_tensor* value_cache,
                                 const pkv_tensor* block_pairs, void* hip_stream) {
   PKV_TRY(check_tensor(key_cache, "key_cache", 4));
@@ -567,6 +659,31 @@ pkv_status pkv_validate_append_slots(const int32_t* slots, const int32_t* block_
                     it->first, it->second, s);
     }
   }
+  return ok();
+}
+
+pkv_status pkv_validate_prefill_inputs(const int32_t* query_start_loc, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t max_blocks_per_seq, int64_t num_blocks,
+                                      int32_t block_size, int64_t num_query_rows,
+                                      int32_t max_query_len) {
+  PKV_TRY(pkv_validate_decode_inputs(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                     num_blocks, block_size));
+  if (!query_start_loc) return fail(PKV_ERR_NULL, "query_start_loc is NULL");
+  if (query_start_loc[0] != 0) return fail(PKV_ERR_RANGE, "query_start_loc[0] = %d, not 0", query_start_loc[0]);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t n = (int64_t)query_start_loc[s + 1] - query_start_loc[s];
+    if (n < 0) return fail(PKV_ERR_RANGE, "query_start_loc decreases at sequence %d", s);
+    if (n > context_lens[s])
+      return fail(PKV_ERR_RANGE, "sequence %d has %lld queries but %d tokens", s, (long long)n,
+                  context_lens[s]);
+    if (n > max_query_len)
+      return fail(PKV_ERR_RANGE, "sequence %d has %lld queries > max_query_len %d", s,
+                  (long long)n, max_query_len);
+  }
+  if (query_start_loc[num_seqs] != num_query_rows)
+    return fail(PKV_ERR_RANGE, "query_start_loc[S] = %d, q has %lld rows", query_start_loc[num_seqs],
+                (long long)num_query_rows);
   return ok();
 }
 

@@ -82,7 +82,32 @@ struct CopyArgs {
   int64_t block_bytes;   // one block of one pool
 };
 
+// One chunked-prefill call: the queries of sequence s are rows
+// qstart[s] .. qstart[s+1]-1 of q, at the last positions of its context.
+struct PrefillArgs {
+  const void* q;        // [T][Hq][D]
+  void* out;            // [T][Hq][D]
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  const int32_t* lens;
+  const int32_t* qstart;  // [S + 1]
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks;
+  int32_t max_query_len;  // sizes the grid only; longer chunks are covered by a stride loop
+  int32_t rows_per_wave;  // 16, 32 or 64 (query, head) rows per wavefront
+  int32_t cache_dtype;
+  float qk_scale;         // scale * log2(e) (* k scale for E4M3)
+  float v_scale;
+};
+
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

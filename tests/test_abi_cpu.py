@@ -298,3 +298,50 @@ def test_append_slot_validator():
     # tables themselves are checked too
     with pytest.raises(B.PagedKVError):
         B.validate_append_slots(good, tables, np.array([40, 17, 49], np.int32), 10, bs)
+
+
+# ------------------------------------------------------------- chunked prefill
+def _prefill(out=None, q=None, qs=None, mql=4, bs=16, rpw=0, **over):
+    lib = B.load()
+    a = _decode_args(**over)
+    T = 6
+    out = out if out is not None else desc([T, 8, 128], B.PKV_BF16, FAKE + (9 << 20))
+    q = q if q is not None else desc([T, 8, 128], B.PKV_BF16, FAKE + (10 << 20))
+    qs = qs if qs is not None else desc([3], B.PKV_I32, FAKE + (11 << 20))
+    o = B.PkvPrefillOpts()
+    o.rows_per_wave = rpw
+    ref = lambda d: ctypes.byref(d) if d is not None else None
+    return lib.paged_attention_prefill(ref(out), ref(q), ref(a["kc"]), ref(a["vc"]),
+                                       ref(a["tables"]), ref(a["lens"]), ref(qs), mql, 0.1, bs,
+                                       ctypes.byref(o), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=desc([2], B.PKV_I32, FAKE + (11 << 20))), 3),              # not [S + 1]
+    (dict(qs=desc([3], B.PKV_BF16, FAKE + (11 << 20))), 2),
+    (dict(q=desc([6, 8, 128], B.PKV_F32, FAKE + (10 << 20))), 2),       # q / cache dtypes
+    (dict(out=desc([5, 8, 128], B.PKV_BF16, FAKE + (9 << 20))), 3),
+    (dict(mql=7), 3),                                                   # > T
+    (dict(mql=-1), 3),
+    (dict(bs=32), 3),
+    (dict(rpw=48), 5),
+    (dict(out=desc([6, 8, 128], B.PKV_BF16, FAKE + (10 << 20))), 4),   # out aliases q
+])
+def test_prefill_rejects_bad_descriptors(kw, status):
+    assert _prefill(**kw) == status
+    assert B.load().pkv_last_error()
+
+
+def test_prefill_validator():
+    tables = np.array([[3, 1, 0], [2, 5, 9]], np.int32)
+    lens = np.array([40, 17], np.int32)
+    B.validate_prefill_inputs(np.array([0, 8, 25], np.int32), tables, lens, 10, 16, 25, 17)
+    B.validate_prefill_inputs(np.array([0, 0, 0], np.int32), tables, lens, 10, 16, 0, 0)
+    for qs, T, mql in [([0, 41, 41], 41, 41),   # more queries than tokens
+                       ([1, 8, 25], 25, 17),    # does not start at 0
+                       ([0, 8, 7], 7, 17),      # decreasing
+                       ([0, 8, 25], 26, 17),    # does not end at T
+                       ([0, 8, 25], 25, 16)]:   # chunk > max_query_len
+        with pytest.raises(B.PagedKVError) as e:
+            B.validate_prefill_inputs(np.array(qs, np.int32), tables, lens, 10, 16, T, mql)
+        assert e.value.status == 8
