@@ -40,9 +40,10 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--workload", default="c2",
-                   choices=["c2", "c3", "c4", "c4bs32", "c5", "cow", "p1"],
+                   choices=["c2", "c3", "c4", "c4bs32", "c5", "cow", "p1", "swap"],
                    help="cow: copy-on-write block copies of the Qwen-shaped pool; p1: chunked "
-                        "prefill of 8 x 512 tokens over cached prefixes (each its own metric)")
+                        "prefill of 8 x 512 tokens over cached prefixes; swap: swap-out gather "
+                        "and swap-in scatter of 4,096 blocks (each its own metric)")
     p.add_argument("--prefill-rows", type=int, default=0,
                    help="p1: (query, head) rows per wavefront (0 = library default)")
     p.add_argument("--mode", default="auto", choices=["single", "partitioned", "balanced", "auto"])
@@ -195,6 +196,89 @@ def bench_copy_blocks(args):
     return 0
 
 
+def bench_swap(args):
+    """Swap-out / swap-in of 4,096 blocks (16 KiB per block and pool, K and V:
+    128 MiB) of the Qwen-shaped pool: gather into a device staging buffer and
+    scatter back (HBM-bound: every byte read and written once), and the same
+    with a copy-engine transfer to / from pinned host memory (host-link-bound)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_135_amd as pkv
+    import workloads
+
+    print("[bench] building swap workload", file=sys.stderr, flush=True)
+    case = workloads.c2_qwen_decode()
+    kc = torch.from_numpy(case.key_cache.view(np.int16)).cuda().view(torch.bfloat16)
+    vc = torch.from_numpy(case.value_cache.view(np.int16)).cuda().view(torch.bfloat16)
+    rng = np.random.default_rng(77)
+    n = 4096
+    ids = torch.from_numpy(rng.choice(kc.shape[0], size=n, replace=False).astype(np.int32)).cuda()
+    per_block = kc[0].numel() * kc.element_size()
+    moved = 2 * n * per_block  # K and V bytes per direction
+    res_all = {}
+    shape = (n,) + tuple(kc.shape[1:])
+    sk = torch.empty(shape, dtype=kc.dtype, device="cuda")
+    sv = torch.empty_like(sk)
+    hk = torch.empty(shape, dtype=kc.dtype, pin_memory=True)
+    hv = torch.empty_like(hk)
+    for where in ("device", "pinned"):
+        if where == "device":
+            gather = lambda: pkv.paged_kv_gather_blocks(kc, vc, ids, sk, sv)
+            scatter = lambda: pkv.paged_kv_scatter_blocks(sk, sv, ids, kc, vc)
+        else:  # device staging + copy-engine transfer to / from pinned host memory
+            gather = lambda: pkv.swap_out_to_host(kc, vc, ids, hk, hv, staging=(sk, sv))
+            scatter = lambda: pkv.swap_in_from_host(hk, hv, ids, kc, vc, staging=(sk, sv))
+        for _ in range(args.warmup):
+            gather()
+            scatter()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        K = args.steps if where == "device" else max(1, args.steps // 10)
+        t = {}
+        for name, fn in (("gather", gather), ("scatter", scatter)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(K):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t[name] = e0.elapsed_time(e1) / 1e3 / K
+        res_all[where] = t
+        print(f"[bench] swap via {where}: gather {t['gather']*1e6:.1f} us "
+              f"({moved / t['gather'] / 1e9:.1f} GB/s out), scatter {t['scatter']*1e6:.1f} us",
+              file=sys.stderr, flush=True)
+    dev_g = res_all["device"]["gather"]
+    res = {
+        "metric": "swap-out gather of whole blocks to a device staging buffer: GB/s moved (read + write)",
+        "value": round(2 * moved / dev_g / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dev_g * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap_4096_blocks", "blocks": n, "block_bytes_per_pool": per_block},
+        "device_staging": {k: round(v * 1e6, 2) for k, v in res_all["device"].items()},
+        "pinned_host_staging_us": {k: round(v * 1e6, 2) for k, v in res_all["pinned"].items()},
+        "pinned_host_gbps": {k: round(moved / v / 1e9, 2) for k, v in res_all["pinned"].items()},
+        "roofline": {"kernel": "copy_blocks_kernel (gather)", "bound": "hbm",
+                     "achieved": round(2 * moved / dev_g / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(2 * moved / dev_g / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        ids_h = ids.cpu().numpy()
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            oracle.gather_blocks(case.key_cache, ids_h)
+            oracle.gather_blocks(case.value_cache, ids_h)
+            reps += 1
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(2 * moved * reps / el / 1e9, 3), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"oracle gather of the same 4,096 blocks, {reps} times"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_prefill(args):
     """Chunked prefill (p1): one call attends 4,096 new query tokens (8 sequences
     x 512) causally over their cached prefixes and chunks.  It is a dense
@@ -314,6 +398,8 @@ def main():
         return bench_copy_blocks(args)
     if args.workload == "p1":
         return bench_prefill(args)
+    if args.workload == "swap":
+        return bench_swap(args)
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
     case = build_workload(args.workload)
     pool_bytes = case.key_cache.nbytes * 2

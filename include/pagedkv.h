@@ -34,6 +34,8 @@
  *                           sequence, causal, the cached prefix read through
  *                           the block table.
  *   paged_kv_copy_blocks    copy-on-write copies of whole blocks.
+ *   paged_kv_gather_blocks / paged_kv_scatter_blocks   swap-out / swap-in of
+ *                           whole blocks to and from a staging buffer.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -74,7 +76,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 #define PKV_MAX_DIMS 4
 
 typedef enum {
@@ -307,6 +309,30 @@ pkv_status paged_attention_prefill(pkv_tensor* out, const pkv_tensor* q,
 pkv_status paged_kv_copy_blocks(pkv_tensor* key_cache, pkv_tensor* value_cache,
                                 const pkv_tensor* block_pairs, void* hip_stream);
 
+/*
+ * Swap-out and swap-in of whole blocks (preemption under memory pressure:
+ * "What problem does PagedAttention solve for the KV cache in vLLM?", section
+ * "Operational consequences": a preempted sequence's blocks are freed and its
+ * state swapped out, to be written back into free blocks later).
+ *   key_cache, value_cache  [NB, Hkv, bs, D]
+ *   block_ids               [n] int32; a negative id skips its staging slot
+ *   out_k/out_v, in_k/in_v  [n, Hkv, bs, D], the pools' element type: staging
+ *                           slot i holds block block_ids[i]; device memory (a
+ *                           host copy is then one contiguous copy-engine
+ *                           transfer per buffer, made by the caller)
+ * gather: out[i] = pool[block_ids[i]];  scatter: pool[block_ids[i]] = in[i].
+ * Caller contract (pkv_validate_block_ids on host copies): ids < NB, and for a
+ * scatter no id repeated.  The staging buffers must not overlap the pools.
+ * Errors: PKV_ERR_NULL, PKV_ERR_DTYPE, PKV_ERR_SHAPE, PKV_ERR_LAYOUT (also: a
+ * pool or staging pointer that is not device memory), PKV_ERR_HIP.
+ */
+pkv_status paged_kv_gather_blocks(const pkv_tensor* key_cache, const pkv_tensor* value_cache,
+                                  const pkv_tensor* block_ids, pkv_tensor* out_k,
+                                  pkv_tensor* out_v, void* hip_stream);
+pkv_status paged_kv_scatter_blocks(const pkv_tensor* in_k, const pkv_tensor* in_v,
+                                   const pkv_tensor* block_ids, pkv_tensor* key_cache,
+                                   pkv_tensor* value_cache, void* hip_stream);
+
 /* Workspace bytes paged_attention_decode needs with these sizes and options
  * (0 when none is needed: single pass, or one partition per sequence).
  * Returns 0 as well for invalid arguments. */
@@ -343,6 +369,8 @@ pkv_status pkv_validate_prefill_inputs(const int32_t* query_start_loc, const int
                                        int32_t max_blocks_per_seq, int64_t num_blocks,
                                        int32_t block_size, int64_t num_query_rows,
                                        int32_t max_query_len);
+/* pkv_validate_block_ids: every id >= 0 is < num_blocks and none repeats. */
+pkv_status pkv_validate_block_ids(const int32_t* block_ids, int64_t num_ids, int64_t num_blocks);
 /* pkv_validate_block_pairs: rows with both ids >= 0 name blocks < num_blocks,
  * their destinations are distinct and none is also a source. */
 pkv_status pkv_validate_block_pairs(const int32_t* block_pairs, int64_t num_pairs,

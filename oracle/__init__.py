@@ -71,6 +71,8 @@ def _load():
     lib.orc_paged_attention_prefill.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, P, P, P, i32,
                                                 i32, i32, i32, i64, i32, i32, f32, f32, f32, P]
     lib.orc_paged_attention_prefill.restype = ctypes.c_int
+    lib.orc_move_blocks.argtypes = [P, i64, i64, P, P, i64, ctypes.c_int]
+    lib.orc_move_blocks.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -221,3 +223,25 @@ def paged_attention_prefill(q: np.ndarray, key_cache: np.ndarray, value_cache: n
         _ptr(block_tables), _ptr(context_lens), _ptr(query_start), S, Hq, Hkv, D, NB, bs,
         block_tables.shape[1], float(scale), float(k_scale), float(v_scale), _ptr(out)))
     return out
+
+
+def gather_blocks(pool: np.ndarray, block_ids: np.ndarray) -> np.ndarray:
+    """Swap-out: staging slot i = pool block ids[i] (slots of negative ids stay 0)."""
+    if not pool.flags.c_contiguous:
+        raise ValueError("oracle arrays must be C-contiguous")
+    ids = np.ascontiguousarray(block_ids, dtype=np.int32)
+    out = np.zeros((ids.size,) + pool.shape[1:], dtype=pool.dtype)
+    bb = pool[0].nbytes if pool.shape[0] else 0
+    _check(_load().orc_move_blocks(_ptr(pool), pool.shape[0], bb, _ptr(out), _ptr(ids), ids.size, 1))
+    return out
+
+
+def scatter_blocks(stage: np.ndarray, block_ids: np.ndarray, pool: np.ndarray) -> None:
+    """Swap-in, in place: pool block ids[i] = staging slot i (negative ids skipped)."""
+    if not pool.flags.c_contiguous or not stage.flags.c_contiguous:
+        raise ValueError("oracle arrays must be C-contiguous")
+    ids = np.ascontiguousarray(block_ids, dtype=np.int32)
+    if stage.shape != (ids.size,) + pool.shape[1:] or stage.dtype != pool.dtype:
+        raise ValueError("staging buffer must be [n] + one block")
+    bb = pool[0].nbytes if pool.shape[0] else 0
+    _check(_load().orc_move_blocks(_ptr(pool), pool.shape[0], bb, _ptr(stage), _ptr(ids), ids.size, 0))

@@ -34,6 +34,9 @@
  *    largest finite 448, smallest subnormal 2^-9.  Encoding rounds to nearest,
  *    ties to even, and saturates finite overflow and infinities to +-448.
  *
+ *  - Block copies (orc_copy_blocks: copy-on-write) and moves to and from a
+ *    staging buffer (orc_move_blocks: swap-out / swap-in); see each function.
+ *
  *  - Chunked-prefill attention (orc_paged_attention_prefill).  "What problem
  *    does PagedAttention solve for the KV cache in vLLM?" (katajob), section
  *    "Sharing, the second dividend": blocks that already hold a prompt
@@ -322,6 +325,32 @@ int orc_copy_blocks(void* kc, void* vc, int64_t num_blocks, int64_t block_bytes,
            (size_t)block_bytes);
     memcpy((char*)vc + (int64_t)dst * block_bytes, (const char*)vc + (int64_t)src * block_bytes,
            (size_t)block_bytes);
+  }
+  return ORC_OK;
+}
+
+/*
+ * Swap-out / swap-in ("What problem does PagedAttention solve...", section
+ * "Operational consequences": a preempted sequence's state is swapped out and
+ * later written back into free blocks).  Staging slot i <-> pool block ids[i];
+ * a negative id skips slot i.  gather: stage[i] = pool[ids[i]];
+ * scatter: pool[ids[i]] = stage[i], in increasing i.
+ */
+int orc_move_blocks(void* pool, int64_t num_blocks, int64_t block_bytes, void* stage,
+                    const int32_t* ids, int64_t n, int gather) {
+  int64_t i;
+  if (num_blocks < 0 || block_bytes < 0 || n < 0) return ORC_ERR_ARG;
+  for (i = 0; i < n; ++i)
+    if (ids[i] >= num_blocks) return ORC_ERR_RANGE;
+  for (i = 0; i < n; ++i) {
+    char* blk;
+    char* slot = (char*)stage + i * block_bytes;
+    if (ids[i] < 0) continue;
+    blk = (char*)pool + (int64_t)ids[i] * block_bytes;
+    if (gather)
+      memcpy(slot, blk, (size_t)block_bytes);
+    else
+      memcpy(blk, slot, (size_t)block_bytes);
   }
   return ORC_OK;
 }

@@ -25,9 +25,10 @@ EXPORTED = (
     "paged_attention_decode_merge", "paged_attention_decode_append", "paged_attention_prefill",
     "paged_attention_decode_workspace_bytes", "paged_kv_copy_blocks", "pkv_validate_slots",
     "pkv_validate_decode_inputs", "pkv_validate_append_slots", "pkv_validate_prefill_inputs",
-    "pkv_validate_block_pairs",
+    "pkv_validate_block_pairs", "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
+    "pkv_validate_block_ids",
 )
-ABI_VERSION = 3
+ABI_VERSION = 4
 DECODE_DEFER_MERGE = 1
 
 
@@ -132,6 +133,12 @@ def load():
     lib.paged_kv_copy_blocks.restype = ctypes.c_int
     lib.pkv_validate_block_pairs.argtypes = [P, ctypes.c_int64, ctypes.c_int64]
     lib.pkv_validate_block_pairs.restype = ctypes.c_int
+    lib.paged_kv_gather_blocks.argtypes = [T, T, T, T, T, P]
+    lib.paged_kv_gather_blocks.restype = ctypes.c_int
+    lib.paged_kv_scatter_blocks.argtypes = [T, T, T, T, T, P]
+    lib.paged_kv_scatter_blocks.restype = ctypes.c_int
+    lib.pkv_validate_block_ids.argtypes = [P, ctypes.c_int64, ctypes.c_int64]
+    lib.pkv_validate_block_ids.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -294,6 +301,77 @@ def paged_kv_copy_blocks(key_cache, value_cache, block_pairs, *, stream=None) ->
     dk, dv, dp = describe(key_cache), describe(value_cache), describe(block_pairs)
     _check(load().paged_kv_copy_blocks(ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(dp),
                                        _stream(key_cache, stream)))
+
+
+def _stream_of(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device if t.device.type == "cuda" else None)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def paged_kv_gather_blocks(key_cache, value_cache, block_ids, out_k, out_v, *,
+                           stream=None) -> None:
+    """Swap-out: staging slot i of out_k/out_v ([n, Hkv, bs, D], device memory)
+    receives block block_ids[i] of the pools."""
+    _same_device(key_cache, value_cache, block_ids, out_k, out_v)
+    d = [describe(key_cache), describe(value_cache), describe(block_ids), describe(out_k),
+         describe(out_v)]
+    _check(load().paged_kv_gather_blocks(*[ctypes.byref(x) for x in d],
+                                         _stream_of(key_cache, stream)))
+
+
+def paged_kv_scatter_blocks(in_k, in_v, block_ids, key_cache, value_cache, *,
+                            stream=None) -> None:
+    """Swap-in: block block_ids[i] of the pools receives staging slot i of
+    in_k/in_v ([n, Hkv, bs, D], device memory)."""
+    _same_device(key_cache, value_cache, block_ids, in_k, in_v)
+    d = [describe(in_k), describe(in_v), describe(block_ids), describe(key_cache),
+         describe(value_cache)]
+    _check(load().paged_kv_scatter_blocks(*[ctypes.byref(x) for x in d],
+                                          _stream_of(key_cache, stream)))
+
+
+def swap_out_to_host(key_cache, value_cache, block_ids, host_k, host_v, *, staging=None,
+                     stream=None):
+    """Swap-out to host memory: gather the blocks into a device staging buffer
+    (the kernel), then copy it to host_k/host_v (pinned CPU tensors,
+    [n, Hkv, bs, D]) with the copy engine.  Returns the staging pair, which
+    must stay alive until the copies are done."""
+    import torch
+    n = block_ids.shape[0]
+    shape = (n,) + tuple(key_cache.shape[1:])
+    if staging is None:
+        staging = (torch.empty(shape, dtype=key_cache.dtype, device=key_cache.device),
+                   torch.empty(shape, dtype=key_cache.dtype, device=key_cache.device))
+    paged_kv_gather_blocks(key_cache, value_cache, block_ids, staging[0], staging[1], stream=stream)
+    s = stream if stream is not None else torch.cuda.current_stream(key_cache.device)
+    with torch.cuda.stream(s):
+        host_k.copy_(staging[0], non_blocking=True)
+        host_v.copy_(staging[1], non_blocking=True)
+    return staging
+
+
+def swap_in_from_host(host_k, host_v, block_ids, key_cache, value_cache, *, staging=None,
+                      stream=None):
+    """Swap-in from host memory: copy host_k/host_v into a device staging buffer
+    with the copy engine, then scatter it into the pools' blocks (the kernel)."""
+    import torch
+    if staging is None:
+        staging = (torch.empty(host_k.shape, dtype=key_cache.dtype, device=key_cache.device),
+                   torch.empty(host_v.shape, dtype=key_cache.dtype, device=key_cache.device))
+    s = stream if stream is not None else torch.cuda.current_stream(key_cache.device)
+    with torch.cuda.stream(s):
+        staging[0].copy_(host_k, non_blocking=True)
+        staging[1].copy_(host_v, non_blocking=True)
+    paged_kv_scatter_blocks(staging[0], staging[1], block_ids, key_cache, value_cache, stream=stream)
+    return staging
+
+
+def validate_block_ids(block_ids: np.ndarray, num_blocks: int) -> None:
+    """Host check of swap block ids (range, no repeats); raises PagedKVError."""
+    b = np.ascontiguousarray(block_ids, dtype=np.int32)
+    _check(load().pkv_validate_block_ids(b.ctypes.data_as(ctypes.c_void_p), b.size, num_blocks))
 
 
 def validate_block_pairs(pairs: np.ndarray, num_blocks: int) -> None:

@@ -2,9 +2,10 @@
 
 What it keeps, by page and section:
   * a pool of fixed-size physical blocks carved once, handed out from a free
-    stack ("pipe-paged-block-allocation-kv-cache", section "In and out": the
-    free-block pool is a stack of physical indices into one pre-allocated
-    tensor per layer);
+    list ("pipe-paged-block-allocation-kv-cache", section "In and out": the
+    free-block pool holds physical indices into one pre-allocated tensor per
+    layer); it is kept as a queue so that, with prefix caching, the least
+    recently freed block is the first one overwritten;
   * a block table per sequence mapping logical block j (tokens j*bs ..
     j*bs+bs-1) to a physical id ("PagedAttention, clearly explained"; foundry
     section "Concept": a page table by another name);
@@ -18,7 +19,17 @@ What it keeps, by page and section:
     Memory Sharing"; katajob section "Sharing, the second dividend");
   * pool sizing from the memory left after weights and a reserve, with the
     per-block byte formula ("PagedAttention Memory Management", section
-    "Calculating Physical Block Sizes").
+    "Calculating Physical Block Sizes");
+  * prefix caching ("pipe-paged-block-allocation-kv-cache", section "The
+    knobs": every filled block is hashed so unrelated requests with the same
+    tokens share physical blocks; hashes are per block, so a shared prefix is
+    reused only in whole blocks and a divergence inside a block loses that
+    block, section "Failure modes"); a freed block keeps its hash and can be
+    matched again until it is handed out for other tokens, least recently
+    freed first;
+  * swap-out / swap-in of a preempted sequence (katajob, section "Operational
+    consequences"): its blocks are released after the caller gathers them to
+    a staging buffer, and fresh blocks are taken when it comes back.
 
 Slots handed to the KV write are ``physical_block * block_size + offset``.
 Copy-on-write returns (source, destination) physical block pairs; copying the
@@ -26,13 +37,15 @@ block contents on the device is the caller's job before the write lands.
 """
 from __future__ import annotations
 
+import hashlib
+from collections import deque
 from dataclasses import dataclass, field
 
 import numpy as np
 
 
 class OutOfBlocks(MemoryError):
-    """The free stack cannot satisfy a request (the point where a scheduler
+    """The free list cannot satisfy a request (the point where a scheduler
     would preempt a sequence)."""
 
 
@@ -53,12 +66,24 @@ def blocks_for_memory(free_bytes: int, one_block_bytes: int) -> int:
 class _Seq:
     table: list = field(default_factory=list)
     num_tokens: int = 0
+    hashes: list = field(default_factory=list)   # chain hash of each full block (prefix caching)
+    tail: list = field(default_factory=list)     # token ids of the partly filled last block
+    cached: int = 0                              # prompt tokens found in the prefix cache
+
+
+def block_hash(parent: bytes, tokens) -> bytes:
+    """Chain hash of one full block: its token ids and the hash of the block
+    before it, so equal hashes mean equal prefixes up to this block."""
+    h = hashlib.blake2b(parent, digest_size=16)
+    h.update(np.asarray(tokens, dtype=np.int64).tobytes())
+    return h.digest()
 
 
 class BlockPool:
-    """Free stack + per-sequence block tables + reference counts."""
+    """Free list + per-sequence block tables + reference counts (+ prefix cache)."""
 
-    def __init__(self, num_blocks: int, block_size: int, max_model_len: int | None = None):
+    def __init__(self, num_blocks: int, block_size: int, max_model_len: int | None = None,
+                 enable_prefix_caching: bool = False):
         if num_blocks <= 0 or block_size <= 0:
             raise ValueError("num_blocks and block_size must be positive")
         if max_model_len is not None and num_blocks * block_size < max_model_len:
@@ -68,10 +93,16 @@ class BlockPool:
                 f"{max_model_len} tokens")
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
-        # pop() takes the top: start with block 0 on top
-        self._free = list(range(self.num_blocks - 1, -1, -1))
+        self.prefix_caching = bool(enable_prefix_caching)
+        # free queue: blocks are taken from the left, released ones go to the
+        # right, so the least recently freed (cached) block is reused first
+        self._free = deque(range(self.num_blocks))
         self._ref = np.zeros(self.num_blocks, dtype=np.int64)
         self._seqs: dict = {}
+        self._hash_of: dict = {}    # block -> chain hash of its content
+        self._block_of: dict = {}   # chain hash -> block
+        self._swapped: dict = {}    # sequence -> its _Seq while swapped out
+        self.prefix_hit_blocks = 0
 
     # ------------------------------------------------------------ queries
     @property
@@ -100,9 +131,25 @@ class BlockPool:
     def _pop(self) -> int:
         if not self._free:
             raise OutOfBlocks("no free block")
-        b = self._free.pop()
+        b = self._free.popleft()
         self._ref[b] = 1
+        h = self._hash_of.pop(b, None)  # its cached content is overwritten from now on
+        if h is not None and self._block_of.get(h) == b:
+            del self._block_of[h]
         return b
+
+    def _register(self, b: int, h: bytes) -> None:
+        if h not in self._block_of:
+            self._block_of[h] = b
+            self._hash_of[b] = h
+
+    def _chain(self, token_ids, n_full: int, parent: bytes = b"") -> list:
+        bs = self.block_size
+        out = []
+        for j in range(n_full):
+            parent = block_hash(parent, token_ids[j * bs:(j + 1) * bs])
+            out.append(parent)
+        return out
 
     def _release(self, b: int) -> None:
         self._ref[b] -= 1
@@ -111,41 +158,80 @@ class BlockPool:
         elif self._ref[b] < 0:  # pragma: no cover - bookkeeping bug
             raise AssertionError("negative reference count")
 
-    def allocate(self, seq, n_tokens: int, prefix_of=None, prefix_blocks: int = 0) -> np.ndarray:
+    def allocate(self, seq, n_tokens: int, prefix_of=None, prefix_blocks: int = 0,
+                 token_ids=None) -> np.ndarray:
         """Admit a sequence with ``n_tokens`` prompt tokens; returns their slots.
 
         ``prefix_of``/``prefix_blocks``: the first ``prefix_blocks`` logical
         blocks are the ones another sequence already lists (a shared prompt
-        prefix); only the rest are taken from the pool."""
-        if seq in self._seqs:
+        prefix); only the rest are taken from the pool.
+
+        ``token_ids`` (with prefix caching on): the prompt's token ids.  The
+        longest run of leading full blocks whose chain hashes are cached is
+        reused; ``cached_tokens(seq)`` then tells how many prompt tokens need
+        no prefill."""
+        if seq in self._seqs or seq in self._swapped:
             raise KeyError(f"sequence {seq!r} exists")
         n_tokens = int(n_tokens)
+        bs = self.block_size
         need = self.blocks_needed(n_tokens)
         shared = []
+        hashes = []
+        if token_ids is not None:
+            token_ids = list(token_ids)
+            if len(token_ids) != n_tokens:
+                raise ValueError("token_ids must hold n_tokens ids")
+            if self.prefix_caching:
+                hashes = self._chain(token_ids, n_tokens // bs)
         if prefix_of is not None:
             src = self._seqs[prefix_of]
-            if prefix_blocks > len(src.table) or prefix_blocks * self.block_size > n_tokens:
+            if prefix_blocks > len(src.table) or prefix_blocks * bs > n_tokens:
                 raise ValueError("prefix longer than the source or the new sequence")
-            if prefix_blocks * self.block_size > src.num_tokens:
+            if prefix_blocks * bs > src.num_tokens:
                 raise ValueError("only filled blocks can be shared")
             shared = src.table[:prefix_blocks]
+        elif hashes:
+            for h in hashes:
+                b = self._block_of.get(h)
+                if b is None:
+                    break
+                shared.append(b)
         fresh = need - len(shared)
-        if fresh > len(self._free):
-            raise OutOfBlocks(f"need {fresh} blocks, {len(self._free)} free")
+        revive = sum(1 for b in shared if self._ref[b] == 0)
+        if fresh + revive > len(self._free):
+            raise OutOfBlocks(f"need {fresh} blocks, {len(self._free) - revive} free")
         for b in shared:
+            if self._ref[b] == 0:
+                self._free.remove(b)  # a cached block comes back into use
             self._ref[b] += 1
+        if prefix_of is None:
+            self.prefix_hit_blocks += len(shared)
         s = _Seq(table=list(shared) + [self._pop() for _ in range(fresh)], num_tokens=n_tokens)
+        s.cached = len(shared) * bs if prefix_of is None else 0
+        if token_ids is not None and self.prefix_caching:
+            for j, h in enumerate(hashes):
+                self._register(s.table[j], h)
+            s.hashes = hashes
+            s.tail = token_ids[len(hashes) * bs:]
         self._seqs[seq] = s
         return self._slots(s, 0, n_tokens)
 
-    def append(self, seq, n: int = 1):
+    def cached_tokens(self, seq) -> int:
+        """Prompt tokens of ``seq`` found in the prefix cache at admission."""
+        return self._seqs[seq].cached
+
+    def append(self, seq, n: int = 1, token_ids=None):
         """Grow a sequence by ``n`` tokens.  Returns (slots, cow_pairs): the new
         tokens' slots and the (source, destination) physical blocks to copy
-        before writing (copy-on-write of a shared, partly filled last block)."""
+        before writing (copy-on-write of a shared, partly filled last block).
+        With prefix caching, ``token_ids`` of the new tokens let every block
+        they fill join the cache."""
         s = self._seqs[seq]
         bs = self.block_size
         cow = []
         n = int(n)
+        if token_ids is not None and len(token_ids) != n:
+            raise ValueError("token_ids must hold n ids")
         if n <= 0:
             return np.zeros(0, np.int32), cow
         new_total = s.num_tokens + n
@@ -163,6 +249,14 @@ class BlockPool:
             s.table.append(self._pop())
         first = s.num_tokens
         s.num_tokens = new_total
+        if self.prefix_caching and token_ids is not None and len(s.hashes) * bs + len(s.tail) == first:
+            s.tail = list(s.tail) + list(token_ids)
+            while len(s.tail) >= bs:
+                parent = s.hashes[-1] if s.hashes else b""
+                h = block_hash(parent, s.tail[:bs])
+                self._register(s.table[len(s.hashes)], h)
+                s.hashes.append(h)
+                s.tail = s.tail[bs:]
         return self._slots(s, first, new_total), cow
 
     def fork(self, seq, new_seq) -> None:
@@ -175,10 +269,43 @@ class BlockPool:
         self._seqs[new_seq] = _Seq(table=list(s.table), num_tokens=s.num_tokens)
 
     def free(self, seq) -> None:
-        """Finish a sequence: its blocks go back to the pool once unreferenced."""
-        s = self._seqs.pop(seq)
+        """Finish a sequence: its blocks go back to the pool once unreferenced
+        (with prefix caching, still matchable until handed out again)."""
+        s = self._seqs.pop(seq, None)
+        if s is None:
+            self._swapped.pop(seq)
+            return
         for b in reversed(s.table):
             self._release(b)
+
+    def swap_out(self, seq) -> np.ndarray:
+        """Preempt ``seq``: returns its physical blocks in logical order (the
+        caller gathers them to a staging buffer before anything else is
+        written to the pool) and releases them."""
+        s = self._seqs.pop(seq)
+        ids = np.asarray(s.table, dtype=np.int32)
+        for b in reversed(s.table):
+            self._release(b)
+        s.table = []
+        self._swapped[seq] = s
+        return ids
+
+    def swap_in(self, seq) -> np.ndarray:
+        """Bring ``seq`` back: takes fresh blocks and returns them in logical
+        order (the caller scatters the staged blocks into them)."""
+        s = self._swapped[seq]
+        need = self.blocks_needed(s.num_tokens)
+        if need > len(self._free):
+            raise OutOfBlocks(f"need {need} blocks, {len(self._free)} free")
+        del self._swapped[seq]
+        s.table = [self._pop() for _ in range(need)]
+        for j, h in enumerate(s.hashes):
+            self._register(s.table[j], h)
+        self._seqs[seq] = s
+        return np.asarray(s.table, dtype=np.int32)
+
+    def is_swapped(self, seq) -> bool:
+        return seq in self._swapped
 
     # ---------------------------------------------------- kernel inputs
     def _slots(self, s: _Seq, lo: int, hi: int) -> np.ndarray:
@@ -218,6 +345,8 @@ class BlockPool:
         return {
             "blocks_in_use": in_use,
             "blocks_free": len(self._free),
+            "blocks_cached": len(self._hash_of),
+            "prefix_hit_blocks": self.prefix_hit_blocks,
             "live_fraction": held / (in_use * bs) if in_use else 1.0,
             "waste_per_seq": waste,
             "max_waste": max(waste.values()) if waste else 0,

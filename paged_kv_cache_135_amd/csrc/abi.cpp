@@ -373,14 +373,106 @@ pkv_status paged_kv_copy_blocks(pkv_tensor* key_cache, pkv_tensor* value_cache,
     return fail(PKV_ERR_LAYOUT, "block_pairs overlaps a cache");
   if (P == 0) return ok();
   pkv::CopyArgs a{};
-  a.kc = key_cache->data;
-  a.vc = value_cache->data;
-  a.pairs = static_cast<const int32_t*>(block_pairs->data);
+  a.src_k = key_cache->data;
+  a.src_v = value_cache->data;
+  a.dst_k = key_cache->data;
+  a.dst_v = value_cache->data;
+  a.src_ids = static_cast<const int32_t*>(block_pairs->data);
+  a.dst_ids = a.src_ids + 1;
+  a.id_stride = 2;
+  a.skip_same = 1;
   a.num_pairs = P;
   a.block_bytes = block_bytes;
   const hipError_t e = pkv::launch_copy_blocks(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "paged_kv_copy_blocks launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device memory of the current process (not host memory, pinned or not):
+// the kernels dereference every pointer they are given.
+bool device_memory(const void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // an unknown pointer: clear the query's error
+    return false;
+  }
+  return at.type == hipMemoryTypeDevice;
+}
+
+// Shared checks of a gather (pools -> staging) or scatter (staging -> pools).
+pkv_status block_move(const char* fn, const pkv_tensor* pool_k, const pkv_tensor* pool_v,
+                      const pkv_tensor* stage_k, const pkv_tensor* stage_v,
+                      const pkv_tensor* block_ids, bool gather, void* hip_stream) {
+  PKV_TRY(check_tensor(pool_k, "key_cache", 4));
+  PKV_TRY(check_tensor(pool_v, "value_cache", 4));
+  PKV_TRY(check_tensor(stage_k, gather ? "out_k" : "in_k", 4));
+  PKV_TRY(check_tensor(stage_v, gather ? "out_v" : "in_v", 4));
+  PKV_TRY(check_tensor(block_ids, "block_ids", 1));
+  if (block_ids->dtype != PKV_I32) return fail(PKV_ERR_DTYPE, "block_ids: must be int32");
+  const pkv_tensor* all[] = {pool_v, stage_k, stage_v};
+  for (const pkv_tensor* t : all)
+    if (t->dtype != pool_k->dtype) return fail(PKV_ERR_DTYPE, "pools and staging buffers differ in dtype");
+  if (pool_k->dtype != PKV_F32 && pool_k->dtype != PKV_BF16 && pool_k->dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_DTYPE, "key_cache: must be f32, bf16 or E4M3");
+  const int64_t n = block_ids->shape[0];
+  for (int i = 0; i < 4; ++i) {
+    if (pool_v->shape[i] != pool_k->shape[i]) return fail(PKV_ERR_SHAPE, "value_cache: shape differs from key_cache");
+    if (i > 0 && (stage_k->shape[i] != pool_k->shape[i] || stage_v->shape[i] != pool_k->shape[i]))
+      return fail(PKV_ERR_SHAPE, "staging buffers must be [n, Hkv, bs, D] like the pools");
+  }
+  if (stage_k->shape[0] != n || stage_v->shape[0] != n)
+    return fail(PKV_ERR_SHAPE, "staging buffers must hold one block per id (%lld)", (long long)n);
+  const int64_t bb = pool_k->shape[1] * pool_k->shape[2] * pool_k->shape[3] * elem_bytes(pool_k->dtype);
+  if (bb % 16 != 0) return fail(PKV_ERR_LAYOUT, "one block must be a multiple of 16 bytes");
+  if (n > INT32_MAX / 2) return fail(PKV_ERR_SHAPE, "too many blocks");
+  const pkv_tensor* bufs[] = {pool_k, pool_v, stage_k, stage_v};
+  for (const pkv_tensor* t : bufs) PKV_TRY(check_align(t, "buffer", 16));
+  PKV_TRY(check_align(block_ids, "block_ids", 4));
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(bufs[i], bufs[j])) return fail(PKV_ERR_LAYOUT, "pools and staging buffers overlap");
+  for (const pkv_tensor* t : bufs)
+    if (overlap(block_ids, t)) return fail(PKV_ERR_LAYOUT, "block_ids overlaps a buffer");
+  if (n == 0) return ok();
+  for (const pkv_tensor* t : bufs)
+    if (!device_memory(t->data))
+      return fail(PKV_ERR_LAYOUT, "%s: pools and staging buffers must be device memory", fn);
+  pkv::CopyArgs a{};
+  a.src_k = gather ? pool_k->data : stage_k->data;
+  a.src_v = gather ? pool_v->data : stage_v->data;
+  a.dst_k = gather ? stage_k->data : pool_k->data;
+  a.dst_v = gather ? stage_v->data : pool_v->data;
+  a.src_ids = gather ? static_cast<const int32_t*>(block_ids->data) : nullptr;
+  a.dst_ids = gather ? nullptr : static_cast<const int32_t*>(block_ids->data);
+  a.id_stride = 1;
+  a.skip_same = 0;
+  a.num_pairs = n;
+  a.block_bytes = bb;
+  const hipError_t e = pkv::launch_copy_blocks(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_kv_gather_blocks(const pkv_tensor* key_cache, const pkv_tensor* value_cache,
+                                  const pkv_tensor* block_ids, pkv_tensor* out_k,
+                                  pkv_tensor* out_v, void* hip_stream) {
+  return block_move("paged_kv_gather_blocks", key_cache, value_cache, out_k, out_v, block_ids,
+                    true, hip_stream);
+}
+
+pkv_status paged_kv_scatter_blocks(const pkv_tensor* in_k, const pkv_tensor* in_v,
+                                   const pkv_tensor* block_ids, pkv_tensor* key_cache,
+                                   pkv_tensor* value_cache, void* hip_stream) {
+  return block_move("paged_kv_scatter_blocks", key_cache, value_cache, in_k, in_v, block_ids,
+                    false, hip_stream);
 }
 
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -684,6 +776,23 @@ pkv_status pkv_validate_prefill_inputs(const int32_t* query_start_loc, const int
   if (query_start_loc[num_seqs] != num_query_rows)
     return fail(PKV_ERR_RANGE, "query_start_loc[S] = %d, q has %lld rows", query_start_loc[num_seqs],
                 (long long)num_query_rows);
+  return ok();
+}
+
+pkv_status pkv_validate_block_ids(const int32_t* block_ids, int64_t num_ids, int64_t num_blocks) {
+  if (num_ids < 0 || num_blocks < 0) return fail(PKV_ERR_SHAPE, "negative sizes");
+  if (num_ids > 0 && !block_ids) return fail(PKV_ERR_NULL, "block_ids is NULL");
+  std::vector<int32_t> ids;
+  for (int64_t i = 0; i < num_ids; ++i) {
+    if (block_ids[i] < 0) continue;
+    if (block_ids[i] >= num_blocks)
+      return fail(PKV_ERR_RANGE, "block id %d outside the pool of %lld blocks", block_ids[i],
+                  (long long)num_blocks);
+    ids.push_back(block_ids[i]);
+  }
+  std::sort(ids.begin(), ids.end());
+  for (size_t i = 1; i < ids.size(); ++i)
+    if (ids[i] == ids[i - 1]) return fail(PKV_ERR_RANGE, "block id %d repeated", ids[i]);
   return ok();
 }
 

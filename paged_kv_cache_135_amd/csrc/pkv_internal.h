@@ -72,14 +72,22 @@ struct DecodeArgs {
   float inv_v;
 };
 
-// Copy-on-write block copies: for each (src, dst) pair, both pools' block dst
-// becomes a copy of block src.
+// Whole-block moves between pools and staging buffers: for each p < num_pairs,
+// block src_ids[p * id_stride] of src becomes block dst_ids[p * id_stride] of
+// dst, for the K and the V buffers.  A null id array means the identity (p).
+// Negative ids skip the pair; with skip_same, src == dst skips it too (an
+// in-place copy-on-write pair naming one block twice).
 struct CopyArgs {
-  void* kc;
-  void* vc;
-  const int32_t* pairs;  // [num_pairs][2]
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int32_t* src_ids;
+  const int32_t* dst_ids;
+  int32_t id_stride;
+  int32_t skip_same;
   int64_t num_pairs;
-  int64_t block_bytes;   // one block of one pool
+  int64_t block_bytes;   // one block of one buffer
 };
 
 // One chunked-prefill call: the queries of sequence s are rows

@@ -345,3 +345,34 @@ def test_prefill_validator():
         with pytest.raises(B.PagedKVError) as e:
             B.validate_prefill_inputs(np.array(qs, np.int32), tables, lens, 10, 16, T, mql)
         assert e.value.status == 8
+
+
+# ------------------------------------------------------------- swap moves
+def test_gather_scatter_reject_bad_descriptors():
+    lib = B.load()
+    kc = desc([8, 2, 16, 64], B.PKV_BF16, FAKE)
+    vc = desc([8, 2, 16, 64], B.PKV_BF16, FAKE + (1 << 20))
+    ids = desc([3], B.PKV_I32, FAKE + (2 << 20))
+    ok_k = desc([3, 2, 16, 64], B.PKV_BF16, FAKE + (3 << 20))
+    ok_v = desc([3, 2, 16, 64], B.PKV_BF16, FAKE + (4 << 20))
+    ref = lambda x: ctypes.byref(x) if x is not None else None
+    g = lambda a, b, c, d, e: lib.paged_kv_gather_blocks(ref(a), ref(b), ref(c), ref(d), ref(e), None)
+    sc = lambda a, b, c, d, e: lib.paged_kv_scatter_blocks(ref(a), ref(b), ref(c), ref(d), ref(e), None)
+    assert g(kc, vc, None, ok_k, ok_v) == 1
+    assert g(kc, vc, desc([3], B.PKV_BF16, FAKE + (2 << 20)), ok_k, ok_v) == 2
+    assert g(kc, vc, ids, desc([3, 2, 16, 64], B.PKV_F32, FAKE + (3 << 20)), ok_v) == 2
+    assert g(kc, vc, ids, desc([4, 2, 16, 64], B.PKV_BF16, FAKE + (3 << 20)), ok_v) == 3
+    assert g(kc, vc, ids, desc([3, 2, 32, 64], B.PKV_BF16, FAKE + (3 << 20)), ok_v) == 3
+    assert g(kc, vc, ids, desc([3, 2, 16, 64], B.PKV_BF16, FAKE + 4096), ok_v) == 4  # inside the pool
+    assert sc(ok_k, ok_v, ids, kc, desc([8, 2, 16, 32], B.PKV_BF16, FAKE + (1 << 20))) == 3
+    e = desc([0], B.PKV_I32, 0)
+    z = desc([0, 2, 16, 64], B.PKV_BF16, 0)
+    assert g(kc, vc, e, z, desc([0, 2, 16, 64], B.PKV_BF16, 0)) == 0  # nothing to move
+
+
+def test_block_id_validator():
+    B.validate_block_ids(np.array([3, -1, 0, 7], np.int32), 8)
+    for bad in ([8], [1, 1], [2, -1, 2]):
+        with pytest.raises(B.PagedKVError) as e:
+            B.validate_block_ids(np.array(bad, np.int32), 8)
+        assert e.value.status == 8

@@ -141,3 +141,95 @@ def test_tables_and_slots_agree():
         for p in rng.integers(0, n, size=5):
             p = int(p)
             assert pool.slot(i, p) == tables[i, p // 16] * 16 + p % 16
+
+
+# ------------------------------------------------------------ prefix caching
+def test_block_granular_prefix_reuse_matches_the_pages_example():
+    """[foundry] "Failure modes": with block_size 32 a shared 1,000-token
+    prefix reuses at most 992 tokens."""
+    pool = BlockPool(200, 32, enable_prefix_caching=True)
+    rng = np.random.default_rng(0)
+    prefix = list(rng.integers(0, 50000, 1000))
+    a = prefix + list(rng.integers(0, 50000, 300))
+    b = prefix + list(rng.integers(0, 50000, 17))
+    pool.allocate("a", len(a), token_ids=a)
+    assert pool.cached_tokens("a") == 0
+    pool.allocate("b", len(b), token_ids=b)
+    assert pool.cached_tokens("b") == 992
+    assert pool.table("b")[:31] == pool.table("a")[:31]
+    assert pool.table("b")[31] != pool.table("a")[31]
+    assert all(pool.refcount(x) == 2 for x in pool.table("a")[:31])
+
+
+def test_divergence_inside_a_block_loses_that_block():
+    pool = BlockPool(100, 32, enable_prefix_caching=True)
+    base = list(range(1000))
+    other = list(base)
+    other[500] = -7  # inside block 15 (tokens 480..511)
+    pool.allocate("a", 1000, token_ids=base)
+    pool.allocate("b", 1000, token_ids=other)
+    assert pool.cached_tokens("b") == 15 * 32
+    assert pool.table("b")[:15] == pool.table("a")[:15]
+
+
+def test_freed_blocks_stay_matchable_until_reused_for_other_tokens():
+    pool = BlockPool(12, 16, enable_prefix_caching=True)
+    t = list(range(100, 164))  # 4 full blocks
+    pool.allocate("a", 64, token_ids=t)
+    first = pool.table("a")
+    pool.free("a")
+    pool.allocate("b", 64, token_ids=t)
+    assert pool.cached_tokens("b") == 64 and pool.table("b") == first
+    pool.free("b")
+    # 8 blocks never used come off the free list first (least recently freed) ...
+    pool.allocate("c", 8 * 16, token_ids=list(range(5000, 5128)))
+    pool.allocate("d", 64, token_ids=t)
+    assert pool.cached_tokens("d") == 64
+    pool.free("d")
+    pool.free("c")
+    # ... then the cached ones are overwritten by new tokens and stop matching
+    pool.allocate("e", 12 * 16, token_ids=list(range(9000, 9192)))
+    pool.free("e")
+    pool.allocate("f", 64, token_ids=t)
+    assert pool.cached_tokens("f") == 0
+
+
+def test_appended_tokens_fill_blocks_that_join_the_cache():
+    pool = BlockPool(20, 16, enable_prefix_caching=True)
+    prompt = list(range(20))
+    pool.allocate("a", 20, token_ids=prompt)
+    gen = list(range(1000, 1030))
+    for tok in gen:
+        pool.append("a", 1, token_ids=[tok])
+    full = prompt + gen  # 50 tokens: 3 full blocks
+    pool.allocate("b", 48, token_ids=full[:48])
+    assert pool.cached_tokens("b") == 48
+    assert pool.table("b") == pool.table("a")[:3]
+
+
+def test_prefix_caching_off_shares_nothing():
+    pool = BlockPool(20, 16)
+    pool.allocate("a", 40, token_ids=list(range(40)))
+    pool.allocate("b", 40, token_ids=list(range(40)))
+    assert pool.cached_tokens("b") == 0
+    assert not set(pool.table("a")) & set(pool.table("b"))
+
+
+# ------------------------------------------------------------------- swapping
+def test_swap_out_releases_and_swap_in_takes_fresh_blocks():
+    pool = BlockPool(10, 16)
+    pool.allocate("a", 40)
+    pool.allocate("b", 16)
+    ids = pool.swap_out("a")
+    assert list(ids) == [0, 1, 2] and pool.num_free == 9 and pool.is_swapped("a")
+    pool.allocate("c", 48)  # reuses the released blocks
+    back = pool.swap_in("a")
+    assert len(back) == 3
+    assert not set(back) & (set(pool.table("c")) | set(pool.table("b")))
+    assert pool.num_tokens("a") == 40 and pool.slot("a", 39) == back[2] * 16 + 7
+    pool.swap_out("b")
+    pool.swap_out("c")
+    pool.allocate("d", pool.num_free * 16)  # takes every free block
+    with pytest.raises(OutOfBlocks):
+        pool.swap_in("b")
+    assert pool.is_swapped("b")

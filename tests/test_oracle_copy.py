@@ -82,3 +82,35 @@ def _contiguous(tokens, bs):
     pad[:T] = tokens
     kc[:] = pad.reshape(nb, bs, H, D).transpose(0, 2, 1, 3)
     return kc, kc.copy(), np.arange(nb, dtype=np.int32)[None], np.array([T], np.int32)
+
+
+# ----------------------------------------------------- swap-out / swap-in moves
+def test_gather_and_scatter_match_numpy_indexing():
+    rng = np.random.default_rng(11)
+    pool = rng.integers(0, 2**16, size=(9, 2, 16, 8), dtype=np.uint16)
+    ids = np.array([4, 0, -1, 8, 3], np.int32)
+    got = oracle.gather_blocks(pool, ids)
+    live = ids >= 0
+    assert np.array_equal(got[live], pool[ids[live]])
+    assert not got[~live].any()
+    stage = rng.integers(0, 2**16, size=(5, 2, 16, 8), dtype=np.uint16)
+    want = pool.copy()
+    want[ids[live]] = stage[live]
+    oracle.scatter_blocks(stage, ids, pool)
+    assert np.array_equal(pool, want)
+
+
+def test_swap_round_trip_restores_a_sequence_in_new_blocks():
+    rng = np.random.default_rng(12)
+    pool = rng.standard_normal((12, 2, 16, 4)).astype(np.float32)
+    before = pool[[2, 7, 5]].copy()
+    staged = oracle.gather_blocks(pool, np.array([2, 7, 5], np.int32))
+    pool[:] = np.nan  # the blocks are reused for other tokens meanwhile
+    oracle.scatter_blocks(staged, np.array([9, 0, 11], np.int32), pool)
+    assert np.array_equal(pool[[9, 0, 11]], before)
+
+
+def test_move_range_errors():
+    pool = np.zeros((4, 1, 16, 4), np.float32)
+    with pytest.raises(ValueError):
+        oracle.gather_blocks(pool, np.array([4], np.int32))
