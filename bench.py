@@ -44,6 +44,9 @@ def parse():
                    help="cow: copy-on-write block copies of the Qwen-shaped pool; p1: chunked "
                         "prefill of 8 x 512 tokens over cached prefixes; swap: swap-out gather "
                         "and swap-in scatter of 4,096 blocks (each its own metric)")
+    p.add_argument("--shared-prefix", action="store_true",
+                   help="c3: decode with paged_attention_decode_shared_prefix (the shared "
+                        "prefix computed once for all sequences)")
     p.add_argument("--prefill-rows", type=int, default=0,
                    help="p1: (query, head) rows per wavefront (0 = library default)")
     p.add_argument("--mode", default="auto", choices=["single", "partitioned", "balanced", "auto"])
@@ -420,6 +423,13 @@ def main():
                                         case.block_size, args.mode, args.partition, args.workers)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     step = args.step
+    prefix_len = 0
+    if args.shared_prefix:
+        if not case.shared_blocks:
+            print("--shared-prefix needs a workload with shared prefix blocks (c3)", file=sys.stderr)
+            return 2
+        prefix_len = case.shared_blocks * case.block_size
+        step = "split"  # the shared-prefix decode takes no appended tokens
     if step == "auto":
         step = "split"
         if case.slot_mapping.shape[0] == case.num_seqs:
@@ -434,7 +444,14 @@ def main():
                partition_size=args.partition, waves_per_group=args.waves,
                num_workers=args.workers, workspace=ws)
 
+    if prefix_len:
+        dkw["mode"] = "auto"
+        dkw["workspace"] = None
+
     def decode_launch(kc, vc, defer):
+        if prefix_len:  # its kernels launch together: time the whole call
+            return pkv.DecodeLaunch(out, q, kc, vc, tables, lens, case.scale, case.block_size,
+                                    prefix_len=prefix_len, **dkw)
         return pkv.DecodeLaunch(out, q, kc, vc, tables, lens, case.scale, case.block_size,
                                 append=(knew, vnew, slots) if append else None,
                                 defer_merge=defer, **dkw)
@@ -462,7 +479,8 @@ def main():
             ev[i][1].record(stream)
             split_decodes[li]()
             ev[i][2].record(stream)
-            split_decodes[li].merge()
+            if not prefix_len:
+                split_decodes[li].merge()
             ev[i][3].record(stream)
 
     if args.copy_calibration_mib:
@@ -525,7 +543,9 @@ def main():
     kv = case.kv_bytes()
     traffic, traffic_kernel = measured_traffic(case.name)
     value = kv / (ms_per_step / 1e3) / 1e9
-    achieved = kv / main_s / 1e9
+    # HBM roofline: bytes that must come from memory; a shared prefix counts once
+    roof_bytes = case.unique_kv_bytes() if case.shared_blocks else kv
+    achieved = roof_bytes / main_s / 1e9
     print(f"[bench] step {step}: streaming kernel {main_s*1e6:.1f} us per launch back to back "
           f"({main_ms.mean()*1e3:.1f} us between events around each, p10 "
           f"{np.percentile(main_ms,10)*1e3:.1f}, p90 {np.percentile(main_ms,90)*1e3:.1f}), "
@@ -560,6 +580,7 @@ def main():
             "layer_pools": layers,
             "graph": bool(args.graph),
             "step": step,
+            "shared_prefix_tokens": prefix_len or None,
         },
         "kv_bytes_per_step": kv,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
@@ -570,7 +591,8 @@ def main():
         "merge_us": round(float(merge_ms.mean()) * 1e3, 2),
         "write_us": round(float(wr_ms.mean()) * 1e3, 2) if not append else 0.0,
         "roofline": {
-            "kernel": "streaming decode kernel (" + (
+            "kernel": "shared-prefix decode call (prefix + tail + merge kernels)" if prefix_len
+            else "streaming decode kernel (" + (
                 "append, " if append else "") + {
                 "single": "single pass", "partitioned": "partitions",
                 "balanced": "balanced split", "auto": "auto mode"}[args.mode] + ")",

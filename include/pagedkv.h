@@ -30,6 +30,8 @@
  *
  *   paged_attention_decode_append   the two above in one launch for one new
  *                           token per sequence.
+ *   paged_attention_decode_shared_prefix   decode for sequences that share a
+ *                           prefix: the shared part computed once (cascade).
  *   paged_attention_prefill chunked prefill: many new query tokens per
  *                           sequence, causal, the cached prefix read through
  *                           the block table.
@@ -76,7 +78,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 #define PKV_MAX_DIMS 4
 
 typedef enum {
@@ -221,6 +223,35 @@ pkv_status paged_attention_decode_merge(pkv_tensor* out, const pkv_tensor* q,
                                         void* hip_stream);
 
 /*
+ * Decode attention for a batch whose sequences all begin with the same
+ * prefix_len tokens, held once in shared physical blocks (a system prompt or a
+ * forked prompt: "PagedAttention Memory Management", section "Complex
+ * Topologies and Memory Sharing"; "What problem does PagedAttention solve...",
+ * section "Sharing, the second dividend").  The shared part is computed once
+ * for all sequences (their query heads against the prefix keys on the matrix
+ * cores, the prefix K/V read once), each sequence's own tail streams through
+ * the balanced split, and the partial softmax states are merged in a fixed
+ * order (prefix pieces, then tail pieces).
+ *   prefix_len    a positive multiple of block_size; every table's first
+ *                 prefix_len / block_size entries name the same blocks and
+ *                 every context_len >= prefix_len (pkv_validate_shared_prefix)
+ *   the rest      as paged_attention_decode; opts->mode must be AUTO or
+ *                 BALANCED (or opts NULL), num_workers is honoured,
+ *                 PKV_DECODE_DEFER_MERGE is refused, and the workspace must hold
+ *                 paged_attention_decode_shared_prefix_workspace_bytes()
+ * Result: attention over each whole context, equal within rounding to
+ * paged_attention_decode on the same inputs; deterministic.
+ * Errors: as paged_attention_decode.
+ */
+pkv_status paged_attention_decode_shared_prefix(pkv_tensor* out, const pkv_tensor* q,
+                                                const pkv_tensor* key_cache,
+                                                const pkv_tensor* value_cache,
+                                                const pkv_tensor* block_tables,
+                                                const pkv_tensor* context_lens, int32_t prefix_len,
+                                                float scale, int32_t block_size,
+                                                const pkv_decode_opts* opts, void* hip_stream);
+
+/*
  * One decode step in one call: the KV write of each sequence's new token (the
  * token the step attends last) followed by decode attention, with the write
  * folded into the decode launch.  Same sources as the two operations: the new
@@ -341,6 +372,14 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
                                               int32_t max_blocks_per_seq, int32_t block_size,
                                               const pkv_decode_opts* opts);
 
+/* Workspace bytes of paged_attention_decode_shared_prefix (0 for invalid
+ * arguments). */
+size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                            int32_t num_kv_heads, int32_t head_dim,
+                                                            int32_t max_blocks_per_seq,
+                                                            int32_t block_size, int32_t prefix_len,
+                                                            const pkv_decode_opts* opts);
+
 /*
  * Opt-in host-side checks of the caller contract, on HOST copies.
  * pkv_validate_slots: every slot < num_blocks * block_size and no slot
@@ -369,6 +408,11 @@ pkv_status pkv_validate_prefill_inputs(const int32_t* query_start_loc, const int
                                        int32_t max_blocks_per_seq, int64_t num_blocks,
                                        int32_t block_size, int64_t num_query_rows,
                                        int32_t max_query_len);
+/* pkv_validate_shared_prefix: the decode inputs as above, every context
+ * length >= prefix_len and every table lists the same prefix blocks. */
+pkv_status pkv_validate_shared_prefix(const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int32_t block_size, int32_t prefix_len);
 /* pkv_validate_block_ids: every id >= 0 is < num_blocks and none repeats. */
 pkv_status pkv_validate_block_ids(const int32_t* block_ids, int64_t num_ids, int64_t num_blocks);
 /* pkv_validate_block_pairs: rows with both ids >= 0 name blocks < num_blocks,

@@ -26,9 +26,10 @@ EXPORTED = (
     "paged_attention_decode_workspace_bytes", "paged_kv_copy_blocks", "pkv_validate_slots",
     "pkv_validate_decode_inputs", "pkv_validate_append_slots", "pkv_validate_prefill_inputs",
     "pkv_validate_block_pairs", "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
-    "pkv_validate_block_ids",
+    "pkv_validate_block_ids", "paged_attention_decode_shared_prefix",
+    "paged_attention_decode_shared_prefix_workspace_bytes", "pkv_validate_shared_prefix",
 )
-ABI_VERSION = 4
+ABI_VERSION = 5
 DECODE_DEFER_MERGE = 1
 
 
@@ -139,6 +140,16 @@ def load():
     lib.paged_kv_scatter_blocks.restype = ctypes.c_int
     lib.pkv_validate_block_ids.argtypes = [P, ctypes.c_int64, ctypes.c_int64]
     lib.pkv_validate_block_ids.restype = ctypes.c_int
+    lib.paged_attention_decode_shared_prefix.argtypes = [T, T, T, T, T, T, ctypes.c_int32,
+                                                         ctypes.c_float, ctypes.c_int32,
+                                                         ctypes.POINTER(PkvDecodeOpts), P]
+    lib.paged_attention_decode_shared_prefix.restype = ctypes.c_int
+    lib.paged_attention_decode_shared_prefix_workspace_bytes.argtypes = [ctypes.c_int32] * 7 + [
+        ctypes.POINTER(PkvDecodeOpts)]
+    lib.paged_attention_decode_shared_prefix_workspace_bytes.restype = ctypes.c_size_t
+    lib.pkv_validate_shared_prefix.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    lib.pkv_validate_shared_prefix.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -213,11 +224,16 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
         ctypes.byref(o)))
 
 
-def _workspace_for(opts: PkvDecodeOpts, q, key_cache, block_tables, block_size, workspace):
+def _workspace_for(opts: PkvDecodeOpts, q, key_cache, block_tables, block_size, workspace,
+                   prefix_len: int = 0):
     import torch
-    need = int(load().paged_attention_decode_workspace_bytes(
-        q.shape[0], q.shape[1], key_cache.shape[1], q.shape[2], block_tables.shape[1],
-        block_size, ctypes.byref(opts)))
+    args = (q.shape[0], q.shape[1], key_cache.shape[1], q.shape[2], block_tables.shape[1],
+            block_size)
+    if prefix_len:
+        need = int(load().paged_attention_decode_shared_prefix_workspace_bytes(
+            *args, int(prefix_len), ctypes.byref(opts)))
+    else:
+        need = int(load().paged_attention_decode_workspace_bytes(*args, ctypes.byref(opts)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
@@ -292,6 +308,39 @@ def paged_attention_prefill(out, q, key_cache, value_cache, block_tables, contex
                                           float(scale), int(block_size), ctypes.byref(o),
                                           _stream(q, stream)))
     return out
+
+
+def paged_attention_decode_shared_prefix(out, q, key_cache, value_cache, block_tables,
+                                         context_lens, prefix_len: int, scale: float,
+                                         block_size: int, *, k_scale: float = 1.0,
+                                         v_scale: float = 1.0, num_workers: int = 0,
+                                         workspace=None, stream=None):
+    """Decode for sequences whose first ``prefix_len`` tokens are the same shared
+    blocks: the prefix part once for all sequences, the tails through the
+    balanced split, merged (see include/pagedkv.h)."""
+    _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
+    opts = decode_opts("auto", 0, 0, num_workers)
+    ws = _workspace_for(opts, q, key_cache, block_tables, block_size, workspace, prefix_len)
+    d = [describe(out), describe(q), describe(key_cache, k_scale), describe(value_cache, v_scale),
+         describe(block_tables), describe(context_lens)]
+    _check(load().paged_attention_decode_shared_prefix(
+        *[ctypes.byref(x) for x in d], int(prefix_len), float(scale), int(block_size),
+        ctypes.byref(opts), _stream(q, stream)))
+    if ws is not None and workspace is None and stream is not None:
+        ws.record_stream(stream)
+    return out
+
+
+def validate_shared_prefix(block_tables: np.ndarray, context_lens: np.ndarray, num_blocks: int,
+                           block_size: int, prefix_len: int) -> None:
+    """Host check of a shared-prefix decode's tables; raises PagedKVError."""
+    t = np.ascontiguousarray(block_tables, dtype=np.int32)
+    n = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if t.ndim != 2 or n.shape != (t.shape[0],):
+        raise ValueError("block_tables must be [S, max_blocks], context_lens [S]")
+    _check(load().pkv_validate_shared_prefix(t.ctypes.data_as(ctypes.c_void_p),
+                                             n.ctypes.data_as(ctypes.c_void_p), t.shape[0],
+                                             t.shape[1], num_blocks, block_size, prefix_len))
 
 
 def paged_kv_copy_blocks(key_cache, value_cache, block_pairs, *, stream=None) -> None:
@@ -491,13 +540,20 @@ class DecodeLaunch:
     def __init__(self, out, q, key_cache, value_cache, block_tables, context_lens, scale: float,
                  block_size: int, *, k_scale: float = 1.0, v_scale: float = 1.0,
                  mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
-                 num_workers: int = 0, workspace=None, append=None, defer_merge: bool = False):
+                 num_workers: int = 0, workspace=None, append=None, defer_merge: bool = False,
+                 prefix_len: int = 0):
         _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
+        if prefix_len and (append is not None or defer_merge):
+            raise ValueError("a shared-prefix decode takes no appended tokens and no deferred merge")
+        if prefix_len and mode is None:
+            mode = "auto"
         self._opts = decode_opts(mode, partition_size, waves_per_group, num_workers, defer_merge)
         self._merge_opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
         self.workspace = _workspace_for(self._opts, q, key_cache, block_tables, block_size,
-                                        workspace)
-        _workspace_for(self._merge_opts, q, key_cache, block_tables, block_size, self.workspace)
+                                        workspace, prefix_len)
+        _workspace_for(self._merge_opts, q, key_cache, block_tables, block_size, self.workspace,
+                       prefix_len)
+        self._prefix = int(prefix_len)
         self._keep = (out, q, key_cache, value_cache, block_tables, context_lens, append)
         self._d = [describe(out), describe(q), describe(key_cache, k_scale),
                    describe(value_cache, v_scale), describe(block_tables), describe(context_lens)]
@@ -520,7 +576,11 @@ class DecodeLaunch:
         return ctypes.c_void_p(s.cuda_stream)
 
     def __call__(self, stream=None):
-        if self._app_refs is not None:
+        if self._prefix:
+            _check(self._lib.paged_attention_decode_shared_prefix(
+                *self._refs, self._prefix, self._scale, self._bs, ctypes.byref(self._opts),
+                self._s(stream)))
+        elif self._app_refs is not None:
             _check(self._lib.paged_attention_decode_append(*self._app_refs, self._scale, self._bs,
                                                            ctypes.byref(self._opts),
                                                            self._s(stream)))

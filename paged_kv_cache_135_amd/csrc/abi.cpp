@@ -122,9 +122,13 @@ struct Plan {
   int64_t part_tiles = 1;
   int32_t waves = 4;
   int32_t workers = 0;      // BALANCED
+  int32_t prefix_splits = 0;  // shared-prefix decode: key splits of the prefix per pair
+  int64_t slots(int64_t S, int64_t Hkv) const {
+    return workers + S * Hkv + S * Hkv * prefix_splits;
+  }
   size_t workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D) const {
     if (mode == PKV_DECODE_PARTITIONED && partitions > 1) return (size_t)(S * Hq * partitions * (D + 2));
-    if (mode == PKV_DECODE_BALANCED) return (size_t)((workers + S * Hkv) * (Hq / Hkv) * (D + 2));
+    if (mode == PKV_DECODE_BALANCED) return (size_t)(slots(S, Hkv) * (Hq / Hkv) * (D + 2));
     return 0;
   }
   size_t meta_bytes(int64_t S, int64_t Hkv) const {
@@ -132,13 +136,31 @@ struct Plan {
   }
 };
 
+// Key splits of a shared prefix: enough (pair-row group, KV head, split)
+// workgroups to cover the device twice, at least four tiles per split.
+int32_t prefix_splits(int64_t S, int64_t G, int64_t Hkv, int64_t prefix_len) {
+  const int64_t tiles = prefix_len / 16;
+  const int64_t row_groups = (S * G + 127) / 128;
+  const int64_t want = (2 * device_cus() + row_groups * Hkv - 1) / (row_groups * Hkv);
+  const int64_t cap = tiles / 4 > 1 ? tiles / 4 : 1;
+  return (int32_t)(want < 1 ? 1 : want > cap ? cap : want);
+}
+
 pkv_status plan(const pkv_decode_opts* opts, int64_t S, int64_t Hq, int64_t Hkv, int64_t maxb,
-                int64_t bs, Plan* p) {
-  (void)Hq;
+                int64_t bs, Plan* p, int64_t prefix_len = 0) {
   int32_t mode = opts ? opts->mode : PKV_DECODE_SINGLE_PASS;
   int32_t waves = opts ? opts->waves_per_group : 0;
   int32_t auto_workers = 0;
-  if (mode == PKV_DECODE_AUTO) {
+  if (prefix_len > 0) {
+    // the tails run the balanced split (cascade pieces need its merge)
+    if (mode != PKV_DECODE_AUTO && mode != PKV_DECODE_BALANCED && opts)
+      return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode runs the balanced split: mode must "
+                                       "be AUTO or BALANCED");
+    const int64_t pairs = S * Hkv, cus = device_cus();
+    auto_workers = (int32_t)((pairs >= 8 * cus ? 8 : 4) * cus);
+    mode = PKV_DECODE_BALANCED;
+    p->prefix_splits = prefix_splits(S, Hq / Hkv, Hkv, prefix_len);
+  } else if (mode == PKV_DECODE_AUTO) {
     // measured on MI355X: many short (sequence, KV head) pairs stream best one
     // workgroup each; few or long ones need the balanced split
     const int64_t pairs = S * Hkv, cus = device_cus();
@@ -171,11 +193,12 @@ pkv_status plan(const pkv_decode_opts* opts, int64_t S, int64_t Hq, int64_t Hkv,
       return PKV_OK;
     }
     case PKV_DECODE_BALANCED: {
-      const int32_t wk = opts->num_workers;
+      const int32_t wk = opts ? opts->num_workers : 0;
       if (wk < 0 || wk > (1 << 24))
         return fail(PKV_ERR_UNSUPPORTED, "num_workers %d: must be in [0, 2^24]", wk);
       p->workers = wk != 0 ? wk : auto_workers != 0 ? auto_workers : default_workers();
       if (S * Hkv > INT32_MAX / 2) return fail(PKV_ERR_UNSUPPORTED, "too many (sequence, KV head) pairs");
+      if (p->slots(S, Hkv) > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "too many partial slots");
       return PKV_OK;
     }
     default:
@@ -251,6 +274,22 @@ pkv_status paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_te
   const hipError_t e = pkv::launch_kv_write(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "paged_kv_write launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                            int32_t num_kv_heads, int32_t head_dim,
+                                                            int32_t max_blocks_per_seq,
+                                                            int32_t block_size, int32_t prefix_len,
+                                                            const pkv_decode_opts* opts) {
+  if (num_seqs < 0 || num_q_heads < 0 || num_kv_heads <= 0 || head_dim < 0 ||
+      max_blocks_per_seq < 0 || block_size <= 0 || num_q_heads % num_kv_heads != 0 ||
+      prefix_len <= 0 || prefix_len % block_size != 0)
+    return 0;
+  Plan p;
+  if (plan(opts, num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size, &p,
+           prefix_len) != PKV_OK)
+    return 0;
+  return p.workspace_floats(num_seqs, num_q_heads, num_kv_heads, head_dim) * 4u + p.meta_bytes(num_seqs, num_kv_heads);
 }
 
 pkv_status paged_attention_prefill(pkv_tensor* out, const pkv_tensor* q,
@@ -503,7 +542,7 @@ pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
                        const pkv_tensor* key_cache, const pkv_tensor* value_cache,
                        const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
                        int32_t block_size, const pkv_decode_opts* opts, const AppendIn* app,
-                       int32_t phase, void* hip_stream) {
+                       int32_t phase, void* hip_stream, int32_t prefix_len = 0) {
   PKV_TRY(check_tensor(out, "out", 3));
   PKV_TRY(check_tensor(q, "q", 3));
   PKV_TRY(check_tensor(key_cache, "key_cache", 4));
@@ -578,19 +617,23 @@ pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
     if (overlap(key_cache, value_cache)) return fail(PKV_ERR_LAYOUT, "key_cache and value_cache overlap");
   }
 
+  if (prefix_len < 0 || prefix_len % bs != 0 || prefix_len > maxb * bs)
+    return fail(PKV_ERR_SHAPE, "prefix_len %d: must be a multiple of block_size in [0, %lld]",
+                prefix_len, (long long)(maxb * bs));
+
   Plan p;
-  PKV_TRY(plan(opts, S, Hq, Hkv, maxb, bs, &p));
+  PKV_TRY(plan(opts, S, Hq, Hkv, maxb, bs, &p, prefix_len));
   pkv::DecodeArgs a{};
   const size_t need = p.workspace_floats(S, Hq, Hkv, D) * 4u + p.meta_bytes(S, Hkv);
   if (need > 0) {
-    if (!opts->workspace || opts->workspace_bytes < need)
+    if (!opts || !opts->workspace || opts->workspace_bytes < need)
       return fail(PKV_ERR_WORKSPACE, "this decode mode needs a workspace of %zu bytes (got %zu)", need,
-                  opts->workspace ? opts->workspace_bytes : (size_t)0);
+                  opts && opts->workspace ? opts->workspace_bytes : (size_t)0);
     if (reinterpret_cast<uintptr_t>(opts->workspace) % 16 != 0)
       return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     a.ws_acc = static_cast<float*>(opts->workspace);
     if (p.mode == PKV_DECODE_BALANCED) {
-      const size_t slots = (size_t)p.workers + (size_t)S * Hkv;
+      const size_t slots = (size_t)p.slots(S, Hkv);
       a.ws_ml = a.ws_acc + slots * (Hq / Hkv) * D;
       a.ws_meta = reinterpret_cast<int32_t*>(a.ws_ml + slots * (Hq / Hkv) * 2);
     } else {
@@ -632,7 +675,39 @@ pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
     a.inv_k = ct == PKV_FP8_E4M3 ? 1.0f / key_cache->scale : 1.0f;
     a.inv_v = ct == PKV_FP8_E4M3 ? 1.0f / value_cache->scale : 1.0f;
   }
-  const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(hip_stream));
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (prefix_len > 0) {
+    // cascade: prefix pieces from the prefix kernel, tail pieces from the
+    // balanced split over the tables past the prefix, merged together
+    a.len_offset = prefix_len;
+    a.cascade = 1;
+    a.num_prefix_splits = p.prefix_splits;
+    a.prefix_slot0 = (int64_t)p.workers + S * Hkv;
+    a.tables += prefix_len / bs;
+    if (phase != pkv::kMergePhase) {
+      pkv::PrefixArgs pa{};
+      pa.q = q->data;
+      pa.kc = key_cache->data;
+      pa.vc = value_cache->data;
+      pa.blocks = static_cast<const int32_t*>(block_tables->data);  // row 0: the shared blocks
+      pa.ws_acc = a.ws_acc;
+      pa.ws_ml = a.ws_ml;
+      pa.slot0 = a.prefix_slot0;
+      pa.num_seqs = (int32_t)S;
+      pa.num_q_heads = (int32_t)Hq;
+      pa.num_kv_heads = (int32_t)Hkv;
+      pa.group = (int32_t)(Hq / Hkv);
+      pa.head_dim = (int32_t)D;
+      pa.block_size = (int32_t)bs;
+      pa.prefix_len = prefix_len;
+      pa.splits = p.prefix_splits;
+      pa.cache_dtype = ct;
+      pa.qk_scale = a.qk_scale;
+      const hipError_t e = pkv::launch_shared_prefix(pa, stream);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+    }
+  }
+  const hipError_t e = pkv::launch_decode(a, stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -661,6 +736,22 @@ pkv_status paged_attention_decode_merge(pkv_tensor* out, const pkv_tensor* q,
                                         void* hip_stream) {
   return decode_impl("paged_attention_decode_merge", out, q, key_cache, value_cache, block_tables,
                      context_lens, scale, block_size, opts, nullptr, pkv::kMergePhase, hip_stream);
+}
+
+pkv_status paged_attention_decode_shared_prefix(pkv_tensor* out, const pkv_tensor* q,
+                                                const pkv_tensor* key_cache,
+                                                const pkv_tensor* value_cache,
+                                                const pkv_tensor* block_tables,
+                                                const pkv_tensor* context_lens, int32_t prefix_len,
+                                                float scale, int32_t block_size,
+                                                const pkv_decode_opts* opts, void* hip_stream) {
+  if (prefix_len <= 0) return fail(PKV_ERR_SHAPE, "prefix_len must be positive");
+  if (opts && (opts->flags & PKV_DECODE_DEFER_MERGE))
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode launches its kernels together: "
+                                     "PKV_DECODE_DEFER_MERGE is not supported");
+  return decode_impl("paged_attention_decode_shared_prefix", out, q, key_cache, value_cache,
+                     block_tables, context_lens, scale, block_size, opts, nullptr, phase_of(opts),
+                     hip_stream, prefix_len);
 }
 
 pkv_status paged_attention_decode_append(pkv_tensor* out, const pkv_tensor* q, const pkv_tensor* k,
@@ -776,6 +867,27 @@ pkv_status pkv_validate_prefill_inputs(const int32_t* query_start_loc, const int
   if (query_start_loc[num_seqs] != num_query_rows)
     return fail(PKV_ERR_RANGE, "query_start_loc[S] = %d, q has %lld rows", query_start_loc[num_seqs],
                 (long long)num_query_rows);
+  return ok();
+}
+
+pkv_status pkv_validate_shared_prefix(const int32_t* block_tables, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t max_blocks_per_seq,
+                                     int64_t num_blocks, int32_t block_size, int32_t prefix_len) {
+  PKV_TRY(pkv_validate_decode_inputs(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                     num_blocks, block_size));
+  if (prefix_len <= 0 || prefix_len % block_size != 0 ||
+      (int64_t)prefix_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_SHAPE, "prefix_len %d: must be a positive multiple of block_size", prefix_len);
+  const int32_t nb = prefix_len / block_size;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (context_lens[s] < prefix_len)
+      return fail(PKV_ERR_RANGE, "sequence %d has %d tokens, fewer than the prefix's %d", s,
+                  context_lens[s], prefix_len);
+    for (int32_t j = 0; j < nb; ++j)
+      if (block_tables[(int64_t)s * max_blocks_per_seq + j] != block_tables[j])
+        return fail(PKV_ERR_RANGE, "sequence %d does not list the shared block %d at entry %d", s,
+                    block_tables[j], j);
+  }
   return ok();
 }
 

@@ -379,7 +379,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
   int64_t total = 0;
   for (int c = 0, r = 0; c < S; c += 64, ++r) {
     const int s = c + lane;
-    const int ctx = s < S ? a.lens[s] : 0;
+    const int ctx = s < S ? max(0, a.lens[s] - a.len_offset) : 0;
     const uint32_t n = (uint32_t)((ctx + 15) >> 4);
     if (r < kScanRegs) nreg[r] = n;
     total += wave_sum(units(n));
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
       const int s = c + lane;
       uint32_t n;
       if (r < kScanRegs) n = nreg[r];
-      else n = s < S ? (uint32_t)((a.lens[s] + 15) >> 4) : 0u;
+      else n = s < S ? (uint32_t)((max(0, a.lens[s] - a.len_offset) + 15) >> 4) : 0u;
       const uint32_t u = units(n);
       const uint32_t incl = wave_incl_scan(u, lane);
       const int64_t tot = (int64_t)Hkv * __shfl(incl, 63);
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
   int32_t carry = 0;      // first-batch block ids of the next piece, loaded ahead
   bool has_carry = false;
   while (x < x1 && s_cur < S) {
-    const int ctx = a.lens[s_cur];
+    const int ctx = max(0, a.lens[s_cur] - a.len_offset);
     const int n = (ctx + 15) >> 4;
     if (n == 0) {
       ++s_cur;
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
-    const bool whole = tl == 0 && te == n;
+    const bool whole = tl == 0 && te == n && !a.cascade;  // cascade: always pieces
     if (whole || te == n) {
       // the segment's last piece records where its pieces are
       if (lane == 0) {
@@ -561,28 +561,33 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
 }
 
 // Merge the pieces of one segment (sequence, KV head) for one query head.
-// One wavefront: lanes first take the pieces' (max, sum) pairs (pieces
-// strided over lanes) for the common max M and the total L; then lane
-// (group p4 = lane / 16, column chunk c = lane % 16) sums pieces p4, p4+4, ...
-// over its D/16 columns, and the four groups are added in a fixed order.
+// Pieces in order: the shared-prefix pieces (cascade only), then the
+// workers' pieces of the segment's own tiles.  One wavefront: lanes first take
+// the pieces' (max, sum) pairs (pieces strided over lanes) for the common max M
+// and the total L; then lane (group p4 = lane / 16, column chunk c = lane % 16)
+// sums pieces p4, p4+4, ... over its D/16 columns, and the four groups are
+// added in a fixed order.
 template <int CT, int D>
 __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a) {
   constexpr int VE = D / 16;
   const int seg = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
   const int w0 = a.ws_meta[2 * (int64_t)seg], w1 = a.ws_meta[2 * (int64_t)seg + 1];
-  if (w0 < 0) return;
+  const int ns = a.cascade ? a.num_prefix_splits : 0;
+  const int np = ns + (w0 < 0 ? 0 : w1 - w0 + 1);
+  if (np == 0) return;  // finalised in place (or an empty context)
   const int G = a.group;
-  const int np = w1 - w0 + 1;
-  const int64_t slot0 = (int64_t)w0 + seg;
-  auto ml = [&](int p) { return a.ws_ml + ((slot0 + p) * G + g) * 2; };
+  auto slot_of = [&](int p) -> int64_t {
+    return p < ns ? a.prefix_slot0 + (int64_t)seg * ns + p : (int64_t)w0 + seg + (p - ns);
+  };
+  auto ml = [&](int p) { return a.ws_ml + (slot_of(p) * G + g) * 2; };
   // Lane (p4 = lane / 16, c = lane % 16) sums pieces p4, p4 + 4, ... over
   // columns [VE c, VE c + VE).  Its first two pieces' columns are loaded now,
   // together with the (max, sum) pairs below, so the two latencies overlap.
   const int p4 = lane >> 4, c = lane & 15;
   f32x4 v0[VE / 4], v1[VE / 4];
   {
-    const float* src0 = a.ws_acc + ((slot0 + p4) * G + g) * D + VE * c;
-    const float* src1 = src0 + 4 * (int64_t)G * D;
+    const float* src0 = a.ws_acc + (slot_of(min(p4, np - 1)) * G + g) * D + VE * c;
+    const float* src1 = a.ws_acc + (slot_of(min(p4 + 4, np - 1)) * G + g) * D + VE * c;
 #pragma unroll
     for (int q = 0; q < VE / 4; ++q) {
       v0[q] = p4 < np ? *reinterpret_cast<const f32x4*>(src0 + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -615,7 +620,7 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
   if (p4 < np) add(__builtin_amdgcn_exp2f(ml(p4)[0] - M), v0);
   if (p4 + 4 < np) add(__builtin_amdgcn_exp2f(ml(p4 + 4)[0] - M), v1);
   for (int p = p4 + 8; p < np; p += 4) {
-    const float* src = a.ws_acc + ((slot0 + p) * G + g) * D + VE * c;
+    const float* src = a.ws_acc + (slot_of(p) * G + g) * D + VE * c;
     f32x4 v[VE / 4];
 #pragma unroll
     for (int q = 0; q < VE / 4; ++q) v[q] = *reinterpret_cast<const f32x4*>(src + 4 * q);

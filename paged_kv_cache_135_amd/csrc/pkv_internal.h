@@ -61,6 +61,16 @@ struct DecodeArgs {
   float qk_scale;       // scale * log2(e) (* k scale for E4M3)
   float v_scale;        // 1, or the V scale for E4M3
   int32_t phase;        // DecodePhase
+  // Shared prefix (balanced mode only): the first len_offset tokens of every
+  // sequence are a prefix handled by the prefix kernel; the balanced kernel
+  // walks only the tails (tables already advanced by len_offset / bs columns)
+  // and, with cascade set, leaves every pair as pieces for the merge, which
+  // also takes the prefix pieces: num_prefix_splits slots per pair from slot
+  // prefix_slot0 + pair * num_prefix_splits.
+  int32_t len_offset;
+  int32_t cascade;
+  int32_t num_prefix_splits;
+  int64_t prefix_slot0;
   // Append (write folded into the decode): sequence s's new token, rows
   // [S][Hkv][D] of q's element type, goes to slots[s]; when that slot is
   // position len-1 of the sequence, the attention takes the row from kn/vn.
@@ -114,7 +124,30 @@ struct PrefillArgs {
   float v_scale;
 };
 
+// The shared-prefix part of a cascade decode: every sequence's queries
+// against the prefix keys (one physical block list), split over keys.
+struct PrefixArgs {
+  const void* q;          // [S][Hq][D]
+  const void* kc;
+  const void* vc;
+  const int32_t* blocks;  // the prefix's physical blocks, prefix_len / block_size of them
+  float* ws_acc;          // partial states in the balanced merge's slot layout
+  float* ws_ml;
+  int64_t slot0;          // slot of (pair 0, split 0); pair p, split k -> slot0 + p * splits + k
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t prefix_len;
+  int32_t splits;         // key ranges per (pair): tiles k * T / splits .. (k + 1) * T / splits
+  int32_t cache_dtype;
+  float qk_scale;
+};
+
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_shared_prefix(const PrefixArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

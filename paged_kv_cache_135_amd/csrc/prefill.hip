@@ -27,6 +27,9 @@
 //   key 0 (visible to every row) comes first and every running max is finite
 //   from the first tile on.
 // * Each row's result is finalised in place: no workspace, no second kernel.
+// * The same machinery serves the shared-prefix part of a cascade decode
+//   (shared_prefix_kernel): all sequences' query heads against one prefix,
+//   split over keys, leaving partial states for the decode's merge.
 #include "pkv_internal.h"
 #include "tile.h"
 
@@ -169,6 +172,116 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
   }
 }
 
+// The shared-prefix part of a cascade decode: every sequence's query heads
+// (rows s * G + g of one KV head) against one split of the prefix's tiles, no
+// mask (every query sits past the whole prefix).  Each row leaves its partial
+// state (running max in log2 units, sum, unnormalised accumulator) in the
+// balanced merge's slot layout; the merge adds the sequence's own tail.
+template <int CT, int D, int R, int NBUF>
+__global__ __launch_bounds__(kPrefillWaves * 64) void shared_prefix_kernel(PrefixArgs a) {
+  using T = Tile<CT, D>;
+  constexpr int VE = T::VE;
+  constexpr int NW = kPrefillWaves;
+  constexpr int ROWS_W = 16 * R;
+  constexpr int ROWS_G = ROWS_W * NW;
+  const int split = blockIdx.z, hk = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.group, Hq = a.num_q_heads, bs = a.block_size;
+  const int rows = a.num_seqs * G;
+  const int ntiles = a.prefix_len / 16;
+  const int k0 = (int)((int64_t)split * ntiles / a.splits);
+  const int k1 = (int)((int64_t)(split + 1) * ntiles / a.splits);
+  const int64_t head_rows = (int64_t)hk * bs;
+  const int64_t block_rows = (int64_t)a.num_kv_heads * bs;
+  __shared__ int32_t sm_blk[kPrefillChunkTiles];
+
+  for (int row_g0 = blockIdx.x * ROWS_G; row_g0 < rows; row_g0 += gridDim.x * ROWS_G) {
+    const int row_w0 = row_g0 + wave * ROWS_W;
+    const bool live = row_w0 < rows;
+    typename T::QFrag qf[R];
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb) {
+      const int rr = row_w0 + 16 * rb + (lane & 15);
+      const bool valid = rr < rows;
+      const int s = valid ? rr / G : 0;
+      const int g = valid ? rr - s * G : 0;
+      qf[rb] = T::load_q(static_cast<const QElem<CT>*>(a.q) + ((int64_t)s * Hq + hk * G + g) * D,
+                         valid, lane);
+    }
+    Softmax<VE> st[R];
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+      for (int r = 0; r < VE; ++r) st[rb].acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = k0; c0 < k1; c0 += kPrefillChunkTiles) {
+      const int c1 = min(k1, c0 + kPrefillChunkTiles);
+      __syncthreads();
+      for (int i = threadIdx.x; i < c1 - c0; i += NW * 64) sm_blk[i] = a.blocks[((c0 + i) * 16) / bs];
+      __syncthreads();
+      if (!live) continue;
+      for (int k = c0; k < c1; k += NBUF) {
+        T buf[NBUF];
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          const int t = min(k + j, c1 - 1);
+          buf[j].load(a.kc, a.vc, (int64_t)sm_blk[t - c0] * block_rows + head_rows + ((t * 16) % bs),
+                      lane);
+        }
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          if (k + j >= c1) break;
+          const typename T::PV pv = buf[j].pack_v();
+#pragma unroll
+          for (int rb = 0; rb < R; ++rb)
+            prefill_update<CT, D>(buf[j].scores(qf[rb]), pv, st[rb], 0, 0, false, a.qk_scale, lane);
+        }
+      }
+    }
+
+    if (live) {
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) {
+        float l_run = st[rb].l;
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        const int rr = row_w0 + 16 * rb + (lane & 15);
+        if (rr < rows) {
+          const int s = rr / G, g = rr - s * G;
+          const int64_t slot = a.slot0 + ((int64_t)s * a.num_kv_heads + hk) * a.splits + split;
+          float* o = a.ws_acc + (slot * G + g) * D;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < VE / 4; ++q4)
+              *reinterpret_cast<f32x4*>(o + VE * (4 * (lane >> 4) + i) + 4 * q4) =
+                  f32x4{st[rb].acc[4 * q4][i], st[rb].acc[4 * q4 + 1][i], st[rb].acc[4 * q4 + 2][i],
+                        st[rb].acc[4 * q4 + 3][i]};
+          if (lane < 16) *reinterpret_cast<f32x2*>(a.ws_ml + (slot * G + g) * 2) = f32x2{st[rb].m, l_run};
+        }
+      }
+    }
+  }
+}
+
+template <int CT, int D>
+hipError_t launch_prefix_d(const PrefixArgs& a, hipStream_t stream) {
+  constexpr int ROWS_G = 32 * kPrefillWaves;
+  int64_t gx = ((int64_t)a.num_seqs * a.group + ROWS_G - 1) / ROWS_G;
+  gx = gx < 1 ? 1 : gx > 65535 ? 65535 : gx;
+  const dim3 grid((unsigned)gx, (unsigned)a.num_kv_heads, (unsigned)a.splits);
+  hipLaunchKernelGGL((shared_prefix_kernel<CT, D, 2, 2>), grid, dim3(kPrefillWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int CT>
+hipError_t launch_prefix_ct(const PrefixArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) return launch_prefix_d<CT, 128>(a, stream);
+  if (a.head_dim == 64) return launch_prefix_d<CT, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int CT, int D, int R>
 hipError_t launch_r(const PrefillArgs& a, hipStream_t stream) {
   constexpr int ROWS_G = 16 * R * kPrefillWaves;
@@ -200,6 +313,16 @@ hipError_t launch_ct(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_shared_prefix(const PrefixArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  switch (a.cache_dtype) {
+    case PKV_F32: return launch_prefix_ct<PKV_F32>(a, stream);
+    case PKV_BF16: return launch_prefix_ct<PKV_BF16>(a, stream);
+    case PKV_FP8_E4M3: return launch_prefix_ct<PKV_FP8_E4M3>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;

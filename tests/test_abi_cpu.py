@@ -376,3 +376,41 @@ def test_block_id_validator():
         with pytest.raises(B.PagedKVError) as e:
             B.validate_block_ids(np.array(bad, np.int32), 8)
         assert e.value.status == 8
+
+
+# ------------------------------------------------------- shared-prefix decode
+def test_shared_prefix_workspace_and_refusals():
+    lib = B.load()
+    o = _opts(mode=3)
+    ws = lambda *a: lib.paged_attention_decode_shared_prefix_workspace_bytes(*a, ctypes.byref(o))
+    # 256 x 8 pairs (8 per CU of a 256-CU device -> 2048 workers); prefix of 64 tiles;
+    # 8 row groups of 128 rows x 8 KV heads -> 8 key splits per pair
+    S, Hq, Hkv, D = 256, 32, 8, 128
+    slots = 2048 + S * Hkv + S * Hkv * 8
+    assert ws(S, Hq, Hkv, D, 600, 16, 1024) == slots * 4 * (D + 2) * 4 + S * Hkv * 8
+    assert ws(S, Hq, Hkv, D, 600, 16, 1000) == 0   # not a multiple of the block size
+    assert ws(S, Hq, Hkv, D, 600, 16, 0) == 0
+    a = _decode_args()
+    ref = lambda d: ctypes.byref(d) if d is not None else None
+    call = lambda plen, opts: lib.paged_attention_decode_shared_prefix(
+        ref(a["out"]), ref(a["q"]), ref(a["kc"]), ref(a["vc"]), ref(a["tables"]), ref(a["lens"]),
+        plen, 0.1, 16, ref(opts), None)
+    assert call(8, None) == 3                      # not a multiple of the block size
+    assert call(16 * 5, None) == 3                 # longer than the table
+    assert call(16, _opts(mode=1, part=64)) == 5   # tails must run the balanced split
+    d = _opts(mode=2)
+    d.flags = B.DECODE_DEFER_MERGE
+    assert call(16, d) == 5
+    assert call(16, None) == 6                     # needs a workspace
+
+
+def test_shared_prefix_validator():
+    tables = np.array([[4, 2, 7], [4, 2, 1], [4, 2, 9]], np.int32)
+    lens = np.array([40, 33, 32], np.int32)
+    B.validate_shared_prefix(tables, lens, 10, 16, 32)
+    with pytest.raises(B.PagedKVError):
+        B.validate_shared_prefix(tables, np.array([40, 33, 31], np.int32), 10, 16, 32)
+    with pytest.raises(B.PagedKVError):
+        B.validate_shared_prefix(np.array([[4, 2, 7], [4, 3, 1], [4, 2, 9]], np.int32), lens, 10, 16, 32)
+    with pytest.raises(B.PagedKVError):
+        B.validate_shared_prefix(tables, lens, 10, 16, 24)
