@@ -284,7 +284,7 @@ pkv_status paged_attention_decode_append(pkv_tensor* out, const pkv_tensor* q,
 
 typedef struct {
   int32_t rows_per_wave;  /* (query token, query head) rows per wavefront: 0 = library
-                             default (32), 16, 32, or 64 (not for f32) */
+                             default (32; 16 for f32), 16, 32, or 64 (head_dim 64, not f32) */
 } pkv_prefill_opts;
 
 /*

@@ -343,9 +343,11 @@ pkv_status paged_attention_prefill(pkv_tensor* out, const pkv_tensor* q,
     return fail(PKV_ERR_UNSUPPORTED, "too many query rows");
   if (max_query_len < 0 || max_query_len > T)
     return fail(PKV_ERR_SHAPE, "max_query_len %d outside [0, %lld]", max_query_len, (long long)T);
-  const int32_t rpw = opts && opts->rows_per_wave ? opts->rows_per_wave : 32;
-  if (rpw != 16 && rpw != 32 && (rpw != 64 || ct == PKV_F32))
-    return fail(PKV_ERR_UNSUPPORTED, "rows_per_wave %d: must be 0, 16, 32 or (not f32) 64", rpw);
+  // default: 32 rows per wavefront; f32 fragments are twice as large, so 16
+  const int32_t rpw = opts && opts->rows_per_wave ? opts->rows_per_wave : ct == PKV_F32 ? 16 : 32;
+  if (rpw != 16 && rpw != 32 && (rpw != 64 || ct == PKV_F32 || D != 64))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "rows_per_wave %d: must be 0, 16, 32, or 64 with head_dim 64 (not f32)", rpw);
   PKV_TRY(check_scale(key_cache, "key_cache"));
   PKV_TRY(check_scale(value_cache, "value_cache"));
   PKV_TRY(check_align(out, "out", 16));

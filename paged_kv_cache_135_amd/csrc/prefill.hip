@@ -36,8 +36,13 @@
 namespace pkv {
 namespace {
 
-constexpr int kPrefillWaves = 4;
+constexpr int kPrefillWaves = 8;
 constexpr int kPrefillChunkTiles = 1024;  // block ids staged in LDS per pass
+
+// A column keeps its running max until a score exceeds it by more than
+// kLazyMax (log2 units): its probabilities then stay below 2^kLazyMax and the
+// accumulators need no rescale (an unchanged max rescales by exactly 1).
+constexpr float kLazyMax = 8.0f;
 
 // Online-softmax update of one 16-row block with one tile.
 template <int CT, int D>
@@ -52,60 +57,121 @@ __device__ __forceinline__ void prefill_update(const f32x4 sacc, const typename 
     if (causal) sc[i] = t0 + 4 * (lane >> 4) + i <= pos ? sc[i] : kNegInf;
   }
   const float bm = max_over_lane_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-  const float m_new = fmaxf(st.m, bm);  // finite: tile 0 holds key 0, visible to every row
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  // the first tile a column sees holds a visible key (tile 0 holds key 0), so
+  // its running max is finite from then on
+  const bool grow = bm > st.m + kLazyMax;
+  const float m_new = grow ? bm : st.m;
+  if (__ballot(grow) != 0) {  // wave-uniform: some column's max moved
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+#pragma unroll
+    for (int r = 0; r < VE; ++r) st.acc[r] *= alpha;
+    st.l *= alpha;
+  }
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
-#pragma unroll
-  for (int r = 0; r < VE; ++r) st.acc[r] *= alpha;
-  st.l = st.l * alpha + Tile<CT, D>::pv_packed(pv, p, st.acc);
+  st.l += Tile<CT, D>::pv_packed(pv, p, st.acc);
   st.m = m_new;
 }
 
-template <int CT, int D, int R, int NBUF>
-__global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs a) {
+// K/V of kStageKeys keys of one KV head staged in LDS, rows padded by 16
+// bytes so that the 16 lanes reading one 16-byte column of 16 different rows
+// hit 16 different bank groups.
+constexpr int kStageKeys = 128;
+constexpr int kStageTiles = kStageKeys / 16;
+template <int CT, int D>
+constexpr int row_bytes() {
+  return D * (CT == PKV_F32 ? 4 : CT == PKV_BF16 ? 2 : 1);
+}
+template <int CT, int D>
+constexpr int lds_pitch() {
+  return row_bytes<CT, D>() + 16;
+}
+
+enum RowsJob : int { kPrefillJob = 0, kPrefixJob = 1 };
+
+// Query rows against paged keys on the matrix cores, K/V streamed through LDS.
+//   kPrefillJob: rows = a chunk's (query token, head) pairs of one KV head,
+//     causal, final outputs (PrefillArgs).
+//   kPrefixJob: rows = every sequence's query heads of one KV head against one
+//     key split of a shared prefix, no mask, partial states (PrefixArgs).
+// Per stage the workgroup's 256 threads copy kStageKeys keys of K and V from
+// the pool into LDS (16 bytes per thread and piece), then every wavefront
+// reads its MFMA fragments from LDS.  The next stage's global loads are issued
+// before the current stage is computed, so they are in flight meanwhile.
+template <int CT, int D, int R, int JOB, typename Args>
+__global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
   using T = Tile<CT, D>;
   constexpr int VE = T::VE;
   constexpr int NW = kPrefillWaves;
   constexpr int ROWS_W = 16 * R;
   constexpr int ROWS_G = ROWS_W * NW;
-  const int s = blockIdx.z, hk = blockIdx.y;
+  constexpr int RB = row_bytes<CT, D>();
+  constexpr int PITCH = lds_pitch<CT, D>();
+  constexpr int PER_ROW = RB / 16;                          // 16-byte pieces per key row
+  constexpr int PIECES = kStageKeys * PER_ROW / (NW * 64);  // per thread and pool
+  static_assert(PIECES >= 1 && kStageKeys * PER_ROW % (NW * 64) == 0, "stage split");
+  const int hk = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.group, Hq = a.num_q_heads, bs = a.block_size;
-  const int q0 = a.qstart[s];
-  const int nq = a.qstart[s + 1] - q0;
-  const int rows = nq * G;
-  const int ctx = a.lens[s];
-  const int first_pos = ctx - nq;  // position of the chunk's first query
-  const int32_t* table = a.tables + (int64_t)s * a.max_blocks;
   const int64_t head_rows = (int64_t)hk * bs;
   const int64_t block_rows = (int64_t)a.num_kv_heads * bs;
+
+  // what this workgroup works on
+  int rows, ctx, first_pos = 0, q0 = 0, k_lo, k_hi_all;
+  const int32_t* table;
+  if constexpr (JOB == kPrefillJob) {
+    const int s = blockIdx.z;
+    q0 = a.qstart[s];
+    const int nq = a.qstart[s + 1] - q0;
+    rows = nq * G;
+    ctx = a.lens[s];
+    first_pos = ctx - nq;
+    table = a.tables + (int64_t)s * a.max_blocks;
+    k_lo = 0;
+    k_hi_all = 0;  // per row group below
+  } else {
+    const int split = blockIdx.z;
+    const int ntiles = a.prefix_len / 16;
+    rows = a.num_seqs * G;
+    ctx = a.prefix_len;
+    table = a.blocks;
+    k_lo = (int)((int64_t)split * ntiles / a.splits);
+    k_hi_all = (int)((int64_t)(split + 1) * ntiles / a.splits);
+  }
+
   __shared__ int32_t sm_blk[kPrefillChunkTiles];
+  __shared__ __attribute__((aligned(16))) char sm_k[kStageKeys * PITCH];
+  __shared__ __attribute__((aligned(16))) char sm_v[kStageKeys * PITCH];
 
   for (int row_g0 = blockIdx.x * ROWS_G; row_g0 < rows; row_g0 += gridDim.x * ROWS_G) {
-    const int last_row_g = min(rows, row_g0 + ROWS_G) - 1;
-    const int ntiles_g = (first_pos + last_row_g / G) / 16 + 1;
     const int row_w0 = row_g0 + wave * ROWS_W;
     const bool live = row_w0 < rows;
+    const int last_row_g = min(rows, row_g0 + ROWS_G) - 1;
     const int last_row_w = min(rows, row_w0 + ROWS_W) - 1;
-    const int ntiles_w = live ? (first_pos + last_row_w / G) / 16 + 1 : 0;
-    const int minpos_w = first_pos + row_w0 / G;
+    // key tiles: [k_lo, k_hi) for the workgroup, [k_lo, k_hi_w) for this wavefront
+    int k_hi, k_hi_w, minpos_w = 0;
+    if constexpr (JOB == kPrefillJob) {
+      k_hi = (first_pos + last_row_g / G) / 16 + 1;
+      k_hi_w = live ? (first_pos + last_row_w / G) / 16 + 1 : 0;
+      minpos_w = first_pos + row_w0 / G;
+    } else {
+      k_hi = k_hi_all;
+      k_hi_w = live ? k_hi_all : k_lo;
+    }
 
-    // q fragments and positions of this lane's column in each row block
     typename T::QFrag qf[R];
     int pos[R];
 #pragma unroll
     for (int rb = 0; rb < R; ++rb) {
       const int rr = row_w0 + 16 * rb + (lane & 15);
       const bool valid = rr < rows;
-      const int tok = valid ? rr / G : 0;
-      const int g = valid ? rr - tok * G : 0;
-      const QElem<CT>* qrow = static_cast<const QElem<CT>*>(a.q) +
-                              ((int64_t)(q0 + tok) * Hq + hk * G + g) * D;
-      qf[rb] = T::load_q(qrow, valid, lane);
-      pos[rb] = valid ? first_pos + tok : ctx - 1;  // padding columns see every key
+      const int t = valid ? rr / G : 0;  // query token (prefill) or sequence (prefix)
+      const int g = valid ? rr - t * G : 0;
+      qf[rb] = T::load_q(static_cast<const QElem<CT>*>(a.q) + ((int64_t)(q0 + t) * Hq + hk * G + g) * D,
+                         valid, lane);
+      pos[rb] = valid ? first_pos + t : ctx - 1;  // padding columns see every key
     }
     Softmax<VE> st[R];
 #pragma unroll
@@ -113,37 +179,57 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
 #pragma unroll
       for (int r = 0; r < VE; ++r) st[rb].acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int c0 = 0; c0 < ntiles_g; c0 += kPrefillChunkTiles) {
-      const int c1 = min(ntiles_g, c0 + kPrefillChunkTiles);
-      __syncthreads();  // every wave is done with the previous ids
+    for (int c0 = k_lo; c0 < k_hi; c0 += kPrefillChunkTiles) {
+      const int c1 = min(k_hi, c0 + kPrefillChunkTiles);
+      __syncthreads();  // the previous pass is done with the ids and the stage
       for (int i = threadIdx.x; i < c1 - c0; i += NW * 64) sm_blk[i] = table[((c0 + i) * 16) / bs];
       __syncthreads();
-      const int end = min(c1, ntiles_w);
-      // batches of NBUF tiles: loads issued back to back, then computed in order
-      for (int k = c0; k < end; k += NBUF) {
-        T buf[NBUF];
+
+      // staged copy of stage [t0, t0 + kStageTiles): piece p of a pool is key
+      // p / PER_ROW, 16-byte column p % PER_ROW
+      u32x4 rk[PIECES], rv[PIECES];
+      auto fetch = [&](int tile0) {
 #pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-          const int t = min(k + j, end - 1);
-          buf[j].load(a.kc, a.vc, (int64_t)sm_blk[t - c0] * block_rows + head_rows + ((t * 16) % bs),
-                      lane);
+        for (int i = 0; i < PIECES; ++i) {
+          const int p = threadIdx.x + i * NW * 64;
+          const int key = p / PER_ROW, col = p - key * PER_ROW;
+          const int t = min(tile0 + key / 16, c1 - 1);  // past the end: a valid tile, unused
+          const int64_t row = (int64_t)sm_blk[t - c0] * block_rows + head_rows + ((t * 16) % bs) + (key & 15);
+          rk[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) + row * RB + col * 16);
+          rv[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.vc) + row * RB + col * 16);
         }
+      };
+      fetch(c0);
+      for (int t0s = c0; t0s < c1; t0s += kStageTiles) {
+        __syncthreads();  // every wave has finished reading the previous stage
 #pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-          if (k + j >= end) break;
-          const int t0 = (k + j) * 16;
+        for (int i = 0; i < PIECES; ++i) {
+          const int p = threadIdx.x + i * NW * 64;
+          const int key = p / PER_ROW, col = p - key * PER_ROW;
+          *reinterpret_cast<u32x4*>(sm_k + key * PITCH + col * 16) = rk[i];
+          *reinterpret_cast<u32x4*>(sm_v + key * PITCH + col * 16) = rv[i];
+        }
+        __syncthreads();
+        if (t0s + kStageTiles < c1) fetch(t0s + kStageTiles);  // in flight during the compute
+#pragma unroll
+        for (int j = 0; j < kStageTiles; ++j) {
+          const int tile = t0s + j;
+          if (tile >= k_hi_w) break;  // wave-uniform
+          const int t0 = tile * 16;
+          T tl;
+          tl.load_pitched(sm_k + j * 16 * PITCH, sm_v + j * 16 * PITCH, PITCH, lane);
           if (t0 + 16 > ctx) {  // V rows past the context may hold any bits
             bool ok[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) ok[i] = t0 + 4 * (lane >> 4) + i < ctx;
-            buf[j].mask_rows(ok);
+            tl.mask_rows(ok);
           }
-          const typename T::PV pv = buf[j].pack_v();
-          const bool causal = t0 + 15 > minpos_w;
+          const typename T::PV pv = tl.pack_v();
+          const bool causal = JOB == kPrefillJob && t0 + 15 > minpos_w;
 #pragma unroll
           for (int rb = 0; rb < R; ++rb)
-            prefill_update<CT, D>(buf[j].scores(qf[rb]), pv, st[rb], t0, pos[rb], causal,
-                                  a.qk_scale, lane);
+            prefill_update<CT, D>(tl.scores(qf[rb]), pv, st[rb], t0, pos[rb], causal, a.qk_scale,
+                                  lane);
         }
       }
     }
@@ -155,9 +241,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
         l_run += __shfl_xor(l_run, 16);
         l_run += __shfl_xor(l_run, 32);
         const int rr = row_w0 + 16 * rb + (lane & 15);
-        if (rr < rows) {
-          const int tok = rr / G, g = rr - tok * G;
-          const int64_t orow = (int64_t)(q0 + tok) * Hq + hk * G + g;
+        if (rr >= rows) continue;
+        const int t = rr / G, g = rr - t * G;
+        if constexpr (JOB == kPrefillJob) {
+          const int64_t orow = (int64_t)(q0 + t) * Hq + hk * G + g;
           const float inv = a.v_scale / l_run;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -166,90 +253,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
             for (int r = 0; r < VE; ++r) x[r] = st[rb].acc[r][i] * inv;
             store_run<CT, VE>(a.out, orow * D + VE * (4 * (lane >> 4) + i), x);
           }
-        }
-      }
-    }
-  }
-}
-
-// The shared-prefix part of a cascade decode: every sequence's query heads
-// (rows s * G + g of one KV head) against one split of the prefix's tiles, no
-// mask (every query sits past the whole prefix).  Each row leaves its partial
-// state (running max in log2 units, sum, unnormalised accumulator) in the
-// balanced merge's slot layout; the merge adds the sequence's own tail.
-template <int CT, int D, int R, int NBUF>
-__global__ __launch_bounds__(kPrefillWaves * 64) void shared_prefix_kernel(PrefixArgs a) {
-  using T = Tile<CT, D>;
-  constexpr int VE = T::VE;
-  constexpr int NW = kPrefillWaves;
-  constexpr int ROWS_W = 16 * R;
-  constexpr int ROWS_G = ROWS_W * NW;
-  const int split = blockIdx.z, hk = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = a.group, Hq = a.num_q_heads, bs = a.block_size;
-  const int rows = a.num_seqs * G;
-  const int ntiles = a.prefix_len / 16;
-  const int k0 = (int)((int64_t)split * ntiles / a.splits);
-  const int k1 = (int)((int64_t)(split + 1) * ntiles / a.splits);
-  const int64_t head_rows = (int64_t)hk * bs;
-  const int64_t block_rows = (int64_t)a.num_kv_heads * bs;
-  __shared__ int32_t sm_blk[kPrefillChunkTiles];
-
-  for (int row_g0 = blockIdx.x * ROWS_G; row_g0 < rows; row_g0 += gridDim.x * ROWS_G) {
-    const int row_w0 = row_g0 + wave * ROWS_W;
-    const bool live = row_w0 < rows;
-    typename T::QFrag qf[R];
-#pragma unroll
-    for (int rb = 0; rb < R; ++rb) {
-      const int rr = row_w0 + 16 * rb + (lane & 15);
-      const bool valid = rr < rows;
-      const int s = valid ? rr / G : 0;
-      const int g = valid ? rr - s * G : 0;
-      qf[rb] = T::load_q(static_cast<const QElem<CT>*>(a.q) + ((int64_t)s * Hq + hk * G + g) * D,
-                         valid, lane);
-    }
-    Softmax<VE> st[R];
-#pragma unroll
-    for (int rb = 0; rb < R; ++rb)
-#pragma unroll
-      for (int r = 0; r < VE; ++r) st[rb].acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int c0 = k0; c0 < k1; c0 += kPrefillChunkTiles) {
-      const int c1 = min(k1, c0 + kPrefillChunkTiles);
-      __syncthreads();
-      for (int i = threadIdx.x; i < c1 - c0; i += NW * 64) sm_blk[i] = a.blocks[((c0 + i) * 16) / bs];
-      __syncthreads();
-      if (!live) continue;
-      for (int k = c0; k < c1; k += NBUF) {
-        T buf[NBUF];
-#pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-          const int t = min(k + j, c1 - 1);
-          buf[j].load(a.kc, a.vc, (int64_t)sm_blk[t - c0] * block_rows + head_rows + ((t * 16) % bs),
-                      lane);
-        }
-#pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-          if (k + j >= c1) break;
-          const typename T::PV pv = buf[j].pack_v();
-#pragma unroll
-          for (int rb = 0; rb < R; ++rb)
-            prefill_update<CT, D>(buf[j].scores(qf[rb]), pv, st[rb], 0, 0, false, a.qk_scale, lane);
-        }
-      }
-    }
-
-    if (live) {
-#pragma unroll
-      for (int rb = 0; rb < R; ++rb) {
-        float l_run = st[rb].l;
-        l_run += __shfl_xor(l_run, 16);
-        l_run += __shfl_xor(l_run, 32);
-        const int rr = row_w0 + 16 * rb + (lane & 15);
-        if (rr < rows) {
-          const int s = rr / G, g = rr - s * G;
-          const int64_t slot = a.slot0 + ((int64_t)s * a.num_kv_heads + hk) * a.splits + split;
+        } else {
+          const int64_t slot = a.slot0 + ((int64_t)t * a.num_kv_heads + hk) * a.splits + blockIdx.z;
           float* o = a.ws_acc + (slot * G + g) * D;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -271,7 +276,8 @@ hipError_t launch_prefix_d(const PrefixArgs& a, hipStream_t stream) {
   int64_t gx = ((int64_t)a.num_seqs * a.group + ROWS_G - 1) / ROWS_G;
   gx = gx < 1 ? 1 : gx > 65535 ? 65535 : gx;
   const dim3 grid((unsigned)gx, (unsigned)a.num_kv_heads, (unsigned)a.splits);
-  hipLaunchKernelGGL((shared_prefix_kernel<CT, D, 2, 2>), grid, dim3(kPrefillWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((rows_kernel<CT, D, 2, kPrefixJob, PrefixArgs>), grid, dim3(kPrefillWaves * 64), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -289,7 +295,8 @@ hipError_t launch_r(const PrefillArgs& a, hipStream_t stream) {
   int64_t gx = (rows + ROWS_G - 1) / ROWS_G;
   gx = gx < 1 ? 1 : gx > 65535 ? 65535 : gx;
   const dim3 grid((unsigned)gx, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((prefill_kernel<CT, D, R, 2>), grid, dim3(kPrefillWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((rows_kernel<CT, D, R, kPrefillJob, PrefillArgs>), grid, dim3(kPrefillWaves * 64), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -298,8 +305,8 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
   switch (a.rows_per_wave) {
     case 16: return launch_r<CT, D, 1>(a, stream);
     case 32: return launch_r<CT, D, 2>(a, stream);
-    case 64:  // f32 fragments are twice as large: 64 rows would spill
-      if constexpr (CT != PKV_F32) return launch_r<CT, D, 4>(a, stream);
+    case 64:  // with head_dim 128 or f32 fragments, 64 rows per wavefront would spill
+      if constexpr (CT != PKV_F32 && D == 64) return launch_r<CT, D, 4>(a, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

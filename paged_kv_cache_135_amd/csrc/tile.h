@@ -82,6 +82,16 @@ struct Tile<PKV_BF16, D> {
   u32x4 k[KC];
   VRow v[4];
 
+  // The same fragments from rows `pitch` bytes apart starting at kb / vb (an
+  // LDS copy of the tile, rows padded against bank conflicts).
+  __device__ __forceinline__ void load_pitched(const char* kb, const char* vb, int pitch, int lane) {
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      k[c] = *reinterpret_cast<const u32x4*>(kb + (lane & 15) * pitch + 2 * (c * 32 + (lane >> 4) * 8));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * pitch + 2 * VE * (lane & 15));
+  }
   __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t row0, int lane) {
     const uint16_t* kb = static_cast<const uint16_t*>(kc) + row0 * D;
     const uint16_t* vb = static_cast<const uint16_t*>(vc) + row0 * D;
@@ -177,6 +187,14 @@ struct Tile<PKV_FP8_E4M3, D> {
   u32x4 k[KC];
   VRow v[4];
 
+  __device__ __forceinline__ void load_pitched(const char* kb, const char* vb, int pitch, int lane) {
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      k[c] = *reinterpret_cast<const u32x4*>(kb + (lane & 15) * pitch + 16 * ((lane >> 4) + 4 * c));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * pitch + VE * (lane & 15));
+  }
   __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t row0, int lane) {
     const uint8_t* kb = static_cast<const uint8_t*>(kc) + row0 * D;
     const uint8_t* vb = static_cast<const uint8_t*>(vc) + row0 * D;
@@ -325,6 +343,17 @@ struct Tile<PKV_F32, D> {
   f32x4 k[KC];
   f32x4 v[4][VE / 4];
 
+  __device__ __forceinline__ void load_pitched(const char* kb, const char* vb, int pitch, int lane) {
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      k[c] = *reinterpret_cast<const f32x4*>(kb + (lane & 15) * pitch + 16 * (4 * c + (lane >> 4)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < VE / 4; ++w)
+        v[j][w] = *reinterpret_cast<const f32x4*>(vb + (4 * (lane >> 4) + j) * pitch +
+                                                  4 * (VE * (lane & 15) + 4 * w));
+  }
   __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t row0, int lane) {
     const float* kb = static_cast<const float*>(kc) + row0 * D;
     const float* vb = static_cast<const float*>(vc) + row0 * D;
