@@ -154,3 +154,39 @@ def test_c5_e4m3_sampled_rows():
     case, got, ref, rm = _full("c5", workloads.c5_fp8, ("balanced", 0, 0, 0), row_mask=rows,
                                tokens_mask_fn=tokens)
     gu.assert_close(got, ref, "fp8_e4m3", "c5", mask=rm)
+
+
+def test_many_sequences_take_the_long_scan_path():
+    """More than 512 sequences: the balanced split keeps only 512 tile counts
+    in registers and re-reads the lengths for the rest; empty and one-token
+    contexts are mixed in."""
+    rng = np.random.default_rng(41)
+    lens = rng.integers(0, 90, size=1300)
+    lens[::97] = 0
+    lens[5::101] = 1
+    case = workloads.build_case("many", seed=41, context_lens=lens, num_q_heads=8,
+                                num_kv_heads=2, head_dim=64, block_size=16, cache_dtype="bf16",
+                                std=0.5, scale=0.125, new_token_step=False)
+    g = gu.GpuCase(case)
+    kc, vc = gu.oracle_caches(case)
+    ref = gu.oracle_decode(case, kc, vc)
+    for m in [("balanced", 0, 0, 0), ("balanced", 0, 0, 333), ("auto", 0, 0, 0),
+              ("single", 0, 4, 0)]:
+        got = gu.host(g.decode_mode(m))
+        gu.assert_close(got, ref, "bf16", f"1300 sequences {_mid(m)}")
+        assert np.all(gu.as_f64(got[lens == 0]) == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3", "f32"])
+def test_largest_block_size(dtype):
+    """block_size 256 (the largest supported): 16 tiles per block."""
+    case = workloads.build_case("bs256", seed=43, context_lens=[1, 255, 256, 257, 700],
+                                num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=256,
+                                cache_dtype=dtype, std=0.5 if dtype != "f32" else 1.0,
+                                scale=1.0 / math.sqrt(128))
+    g = gu.GpuCase(case)
+    g.fill_and_step_writes()
+    kc, vc = gu.oracle_caches(case)
+    ref = gu.oracle_decode(case, kc, vc)
+    for m in [("single", 0, 2, 0), ("partitioned", 512, 4, 0), ("balanced", 0, 0, 9)]:
+        gu.assert_close(gu.host(g.decode_mode(m)), ref, dtype, f"bs 256 {_mid(m)}")

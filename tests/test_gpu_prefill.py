@@ -146,3 +146,16 @@ def test_full_size_qwen_prefill_on_sampled_sequences():
             np.ascontiguousarray(case.context_lens[s:s + 1]),
             np.array([0, b - a], np.int32), case.scale, case.block_size)
         gu.assert_close(got[a:b], ref, "bf16", f"full-size prefill, sequence {s}")
+
+
+def test_largest_block_size_and_long_chunk():
+    """block_size 256 and a 1,100-token chunk after a 300-token prefix."""
+    case = workloads.build_prefill_case("bs256", seed=47, prefix_lens=[300, 0],
+                                        chunk_lens=[1100, 257], num_q_heads=16, num_kv_heads=2,
+                                        head_dim=128, block_size=256, cache_dtype="bf16",
+                                        std=0.5, scale=1.0 / math.sqrt(128))
+    g = gu.GpuCase(case)
+    qs = gu.dev(case.query_start)
+    ref = _oracle(case, case.key_cache, case.value_cache)
+    for rpw in (16, 32):
+        gu.assert_close(gu.host(_run(g, case, qs, rpw)), ref, "bf16", f"bs 256 rows/wave {rpw}")
