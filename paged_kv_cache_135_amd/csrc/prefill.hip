@@ -99,6 +99,46 @@ enum RowsJob : int { kPrefillJob = 0, kPrefixJob = 1 };
 // the pool into LDS (16 bytes per thread and piece), then every wavefront
 // reads its MFMA fragments from LDS.  The next stage's global loads are issued
 // before the current stage is computed, so they are in flight meanwhile.
+// The same update for two tiles at once (keys t0 .. t0+31): one max, one
+// rescale, and P.V on the double-rate K=32 MFMA.  A second tile that is out of
+// range has all its scores at -inf (and its V rows zeroed by the caller).
+template <int CT, int D>
+__device__ __forceinline__ void prefill_update2(const f32x4 sa, const f32x4 sb,
+                                                const typename Tile<CT, D>::PV2& pv,
+                                                Softmax<D / 16>& st, int t0, int pos, bool causal,
+                                                bool b_live, float qk_scale, int lane) {
+  constexpr int VE = D / 16;
+  float pa[4], pb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = t0 + 4 * (lane >> 4) + i;
+    pa[i] = sa[i] * qk_scale;
+    pb[i] = sb[i] * qk_scale;
+    if (causal) {
+      pa[i] = key <= pos ? pa[i] : kNegInf;
+      pb[i] = key + 16 <= pos ? pb[i] : kNegInf;
+    }
+    pb[i] = b_live ? pb[i] : kNegInf;
+  }
+  const float bm = max_over_lane_groups(fmaxf(fmaxf(fmaxf(pa[0], pa[1]), fmaxf(pa[2], pa[3])),
+                                              fmaxf(fmaxf(pb[0], pb[1]), fmaxf(pb[2], pb[3]))));
+  const bool grow = bm > st.m + kLazyMax;
+  const float m_new = grow ? bm : st.m;
+  if (__ballot(grow) != 0) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+#pragma unroll
+    for (int r = 0; r < VE; ++r) st.acc[r] *= alpha;
+    st.l *= alpha;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pa[i] = __builtin_amdgcn_exp2f(pa[i] - m_new);
+    pb[i] = __builtin_amdgcn_exp2f(pb[i] - m_new);
+  }
+  st.l += Tile<CT, D>::pv2(pv, pa, pb, st.acc);
+  st.m = m_new;
+}
+
 template <int CT, int D, int R, int JOB, typename Args>
 __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
   using T = Tile<CT, D>;
@@ -211,25 +251,48 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
         }
         __syncthreads();
         if (t0s + kStageTiles < c1) fetch(t0s + kStageTiles);  // in flight during the compute
-#pragma unroll
-        for (int j = 0; j < kStageTiles; ++j) {
-          const int tile = t0s + j;
-          if (tile >= k_hi_w) break;  // wave-uniform
-          const int t0 = tile * 16;
-          T tl;
+        auto load_masked = [&](T& tl, int j, bool in_range) {
+          const int t0 = (t0s + j) * 16;
           tl.load_pitched(sm_k + j * 16 * PITCH, sm_v + j * 16 * PITCH, PITCH, lane);
-          if (t0 + 16 > ctx) {  // V rows past the context may hold any bits
+          if (!in_range || t0 + 16 > ctx) {  // V rows past the context may hold any bits
             bool ok[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ok[i] = t0 + 4 * (lane >> 4) + i < ctx;
+            for (int i = 0; i < 4; ++i) ok[i] = in_range && t0 + 4 * (lane >> 4) + i < ctx;
             tl.mask_rows(ok);
           }
-          const typename T::PV pv = tl.pack_v();
-          const bool causal = JOB == kPrefillJob && t0 + 15 > minpos_w;
+        };
+        if constexpr (CT == PKV_F32) {  // no K=32 f32 MFMA: one tile at a time
 #pragma unroll
-          for (int rb = 0; rb < R; ++rb)
-            prefill_update<CT, D>(tl.scores(qf[rb]), pv, st[rb], t0, pos[rb], causal, a.qk_scale,
-                                  lane);
+          for (int j = 0; j < kStageTiles; ++j) {
+            const int tile = t0s + j;
+            if (tile >= k_hi_w) break;  // wave-uniform
+            const int t0 = tile * 16;
+            T tl;
+            load_masked(tl, j, true);
+            const typename T::PV pv = tl.pack_v();
+            const bool causal = JOB == kPrefillJob && t0 + 15 > minpos_w;
+#pragma unroll
+            for (int rb = 0; rb < R; ++rb)
+              prefill_update<CT, D>(tl.scores(qf[rb]), pv, st[rb], t0, pos[rb], causal, a.qk_scale,
+                                    lane);
+          }
+        } else {  // tile pairs on the double-rate MFMA
+#pragma unroll
+          for (int j = 0; j < kStageTiles; j += 2) {
+            const int tile = t0s + j;
+            if (tile >= k_hi_w) break;  // wave-uniform
+            const bool b_live = tile + 1 < k_hi_w;
+            const int t0 = tile * 16;
+            T ta, tb;
+            load_masked(ta, j, true);
+            load_masked(tb, j + 1, b_live);
+            const typename T::PV2 pv = T::pack_v2(ta, tb);
+            const bool causal = JOB == kPrefillJob && t0 + 31 > minpos_w;
+#pragma unroll
+            for (int rb = 0; rb < R; ++rb)
+              prefill_update2<CT, D>(ta.scores(qf[rb]), tb.scores(qf[rb]), pv, st[rb], t0, pos[rb],
+                                     causal, b_live, a.qk_scale, lane);
+          }
         }
       }
     }
