@@ -74,9 +74,9 @@ __device__ __forceinline__ void prefill_update(const f32x4 sacc, const typename 
   st.m = m_new;
 }
 
-// K/V of kStageKeys keys of one KV head staged in LDS, rows padded by 16
-// bytes so that the 16 lanes reading one 16-byte column of 16 different rows
-// hit 16 different bank groups.
+// K/V of kStageKeys keys of one KV head staged in LDS, rows padded by 32
+// bytes: the lanes reading one 16-byte column of 16 different rows then meet
+// the fewest bank conflicts (measured against 0, 16, 48, 64 and 96 bytes).
 constexpr int kStageKeys = 128;
 constexpr int kStageTiles = kStageKeys / 16;
 template <int CT, int D>
@@ -85,7 +85,7 @@ constexpr int row_bytes() {
 }
 template <int CT, int D>
 constexpr int lds_pitch() {
-  return row_bytes<CT, D>() + 16;
+  return row_bytes<CT, D>() + 32;
 }
 
 enum RowsJob : int { kPrefillJob = 0, kPrefixJob = 1 };
@@ -149,8 +149,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
   constexpr int RB = row_bytes<CT, D>();
   constexpr int PITCH = lds_pitch<CT, D>();
   constexpr int PER_ROW = RB / 16;                          // 16-byte pieces per key row
-  constexpr int PIECES = kStageKeys * PER_ROW / (NW * 64);  // per thread and pool
-  static_assert(PIECES >= 1 && kStageKeys * PER_ROW % (NW * 64) == 0, "stage split");
+  constexpr int TOTAL = kStageKeys * PER_ROW;               // pieces per stage and pool
+  constexpr int PIECES = (TOTAL + NW * 64 - 1) / (NW * 64);  // per thread and pool
+  static_assert(TOTAL % (NW * 64) == 0 || TOTAL < NW * 64, "stage split");
   const int hk = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -232,6 +233,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < PIECES; ++i) {
           const int p = threadIdx.x + i * NW * 64;
+          if (TOTAL < NW * 64 && p >= TOTAL) break;  // fewer pieces than threads
           const int key = p / PER_ROW, col = p - key * PER_ROW;
           const int t = min(tile0 + key / 16, c1 - 1);  // past the end: a valid tile, unused
           const int64_t row = (int64_t)sm_blk[t - c0] * block_rows + head_rows + ((t * 16) % bs) + (key & 15);
@@ -245,6 +247,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < PIECES; ++i) {
           const int p = threadIdx.x + i * NW * 64;
+          if (TOTAL < NW * 64 && p >= TOTAL) break;
           const int key = p / PER_ROW, col = p - key * PER_ROW;
           *reinterpret_cast<u32x4*>(sm_k + key * PITCH + col * 16) = rk[i];
           *reinterpret_cast<u32x4*>(sm_v + key * PITCH + col * 16) = rv[i];
