@@ -369,19 +369,22 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
   // costs n + kPieceCost units, the first kPieceCost standing for the fixed
   // cost of starting a piece (its q rows, block ids and partial state), so a
   // run that crosses into a new pair gets fewer tiles.
-  // Tile counts of up to kScanRegs * 64 sequences stay in registers (lane l
-  // holds sequences l, l+64, ...); longer batches re-read the lengths.
+  // Lengths of up to kScanRegs * 64 sequences stay in registers (lane l
+  // holds sequences l, l+64, ...), so a piece start reads its length with a
+  // readlane instead of a dependent load; longer batches re-read the rest.
   // Sequences with no tokens have no tiles: worker s % W writes their zero rows.
   constexpr int kScanRegs = 8;
   constexpr int kPieceCost = piece_cost<CT>();
   auto units = [](uint32_t n) { return n ? n + (uint32_t)kPieceCost : 0u; };
-  uint32_t nreg[kScanRegs];
+  int creg[kScanRegs];
+#pragma unroll
+  for (int i = 0; i < kScanRegs; ++i) creg[i] = 0;
   int64_t total = 0;
   for (int c = 0, r = 0; c < S; c += 64, ++r) {
     const int s = c + lane;
     const int ctx = s < S ? max(0, a.lens[s] - a.len_offset) : 0;
     const uint32_t n = (uint32_t)((ctx + 15) >> 4);
-    if (r < kScanRegs) nreg[r] = n;
+    if (r < kScanRegs) creg[r] = ctx;
     total += wave_sum(units(n));
     uint64_t zmask = __ballot(s < S && ctx == 0 && s % W == w);
     while (zmask) {
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
     for (int c = 0, r = 0; c < S; c += 64, ++r) {
       const int s = c + lane;
       uint32_t n;
-      if (r < kScanRegs) n = nreg[r];
+      if (r < kScanRegs) n = (uint32_t)((creg[r] + 15) >> 4);
       else n = s < S ? (uint32_t)((max(0, a.lens[s] - a.len_offset) + 15) >> 4) : 0u;
       const uint32_t u = units(n);
       const uint32_t incl = wave_incl_scan(u, lane);
@@ -438,8 +441,23 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
   int64_t x = x0;
   int32_t carry = 0;      // first-batch block ids of the next piece, loaded ahead
   bool has_carry = false;
+  // the run's sequences lie in the 64-sequence chunk of s_cur and, for runs
+  // that cross it, the next one: keep those two registers
+  const int r0 = s_cur >> 6;
+  int cw0 = 0, cw1 = 0;
+#pragma unroll
+  for (int i = 0; i < kScanRegs; ++i) {
+    if (i == r0) cw0 = creg[i];
+    if (i == r0 + 1) cw1 = creg[i];
+  }
+  auto ctx_of = [&](int sq) -> int {  // sq wave-uniform
+    const int r = sq >> 6;
+    if (r == r0 && r < kScanRegs) return __builtin_amdgcn_readlane(cw0, sq & 63);
+    if (r == r0 + 1 && r < kScanRegs) return __builtin_amdgcn_readlane(cw1, sq & 63);
+    return max(0, a.lens[sq] - a.len_offset);
+  };
   while (x < x1 && s_cur < S) {
-    const int ctx = max(0, a.lens[s_cur] - a.len_offset);
+    const int ctx = ctx_of(s_cur);
     const int n = (ctx + 15) >> 4;
     if (n == 0) {
       ++s_cur;
