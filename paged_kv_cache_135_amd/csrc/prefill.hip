@@ -18,14 +18,19 @@
 //   A wavefront owns R blocks of 16 rows (the B operand's 16 columns); a
 //   workgroup of NW wavefronts owns 16 R NW consecutive rows.
 // * Keys: 16-token tiles from position 0 up to the last position among the
-//   wavefront's rows, loaded straight from the pool in the MFMA operand layout
-//   (the decode tile fragments); V is packed once per tile and reused by the R
-//   row blocks.  Block ids of the workgroup's tiles are staged in LDS.
-// * Causal mask by select (scores of keys past a row's position -> -inf) only
-//   on tiles that reach past the wavefront's first position; V rows past the
-//   context are zeroed by select.  Tiles are visited in increasing order, so
-//   key 0 (visible to every row) comes first and every running max is finite
-//   from the first tile on.
+//   wavefront's rows, staged per workgroup through LDS.  bf16 and E4M3 caches
+//   become bf16 images there: K row-major with an XOR swizzle of its 16-byte
+//   chunks, V transposed into the A operand of V^T.P, so the wavefronts read
+//   MFMA operands with plain 16-byte loads and no per-wavefront repacking or
+//   conversion.  f32 caches are staged as they are.
+// * Softmax per block of four tiles (one max and one lazy rescale per block);
+//   the causal mask and the wavefront's range enter as -inf starting values of
+//   the score accumulators on the few blocks that need them, and keys past the
+//   context are zeroed in the staging.  Tiles are visited in increasing order,
+//   so key 0 (visible to every row) comes first and every running max is
+//   finite from the first tile on.
+// * Workgroups take (sequence, row group) jobs longest first (ranked_job), so
+//   the long rows of sequences with long cached prefixes do not start last.
 // * Each row's result is finalised in place: no workspace, no second kernel.
 // * The same machinery serves the shared-prefix part of a cascade decode
 //   (shared_prefix_kernel): all sequences' query heads against one prefix,
@@ -37,28 +42,30 @@ namespace pkv {
 namespace {
 
 constexpr int kPrefillWaves = 8;
-constexpr int kPrefillChunkTiles = 1024;  // block ids staged in LDS per pass
+constexpr int kPrefillChunkTiles = 1024;  // tile row bases staged in LDS per pass
 
 // A column keeps its running max until a score exceeds it by more than
 // kLazyMax (log2 units): its probabilities then stay below 2^kLazyMax and the
 // accumulators need no rescale (an unchanged max rescales by exactly 1).
 constexpr float kLazyMax = 8.0f;
 
-// Online-softmax update of one 16-row block with one tile.
-template <int CT, int D>
-__device__ __forceinline__ void prefill_update(const f32x4 sacc, const typename Tile<CT, D>::PV& pv,
-                                               Softmax<D / 16>& st, int t0, int pos, bool causal,
-                                               float qk_scale, int lane) {
-  constexpr int VE = D / 16;
-  float sc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sc[i] = sacc[i] * qk_scale;
-    if (causal) sc[i] = t0 + 4 * (lane >> 4) + i <= pos ? sc[i] : kNegInf;
-  }
-  const float bm = max_over_lane_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-  // the first tile a column sees holds a visible key (tile 0 holds key 0), so
-  // its running max is finite from then on
+// Online-softmax state of one 16-row block, per lane: column g = lane % 16.
+// Scores enter raw (q.k) and the positive factor qs (scale * log2 e) is
+// applied inside the exponent's FMA, so m is in log2 units of scaled scores.
+template <int VE>
+struct RowState {
+  float m;       // running max reference, identical in the 4 lane groups
+  f32x4 l;       // running sum of the rounded probabilities (see the updates)
+  f32x4 acc[VE];
+};
+
+// Max of one raw-score column over the lane's keys and the other lane groups,
+// scaled into log2 units, and the lazy rescale it may call for.
+template <int VE>
+__device__ __forceinline__ float raise_max(RowState<VE>& st, float local_max, float qs) {
+  const float bm = max_over_lane_groups(local_max) * qs;
+  // a column's first tile holds a visible key (tile 0 holds key 0), so its
+  // running max is finite from then on; a fully masked tile leaves bm = -inf
   const bool grow = bm > st.m + kLazyMax;
   const float m_new = grow ? bm : st.m;
   if (__ballot(grow) != 0) {  // wave-uniform: some column's max moved
@@ -67,25 +74,253 @@ __device__ __forceinline__ void prefill_update(const f32x4 sacc, const typename 
     for (int r = 0; r < VE; ++r) st.acc[r] *= alpha;
     st.l *= alpha;
   }
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
-  st.l += Tile<CT, D>::pv_packed(pv, p, st.acc);
   st.m = m_new;
+  return m_new;
 }
 
-// K/V of kStageKeys keys of one KV head staged in LDS, rows padded by 32
-// bytes: the lanes reading one 16-byte column of 16 different rows then meet
-// the fewest bank conflicts (measured against 0, 16, 48, 64 and 96 bytes).
+// Keys are staged in LDS kStageKeys at a time.
 constexpr int kStageKeys = 128;
 constexpr int kStageTiles = kStageKeys / 16;
-template <int CT, int D>
-constexpr int row_bytes() {
-  return D * (CT == PKV_F32 ? 4 : CT == PKV_BF16 ? 2 : 1);
+constexpr int kBlockTiles = 4;  // tiles per softmax block (bf16 images)
+
+// f32 caches: K and V rows copied as they are, padded by 32 bytes so that the
+// lanes reading one 16-byte column of 16 different rows meet the fewest bank
+// conflicts (measured against 0, 16, 48, 64 and 96 bytes).
+template <int D>
+constexpr int f32_pitch() {
+  return 4 * D + 32;
 }
-template <int CT, int D>
-constexpr int lds_pitch() {
-  return row_bytes<CT, D>() + 32;
+// bf16 and E4M3 caches: bf16 images of K and V.
+// K: rows of 2D bytes, the 16-byte chunk n of key row k stored at chunk
+// n ^ k_swizzle(k), so that the 16 rows one MFMA operand read touches (one
+// chunk each) fall in distinct banks.
+// V: transposed per tile pair into the A operand of V^T.P: for MFMA row m
+// (d = VE*m + r) and lane group q, 16 bytes hold the bf16 values at d of keys
+// 4q..4q+3 of tile a, then of tile b, at byte 1024 r + 256 q + 16 m of the
+// pair's block, so each 16-lane group of one read covers 256 contiguous bytes.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int key) {
+  return D == 128 ? (key & 15) : ((key >> 1) & 7);  // rows 256 / 128 bytes long
+}
+template <int D>
+constexpr int vpair_bytes() {
+  return 64 * D;
+}
+
+// Probabilities of one column from raw scores x (dropped keys at -inf).
+template <int VE, int N>
+__device__ __forceinline__ void probabilities(RowState<VE>& st, const float (&x)[N], float qs, float (&p)[N]) {
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) mx = fmaxf(mx, x[i]);
+  const float m = raise_max(st, mx, qs);
+#pragma unroll
+  for (int i = 0; i < N; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qs, -m));
+}
+
+// f32 caches, one tile (keys t0 .. t0+15) for the R row blocks on the
+// 16x16x4 f32 MFMA; l[0] holds this lane's share of the column sum.
+// MASKED: keys past lim[rb] (the column's position - t0 - 4 * lane group)
+// are dropped.
+template <int D, int R, bool MASKED>
+__device__ __forceinline__ void update_tile_f32(const Tile<PKV_F32, D>& tl,
+                                                const typename Tile<PKV_F32, D>::QFrag (&qf)[R],
+                                                RowState<D / 16> (&st)[R], const int (&lim)[R], float qs) {
+  f32x4 s[R];
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) s[rb] = tl.scores(qf[rb]);
+  const typename Tile<PKV_F32, D>::PV pv = tl.pack_v();
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    float x[4], p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = !MASKED || i <= lim[rb] ? s[rb][i] : kNegInf;
+    probabilities(st[rb], x, qs, p);
+    st[rb].l[0] += Tile<PKV_F32, D>::pv_packed(pv, p, st[rb].acc);
+  }
+}
+
+// bf16 images (bf16 and E4M3 caches): a block of NT tiles (keys t0 ..
+// t0 + 16 NT - 1) for the R row blocks, with one max and one rescale per row
+// block for the whole block.  Scores come from the K image (kt: the block's
+// first tile, ko: the lane's chunk offsets); P.V runs per tile pair a, b on the
+// double-rate K=32 MFMA, lane group q carrying keys 4q..4q+3 of a, then of b,
+// in P and in V^T alike.  V^T is read from its LDS image one MFMA row group r
+// at a time (vt + pair block + 1024 r) and feeds every row block.  The column
+// sums come from one more MFMA against an all-ones A operand, so every lane's
+// l[0] is its column's full sum of the rounded probabilities.
+// masked: tiles from `live` on and keys past lim[rb] (the column's position -
+// t0 - 4 * lane group) are dropped by starting their score accumulators at
+// -inf; the staging zeroes K and V past the context, so the sums stay -inf.
+template <int D, int R, int NT>
+__device__ __forceinline__ void update_block(const char* kt, const int (&ko)[D / 32],
+                                             const typename Tile<PKV_BF16, D>::QFrag (&qf)[R],
+                                             RowState<D / 16> (&st)[R], const char* vt, bool masked,
+                                             const int (&lim)[R], int live, float qs) {
+  constexpr int VE = D / 16;
+  f32x4 sc[R][NT];
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sc[rb][t][i] = !masked || (t < live && 16 * t + i <= lim[rb]) ? 0.f : kNegInf;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {  // 32 d at a time, every tile and row block
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 k = *reinterpret_cast<const u32x4*>(kt + t * 32 * D + ko[c]);
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) sc[rb][t] = mfma_bf16_k32(k, qf[rb].q[c], sc[rb][t]);
+    }
+  }
+  u32x4 pk[R][NT / 2];
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    float x[4 * NT], p[4 * NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * t + i] = sc[rb][t][i];
+    probabilities(st[rb], x, qs, p);
+#pragma unroll
+    for (int h = 0; h < NT / 2; ++h)
+      pk[rb][h] = u32x4{pack_bf16(p[8 * h], p[8 * h + 1]), pack_bf16(p[8 * h + 2], p[8 * h + 3]),
+                        pack_bf16(p[8 * h + 4], p[8 * h + 5]), pack_bf16(p[8 * h + 6], p[8 * h + 7])};
+  }
+  constexpr uint32_t kOnes = 0x3f803f80u;  // two bf16 1.0
+#pragma unroll
+  for (int h = 0; h < NT / 2; ++h) {
+#pragma unroll
+    for (int r = 0; r < VE; ++r) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(vt + h * vpair_bytes<D>() + 1024 * r);
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) st[rb].acc[r] = mfma_bf16_k32(v, pk[rb][h], st[rb].acc[r]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb)
+      st[rb].l = mfma_bf16_k32(u32x4{kOnes, kOnes, kOnes, kOnes}, pk[rb][h], st[rb].l);
+  }
+}
+
+// q fragments prepared for a positive factor: a negative scale flips the sign
+// bits of q (exact) and a zero scale zeroes q and uses factor 1; scores, max
+// and probabilities are then those of the signed scale.
+__device__ __forceinline__ void condition_q(u32x4& q, uint32_t sign, bool zero) {
+  q = zero ? u32x4{0, 0, 0, 0} : (q ^ sign);
+}
+__device__ __forceinline__ void condition_q(f32x4& q, uint32_t sign, bool zero) {
+  const u32x4 w = __builtin_bit_cast(u32x4, q);
+  q = __builtin_bit_cast(f32x4, zero ? u32x4{0, 0, 0, 0} : (w ^ sign));
+}
+
+// Exclusive prefix sum of one value per thread over a workgroup of NT
+// threads; scratch holds NT / 64 ints.  Every thread calls it.
+template <int NT>
+__device__ int block_exclusive_scan(int v, int* scratch, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) scratch[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const int t = scratch[i];
+    base += i < w ? t : 0;
+    tot += t;
+  }
+  __syncthreads();  // scratch free again
+  total = tot;
+  return base + x - v;
+}
+
+// Longest-first order of a chunked-prefill grid.  A job is (sequence s, row
+// group rg) and costs its key tile count, which grows with the position of the
+// group's last row; workgroups take jobs in decreasing cost (in buckets of
+// 2^shift tiles, at most kRankBuckets of them), then by s, then by rg, so the
+// long jobs start first and the short ones fill in behind them.  Every
+// workgroup computes the same counting sort over the lengths and keeps the
+// job of its own rank; false: no job of that rank.  scratch: kRankBuckets + 16
+// ints of LDS.
+constexpr int kRankBuckets = 2 * kPrefillWaves * 64;
+__device__ bool ranked_job(const PrefillArgs& a, int rows_g, int rank, int* scratch, int& s_out, int& rg_out) {
+  constexpr int NT = kPrefillWaves * 64;
+  const int S = a.num_seqs, G = a.group, tid = threadIdx.x;
+  int* hist = scratch;
+  int* tmp = scratch + kRankBuckets;  // [0, 8): scan, [8, 12): results
+  auto cost = [&](int first, int rows, int rg) {
+    return (first + (min(rows, (rg + 1) * rows_g) - 1) / G) / 16 + 1;
+  };
+  // the largest cost (every sequence's last row group) sets the bucket width
+  int mx = 0;
+  for (int s = tid; s < S; s += NT) {
+    const int nq = a.qstart[s + 1] - a.qstart[s];
+    if (nq > 0) mx = max(mx, cost(a.lens[s] - nq, nq * G, (nq * G - 1) / rows_g));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+  if ((tid & 63) == 0) tmp[tid >> 6] = mx;
+  for (int i = tid; i < kRankBuckets; i += NT) hist[i] = 0;
+  __syncthreads();
+  mx = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) mx = max(mx, tmp[i]);
+  int shift = 0;
+  while ((mx >> shift) >= kRankBuckets) ++shift;
+  __syncthreads();  // tmp read before the scans reuse it
+  for (int s = tid; s < S; s += NT) {
+    const int nq = a.qstart[s + 1] - a.qstart[s], rows = nq * G, first = a.lens[s] - nq;
+    for (int rg = 0; rg * rows_g < rows; ++rg) atomicAdd(&hist[cost(first, rows, rg) >> shift], 1);
+  }
+  __syncthreads();
+  // thread t owns buckets kRankBuckets-1-2t and kRankBuckets-2-2t (descending)
+  const int b0 = kRankBuckets - 1 - 2 * tid, h0 = hist[b0], h1 = hist[b0 - 1];
+  int total;
+  const int above = block_exclusive_scan<NT>(h0 + h1, tmp, total);
+  if (rank >= total) return false;  // workgroup-uniform
+  if (rank >= above && rank < above + h0) {
+    tmp[8] = b0;
+    tmp[9] = rank - above;
+  } else if (rank >= above + h0 && rank < above + h0 + h1) {
+    tmp[8] = b0 - 1;
+    tmp[9] = rank - above - h0;
+  }
+  __syncthreads();
+  const int bucket = tmp[8], off = tmp[9];
+  // the off-th job of that bucket in (s, rg) order: sequences in contiguous
+  // runs per thread
+  const int per = (S + NT - 1) / NT, s_lo = min(S, tid * per), s_hi = min(S, s_lo + per);
+  int cnt = 0;
+  for (int s = s_lo; s < s_hi; ++s) {
+    const int nq = a.qstart[s + 1] - a.qstart[s], rows = nq * G, first = a.lens[s] - nq;
+    for (int rg = 0; rg * rows_g < rows; ++rg) cnt += (cost(first, rows, rg) >> shift) == bucket;
+  }
+  int total2;
+  const int before = block_exclusive_scan<NT>(cnt, tmp, total2);
+  if (off >= before && off < before + cnt) {
+    int k = off - before;
+    for (int s = s_lo; s < s_hi && k >= 0; ++s) {
+      const int nq = a.qstart[s + 1] - a.qstart[s], rows = nq * G, first = a.lens[s] - nq;
+      for (int rg = 0; rg * rows_g < rows && k >= 0; ++rg) {
+        if ((cost(first, rows, rg) >> shift) != bucket) continue;
+        if (k == 0) {
+          tmp[10] = s;
+          tmp[11] = rg;
+        }
+        --k;
+      }
+    }
+  }
+  __syncthreads();
+  s_out = tmp[10];
+  rg_out = tmp[11];
+  return true;
 }
 
 enum RowsJob : int { kPrefillJob = 0, kPrefixJob = 1 };
@@ -95,85 +330,47 @@ enum RowsJob : int { kPrefillJob = 0, kPrefixJob = 1 };
 //     causal, final outputs (PrefillArgs).
 //   kPrefixJob: rows = every sequence's query heads of one KV head against one
 //     key split of a shared prefix, no mask, partial states (PrefixArgs).
-// Per stage the workgroup's 256 threads copy kStageKeys keys of K and V from
-// the pool into LDS (16 bytes per thread and piece), then every wavefront
-// reads its MFMA fragments from LDS.  The next stage's global loads are issued
-// before the current stage is computed, so they are in flight meanwhile.
-// The same update for two tiles at once (keys t0 .. t0+31): one max, one
-// rescale, and P.V on the double-rate K=32 MFMA.  A second tile that is out of
-// range has all its scores at -inf (and its V rows zeroed by the caller).
-template <int CT, int D>
-__device__ __forceinline__ void prefill_update2(const f32x4 sa, const f32x4 sb,
-                                                const typename Tile<CT, D>::PV2& pv,
-                                                Softmax<D / 16>& st, int t0, int pos, bool causal,
-                                                bool b_live, float qk_scale, int lane) {
-  constexpr int VE = D / 16;
-  float pa[4], pb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = t0 + 4 * (lane >> 4) + i;
-    pa[i] = sa[i] * qk_scale;
-    pb[i] = sb[i] * qk_scale;
-    if (causal) {
-      pa[i] = key <= pos ? pa[i] : kNegInf;
-      pb[i] = key + 16 <= pos ? pb[i] : kNegInf;
-    }
-    pb[i] = b_live ? pb[i] : kNegInf;
-  }
-  const float bm = max_over_lane_groups(fmaxf(fmaxf(fmaxf(pa[0], pa[1]), fmaxf(pa[2], pa[3])),
-                                              fmaxf(fmaxf(pb[0], pb[1]), fmaxf(pb[2], pb[3]))));
-  const bool grow = bm > st.m + kLazyMax;
-  const float m_new = grow ? bm : st.m;
-  if (__ballot(grow) != 0) {
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-#pragma unroll
-    for (int r = 0; r < VE; ++r) st.acc[r] *= alpha;
-    st.l *= alpha;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    pa[i] = __builtin_amdgcn_exp2f(pa[i] - m_new);
-    pb[i] = __builtin_amdgcn_exp2f(pb[i] - m_new);
-  }
-  st.l += Tile<CT, D>::pv2(pv, pa, pb, st.acc);
-  st.m = m_new;
-}
-
+// Per stage the workgroup's threads copy kStageKeys keys of K and V from the
+// pool into LDS, then every wavefront reads its MFMA fragments from there.
+// The next stage's global loads are issued before the current stage is
+// computed, so they are in flight meanwhile.
 template <int CT, int D, int R, int JOB, typename Args>
 __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
-  using T = Tile<CT, D>;
-  constexpr int VE = T::VE;
+  constexpr bool F32 = CT == PKV_F32;
+  using T = Tile<F32 ? PKV_F32 : PKV_BF16, D>;  // fragments read from LDS
+  constexpr int VE = D / 16;
   constexpr int NW = kPrefillWaves;
   constexpr int ROWS_W = 16 * R;
   constexpr int ROWS_G = ROWS_W * NW;
-  constexpr int RB = row_bytes<CT, D>();
-  constexpr int PITCH = lds_pitch<CT, D>();
-  constexpr int PER_ROW = RB / 16;                          // 16-byte pieces per key row
-  constexpr int TOTAL = kStageKeys * PER_ROW;               // pieces per stage and pool
-  constexpr int PIECES = (TOTAL + NW * 64 - 1) / (NW * 64);  // per thread and pool
-  static_assert(TOTAL % (NW * 64) == 0 || TOTAL < NW * 64, "stage split");
-  const int hk = blockIdx.y;
+  constexpr int EB = CT == PKV_F32 ? 4 : CT == PKV_BF16 ? 2 : 1;  // cache bytes per element
+  constexpr int RB = D * EB;                                     // cache bytes per key row
+  constexpr int PER_ROW = RB / 16;                               // 16-byte pieces per key row
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = a.group, Hq = a.num_q_heads, bs = a.block_size;
-  const int64_t head_rows = (int64_t)hk * bs;
-  const int64_t block_rows = (int64_t)a.num_kv_heads * bs;
+  const int G = a.group, Hq = a.num_q_heads, bs = a.block_size, Hkv = a.num_kv_heads;
+  const int64_t block_rows = (int64_t)Hkv * bs;
+  // the factor applied to raw scores, made positive (condition_q)
+  const float qs_in = a.qk_scale;
+  const bool q_zero = qs_in == 0.f;
+  const uint32_t q_sign = qs_in < 0.f ? (F32 ? 0x80000000u : 0x80008000u) : 0u;
+  const float qs = q_zero ? 1.f : fabsf(qs_in);
 
-  // what this workgroup works on
-  int rows, ctx, first_pos = 0, q0 = 0, k_lo, k_hi_all;
-  const int32_t* table;
-  if constexpr (JOB == kPrefillJob) {
-    const int s = blockIdx.z;
-    q0 = a.qstart[s];
-    const int nq = a.qstart[s + 1] - q0;
-    rows = nq * G;
-    ctx = a.lens[s];
-    first_pos = ctx - nq;
-    table = a.tables + (int64_t)s * a.max_blocks;
-    k_lo = 0;
-    k_hi_all = 0;  // per row group below
-  } else {
-    const int split = blockIdx.z;
+  __shared__ int64_t sm_row[kPrefillChunkTiles];  // pool row of each tile's first key
+  constexpr int K_BYTES = kStageKeys * (F32 ? f32_pitch<D>() : 2 * D);
+  constexpr int V_BYTES = F32 ? kStageKeys * f32_pitch<D>() : (kStageTiles / 2) * vpair_bytes<D>();
+  __shared__ __attribute__((aligned(16))) char sm_k[K_BYTES];
+  __shared__ __attribute__((aligned(16))) char sm_v[V_BYTES];
+  static_assert(K_BYTES >= 4 * (kRankBuckets + 16), "ranking scratch");
+
+  // Jobs: prefill: grid x = job slots x KV heads, job of rank x / Hkv (then +
+  // gridDim.x / Hkv while jobs remain); prefix: x = KV head, y = key split,
+  // z = row group, from the last row group down.
+  const int hk = JOB == kPrefillJob ? (int)(blockIdx.x % Hkv) : (int)blockIdx.x;
+  const int64_t head_rows = (int64_t)hk * bs;
+  int rows = 0, ctx = 0, first_pos = 0, q0 = 0, k_lo = 0, k_hi_all = 0;
+  const int32_t* table = nullptr;
+  if constexpr (JOB == kPrefixJob) {
+    const int split = blockIdx.y;
     const int ntiles = a.prefix_len / 16;
     rows = a.num_seqs * G;
     ctx = a.prefix_len;
@@ -182,11 +379,25 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
     k_hi_all = (int)((int64_t)(split + 1) * ntiles / a.splits);
   }
 
-  __shared__ int32_t sm_blk[kPrefillChunkTiles];
-  __shared__ __attribute__((aligned(16))) char sm_k[kStageKeys * PITCH];
-  __shared__ __attribute__((aligned(16))) char sm_v[kStageKeys * PITCH];
-
-  for (int row_g0 = blockIdx.x * ROWS_G; row_g0 < rows; row_g0 += gridDim.x * ROWS_G) {
+  for (int it = 0;; ++it) {
+    int rg;
+    if constexpr (JOB == kPrefillJob) {
+      __syncthreads();  // the ranking scratch aliases the K stage
+      int s;
+      if (!ranked_job(a, ROWS_G, (int)(blockIdx.x / Hkv) + it * (int)(gridDim.x / Hkv),
+                      reinterpret_cast<int*>(sm_k), s, rg))
+        break;
+      q0 = a.qstart[s];
+      const int nq = a.qstart[s + 1] - q0;
+      rows = nq * G;
+      ctx = a.lens[s];
+      first_pos = ctx - nq;
+      table = a.tables + (int64_t)s * a.max_blocks;
+    } else {
+      rg = (int)(gridDim.z - 1 - blockIdx.z) + it * (int)gridDim.z;
+      if (rg * ROWS_G >= rows) break;
+    }
+    const int row_g0 = rg * ROWS_G;
     const int row_w0 = row_g0 + wave * ROWS_W;
     const bool live = row_w0 < rows;
     const int last_row_g = min(rows, row_g0 + ROWS_G) - 1;
@@ -203,7 +414,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
     }
 
     typename T::QFrag qf[R];
-    int pos[R];
+    int pos4[R];  // the column's position minus 4 * lane group
 #pragma unroll
     for (int rb = 0; rb < R; ++rb) {
       const int rr = row_w0 + 16 * rb + (lane & 15);
@@ -212,89 +423,224 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
       const int g = valid ? rr - t * G : 0;
       qf[rb] = T::load_q(static_cast<const QElem<CT>*>(a.q) + ((int64_t)(q0 + t) * Hq + hk * G + g) * D,
                          valid, lane);
-      pos[rb] = valid ? first_pos + t : ctx - 1;  // padding columns see every key
-    }
-    Softmax<VE> st[R];
 #pragma unroll
-    for (int rb = 0; rb < R; ++rb)
+      for (int c = 0; c < (int)(sizeof(qf[rb].q) / sizeof(qf[rb].q[0])); ++c)
+        condition_q(qf[rb].q[c], q_sign, q_zero);
+      // the prefix job's rows and padding columns see every key
+      pos4[rb] = (JOB == kPrefillJob && valid ? first_pos + t : ctx - 1) - 4 * (lane >> 4);
+    }
+    RowState<VE> st[R];
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb) {
+      st[rb].m = kNegInf;
+      st[rb].l = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < VE; ++r) st[rb].acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     for (int c0 = k_lo; c0 < k_hi; c0 += kPrefillChunkTiles) {
       const int c1 = min(k_hi, c0 + kPrefillChunkTiles);
       __syncthreads();  // the previous pass is done with the ids and the stage
-      for (int i = threadIdx.x; i < c1 - c0; i += NW * 64) sm_blk[i] = table[((c0 + i) * 16) / bs];
+      for (int i = threadIdx.x; i < c1 - c0; i += NW * 64) {
+        const int key0 = (c0 + i) * 16;
+        sm_row[i] = (int64_t)table[key0 / bs] * block_rows + head_rows + key0 % bs;
+      }
       __syncthreads();
 
-      // staged copy of stage [t0, t0 + kStageTiles): piece p of a pool is key
-      // p / PER_ROW, 16-byte column p % PER_ROW
-      u32x4 rk[PIECES], rv[PIECES];
-      auto fetch = [&](int tile0) {
+      if constexpr (F32) {
+        // piece p of a pool is key p / PER_ROW, 16-byte column p % PER_ROW
+        constexpr int PITCH = f32_pitch<D>();
+        constexpr int TOTAL = kStageKeys * PER_ROW;
+        constexpr int PIECES = (TOTAL + NW * 64 - 1) / (NW * 64);
+        static_assert(TOTAL % (NW * 64) == 0 || TOTAL < NW * 64, "stage split");
+        u32x4 rk[PIECES], rv[PIECES];
+        auto fetch = [&](int tile0) {
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i) {
-          const int p = threadIdx.x + i * NW * 64;
-          if (TOTAL < NW * 64 && p >= TOTAL) break;  // fewer pieces than threads
-          const int key = p / PER_ROW, col = p - key * PER_ROW;
-          const int t = min(tile0 + key / 16, c1 - 1);  // past the end: a valid tile, unused
-          const int64_t row = (int64_t)sm_blk[t - c0] * block_rows + head_rows + ((t * 16) % bs) + (key & 15);
-          rk[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) + row * RB + col * 16);
-          rv[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.vc) + row * RB + col * 16);
-        }
-      };
-      fetch(c0);
-      for (int t0s = c0; t0s < c1; t0s += kStageTiles) {
-        __syncthreads();  // every wave has finished reading the previous stage
-#pragma unroll
-        for (int i = 0; i < PIECES; ++i) {
-          const int p = threadIdx.x + i * NW * 64;
-          if (TOTAL < NW * 64 && p >= TOTAL) break;
-          const int key = p / PER_ROW, col = p - key * PER_ROW;
-          *reinterpret_cast<u32x4*>(sm_k + key * PITCH + col * 16) = rk[i];
-          *reinterpret_cast<u32x4*>(sm_v + key * PITCH + col * 16) = rv[i];
-        }
-        __syncthreads();
-        if (t0s + kStageTiles < c1) fetch(t0s + kStageTiles);  // in flight during the compute
-        auto load_masked = [&](T& tl, int j, bool in_range) {
-          const int t0 = (t0s + j) * 16;
-          tl.load_pitched(sm_k + j * 16 * PITCH, sm_v + j * 16 * PITCH, PITCH, lane);
-          if (!in_range || t0 + 16 > ctx) {  // V rows past the context may hold any bits
-            bool ok[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ok[i] = in_range && t0 + 4 * (lane >> 4) + i < ctx;
-            tl.mask_rows(ok);
+          for (int i = 0; i < PIECES; ++i) {
+            const int p = threadIdx.x + i * NW * 64;
+            if (TOTAL < NW * 64 && p >= TOTAL) break;  // fewer pieces than threads
+            const int key = p / PER_ROW, col = p - key * PER_ROW;
+            const int t = min(tile0 + key / 16, c1 - 1);  // past the end: a valid tile, unused
+            const int64_t row =
+                sm_row[t - c0] + (key & 15);
+            rk[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) + row * RB + col * 16);
+            rv[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.vc) + row * RB + col * 16);
           }
         };
-        if constexpr (CT == PKV_F32) {  // no K=32 f32 MFMA: one tile at a time
+        fetch(c0);
+        for (int t0s = c0; t0s < c1; t0s += kStageTiles) {
+          __syncthreads();  // every wave has finished reading the previous stage
+#pragma unroll
+          for (int i = 0; i < PIECES; ++i) {
+            const int p = threadIdx.x + i * NW * 64;
+            if (TOTAL < NW * 64 && p >= TOTAL) break;
+            const int key = p / PER_ROW, col = p - key * PER_ROW;
+            *reinterpret_cast<u32x4*>(sm_k + key * PITCH + col * 16) = rk[i];
+            *reinterpret_cast<u32x4*>(sm_v + key * PITCH + col * 16) = rv[i];
+          }
+          __syncthreads();
+          if (t0s + kStageTiles < c1) fetch(t0s + kStageTiles);  // in flight during the compute
 #pragma unroll
           for (int j = 0; j < kStageTiles; ++j) {
             const int tile = t0s + j;
             if (tile >= k_hi_w) break;  // wave-uniform
             const int t0 = tile * 16;
             T tl;
-            load_masked(tl, j, true);
-            const typename T::PV pv = tl.pack_v();
-            const bool causal = JOB == kPrefillJob && t0 + 15 > minpos_w;
+            tl.load_pitched(sm_k + j * 16 * PITCH, sm_v + j * 16 * PITCH, PITCH, lane);
+            if (t0 + 16 > ctx) {  // V rows past the context may hold any bits
+              bool ok[4];
 #pragma unroll
-            for (int rb = 0; rb < R; ++rb)
-              prefill_update<CT, D>(tl.scores(qf[rb]), pv, st[rb], t0, pos[rb], causal, a.qk_scale,
-                                    lane);
+              for (int i = 0; i < 4; ++i) ok[i] = t0 + 4 * (lane >> 4) + i < ctx;
+              tl.mask_rows(ok);
+            }
+            int lim[R];
+#pragma unroll
+            for (int rb = 0; rb < R; ++rb) lim[rb] = pos4[rb] - t0;
+            if (JOB == kPrefillJob && t0 + 15 > minpos_w)  // causal tile, wave-uniform
+              update_tile_f32<D, R, true>(tl, qf, st, lim, qs);
+            else
+              update_tile_f32<D, R, false>(tl, qf, st, lim, qs);
           }
-        } else {  // tile pairs on the double-rate MFMA
+        }
+      } else {
+        // Waves 0-3 stage V, waves 4-7 stage K.  V unit (pair pp, quad qd,
+        // 16-byte column col): keys 4qd..4qd+3 of both tiles of the pair at one
+        // column, so the thread holds the 8 keys of each 16-byte piece of the
+        // transposed image.  K: the stage's 16-byte pieces, 1 of every 256.
+        constexpr int E = 16 / EB;  // elements per 16-byte piece
+        constexpr int VUNITS = (kStageTiles / 2) * 4 * PER_ROW;
+        constexpr int KPIECES = kStageKeys * PER_ROW / 256;
+        static_assert(VUNITS <= 256 && KPIECES <= 8 && NW == 8, "staging split");
+        const bool v_stager = threadIdx.x < VUNITS;
+        const bool k_stager = threadIdx.x >= 256;
+        const int u = threadIdx.x, uk = threadIdx.x - 256;
+        const int col = u % PER_ROW, qd = (u / PER_ROW) & 3, pp = u / (4 * PER_ROW);
+        u32x4 pre[8];  // V: keys 4qd+i of tile a (i), then of tile b (4+i); K: pieces
+        int nva = 0, nvb = 0;  // V keys of tiles a, b inside the context and the range
+        auto pool_row = [&](int t) {  // pool row of the first key of tile t (< c1)
+          return sm_row[t - c0];
+        };
+        auto fetch = [&](int tile0) {
+          if (v_stager) {
 #pragma unroll
-          for (int j = 0; j < kStageTiles; j += 2) {
+            for (int h = 0; h < 2; ++h) {
+              const int t = tile0 + 2 * pp + h;
+              const int tc = min(t, c1 - 1);  // past the end: a valid tile, its V zeroed
+              const char* vp = static_cast<const char*>(a.vc) + (pool_row(tc) + 4 * qd) * RB + col * 16;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pre[4 * h + i] = *reinterpret_cast<const u32x4*>(vp + i * RB);
+              const int n = t < c1 ? min(4, max(0, ctx - (t * 16 + 4 * qd))) : 0;
+              (h ? nvb : nva) = n;
+            }
+          } else if (k_stager) {
+#pragma unroll
+            for (int i = 0; i < KPIECES; ++i) {
+              const int p = uk + 256 * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
+              const int tc = min(tile0 + key / 16, c1 - 1);
+              pre[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) +
+                                                       (pool_row(tc) + (key & 15)) * RB + kcol * 16);
+            }
+          }
+        };
+        // lane's K chunk offsets within a tile: row lane % 16, d = 32 c + 8 (lane / 16) + 0..7
+        int ko[D / 32];
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+          ko[c] = (lane & 15) * 2 * D + (((lane >> 4) + 4 * c) ^ k_swizzle<D>(lane & 15)) * 16;
+        fetch(c0);
+        for (int t0s = c0; t0s < c1; t0s += kStageTiles) {
+          __syncthreads();  // every wave has finished reading the previous stage
+          if (v_stager) {
+            // V of keys past the context or the range: zero, as its
+            // probabilities are, so that no stray bits reach the sums
+            if (nva < 4 || nvb < 4) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                pre[i] = i < nva ? pre[i] : u32x4{0, 0, 0, 0};
+                pre[4 + i] = i < nvb ? pre[4 + i] : u32x4{0, 0, 0, 0};
+              }
+            }
+            char* vd = sm_v + pp * vpair_bytes<D>() + 256 * qd;
+            if constexpr (CT == PKV_BF16) {
+#pragma unroll
+              for (int e = 0; e < E; ++e) {
+                const int d = E * col + e, m = d / VE, r = d % VE, w = e >> 1;
+                const uint32_t sel = (e & 1) ? kSelHi : kSelLo;
+                *reinterpret_cast<u32x4*>(vd + 1024 * r + 16 * m) =
+                    u32x4{__builtin_amdgcn_perm(pre[1][w], pre[0][w], sel),
+                          __builtin_amdgcn_perm(pre[3][w], pre[2][w], sel),
+                          __builtin_amdgcn_perm(pre[5][w], pre[4][w], sel),
+                          __builtin_amdgcn_perm(pre[7][w], pre[6][w], sel)};
+              }
+            } else {  // E4M3 codes -> bf16 (exact)
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                float f[8][4];  // f[i][b]: key i (4..7: tile b), element 4w + b
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                  const f32x2 x = fp8x2_lo(pre[i][w]), y = fp8x2_hi(pre[i][w]);
+                  f[i][0] = x[0];
+                  f[i][1] = x[1];
+                  f[i][2] = y[0];
+                  f[i][3] = y[1];
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                  const int d = E * col + 4 * w + b, m = d / VE, r = d % VE;
+                  *reinterpret_cast<u32x4*>(vd + 1024 * r + 16 * m) =
+                      u32x4{pack_exact(f[0][b], f[1][b]), pack_exact(f[2][b], f[3][b]),
+                            pack_exact(f[4][b], f[5][b]), pack_exact(f[6][b], f[7][b])};
+                }
+              }
+            }
+          } else if (k_stager) {
+            // K of keys past the context or the range: zero (finite), so that
+            // a score accumulator started at -inf stays -inf
+            if (t0s * 16 + kStageKeys > ctx || t0s + kStageTiles > c1) {  // workgroup-uniform
+#pragma unroll
+              for (int i = 0; i < KPIECES; ++i) {
+                const int key = (uk + 256 * i) / PER_ROW, t = t0s + key / 16;
+                if (t >= c1 || t * 16 + (key & 15) >= ctx) pre[i] = u32x4{0, 0, 0, 0};
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < KPIECES; ++i) {
+              const int p = uk + 256 * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
+              char* kd = sm_k + key * 2 * D;
+              const int sw = k_swizzle<D>(key);
+              if constexpr (CT == PKV_BF16) {
+                *reinterpret_cast<u32x4*>(kd + ((kcol ^ sw) * 16)) = pre[i];
+              } else {  // E4M3 codes -> bf16 (exact): chunks 2 kcol, 2 kcol + 1
+                uint32_t b[8];  // bf16 pairs of elements 2n, 2n+1
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                  const f32x2 x = fp8x2_lo(pre[i][w]), y = fp8x2_hi(pre[i][w]);
+                  b[2 * w] = pack_exact(x[0], x[1]);
+                  b[2 * w + 1] = pack_exact(y[0], y[1]);
+                }
+                *reinterpret_cast<u32x4*>(kd + (((2 * kcol) ^ sw) * 16)) = u32x4{b[0], b[1], b[2], b[3]};
+                *reinterpret_cast<u32x4*>(kd + (((2 * kcol + 1) ^ sw) * 16)) = u32x4{b[4], b[5], b[6], b[7]};
+              }
+            }
+          }
+          __syncthreads();
+          if (t0s + kStageTiles < c1) fetch(t0s + kStageTiles);  // in flight during the compute
+          constexpr int NT = kBlockTiles;
+#pragma unroll
+          for (int j = 0; j < kStageTiles; j += NT) {
             const int tile = t0s + j;
             if (tile >= k_hi_w) break;  // wave-uniform
-            const bool b_live = tile + 1 < k_hi_w;
             const int t0 = tile * 16;
-            T ta, tb;
-            load_masked(ta, j, true);
-            load_masked(tb, j + 1, b_live);
-            const typename T::PV2 pv = T::pack_v2(ta, tb);
-            const bool causal = JOB == kPrefillJob && t0 + 31 > minpos_w;
+            const char* kt = sm_k + j * 32 * D;
+            const char* vt = sm_v + (j >> 1) * vpair_bytes<D>() + (lane >> 4) * 256 + (lane & 15) * 16;
+            int lim[R];
 #pragma unroll
-            for (int rb = 0; rb < R; ++rb)
-              prefill_update2<CT, D>(ta.scores(qf[rb]), tb.scores(qf[rb]), pv, st[rb], t0, pos[rb],
-                                     causal, b_live, a.qk_scale, lane);
+            for (int rb = 0; rb < R; ++rb) lim[rb] = pos4[rb] - t0;
+            // wave-uniform: a block reaching past the first row's position, or
+            // with tiles past the wavefront's range, takes the masked update
+            const int live_tiles = k_hi_w - tile;
+            const bool masked = (JOB == kPrefillJob && t0 + 16 * NT - 1 > minpos_w) || live_tiles < NT;
+            update_block<D, R, NT>(kt, ko, qf, st, vt, masked, lim, live_tiles, qs);
           }
         }
       }
@@ -303,9 +649,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
     if (live) {
 #pragma unroll
       for (int rb = 0; rb < R; ++rb) {
-        float l_run = st[rb].l;
-        l_run += __shfl_xor(l_run, 16);
-        l_run += __shfl_xor(l_run, 32);
+        float l_run = st[rb].l[0];
+        if constexpr (F32) {  // lane shares -> column sum
+          l_run += __shfl_xor(l_run, 16);
+          l_run += __shfl_xor(l_run, 32);
+        }
         const int rr = row_w0 + 16 * rb + (lane & 15);
         if (rr >= rows) continue;
         const int t = rr / G, g = rr - t * G;
@@ -320,7 +668,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
             store_run<CT, VE>(a.out, orow * D + VE * (4 * (lane >> 4) + i), x);
           }
         } else {
-          const int64_t slot = a.slot0 + ((int64_t)t * a.num_kv_heads + hk) * a.splits + blockIdx.z;
+          const int64_t slot = a.slot0 + ((int64_t)t * a.num_kv_heads + hk) * a.splits + blockIdx.y;
           float* o = a.ws_acc + (slot * G + g) * D;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -339,9 +687,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
 template <int CT, int D>
 hipError_t launch_prefix_d(const PrefixArgs& a, hipStream_t stream) {
   constexpr int ROWS_G = 32 * kPrefillWaves;
-  int64_t gx = ((int64_t)a.num_seqs * a.group + ROWS_G - 1) / ROWS_G;
-  gx = gx < 1 ? 1 : gx > 65535 ? 65535 : gx;
-  const dim3 grid((unsigned)gx, (unsigned)a.num_kv_heads, (unsigned)a.splits);
+  int64_t gz = ((int64_t)a.num_seqs * a.group + ROWS_G - 1) / ROWS_G;
+  gz = gz < 1 ? 1 : gz > 65535 ? 65535 : gz;
+  const dim3 grid((unsigned)a.num_kv_heads, (unsigned)a.splits, (unsigned)gz);
   hipLaunchKernelGGL((rows_kernel<CT, D, 2, kPrefixJob, PrefixArgs>), grid, dim3(kPrefillWaves * 64), 0,
                      stream, a);
   return hipGetLastError();
@@ -357,10 +705,13 @@ hipError_t launch_prefix_ct(const PrefixArgs& a, hipStream_t stream) {
 template <int CT, int D, int R>
 hipError_t launch_r(const PrefillArgs& a, hipStream_t stream) {
   constexpr int ROWS_G = 16 * R * kPrefillWaves;
-  const int64_t rows = (int64_t)a.max_query_len * a.group;
-  int64_t gx = (rows + ROWS_G - 1) / ROWS_G;
-  gx = gx < 1 ? 1 : gx > 65535 ? 65535 : gx;
-  const dim3 grid((unsigned)gx, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+  // job slots for max_query_len-long chunks; any further jobs are taken by
+  // the same workgroups in later rounds
+  const int64_t per_seq = ((int64_t)a.max_query_len * a.group + ROWS_G - 1) / ROWS_G;
+  int64_t slots = (int64_t)a.num_seqs * (per_seq < 1 ? 1 : per_seq);
+  const int64_t cap = 0x7fffffff / a.num_kv_heads;
+  slots = slots > cap ? cap : slots;
+  const dim3 grid((unsigned)(slots * a.num_kv_heads));
   hipLaunchKernelGGL((rows_kernel<CT, D, R, kPrefillJob, PrefillArgs>), grid, dim3(kPrefillWaves * 64), 0,
                      stream, a);
   return hipGetLastError();
