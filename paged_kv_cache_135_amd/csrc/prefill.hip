@@ -150,8 +150,8 @@ __device__ __forceinline__ void update_tile_f32(const Tile<PKV_F32, D>& tl,
 // sums come from one more MFMA against an all-ones A operand, so every lane's
 // l[0] is its column's full sum of the rounded probabilities.
 // masked: tiles from `live` on and keys past lim[rb] (the column's position -
-// t0 - 4 * lane group) are dropped by starting their score accumulators at
-// -inf; the staging zeroes K and V past the context, so the sums stay -inf.
+// t0 - 4 * lane group) are dropped (score -inf); the staging zeroes V past
+// the context, so no stray bits reach the sums.
 template <int D, int R, int NT>
 __device__ __forceinline__ void update_block(const char* kt, const int (&ko)[D / 32],
                                              const typename Tile<PKV_BF16, D>::QFrag (&qf)[R],
@@ -162,10 +162,7 @@ __device__ __forceinline__ void update_block(const char* kt, const int (&ko)[D /
 #pragma unroll
   for (int rb = 0; rb < R; ++rb)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sc[rb][t][i] = !masked || (t < live && 16 * t + i <= lim[rb]) ? 0.f : kNegInf;
+    for (int t = 0; t < NT; ++t) sc[rb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {  // 32 d at a time, every tile and row block
 #pragma unroll
@@ -174,6 +171,15 @@ __device__ __forceinline__ void update_block(const char* kt, const int (&ko)[D /
 #pragma unroll
       for (int rb = 0; rb < R; ++rb) sc[rb][t] = mfma_bf16_k32(k, qf[rb].q[c], sc[rb][t]);
     }
+  }
+  if (masked) {  // wave-uniform and rare: a real branch, not selects on every block
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!(t < live && 16 * t + i <= lim[rb])) sc[rb][t][i] = kNegInf;
   }
   u32x4 pk[R][NT / 2];
 #pragma unroll
@@ -356,8 +362,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
   const float qs = q_zero ? 1.f : fabsf(qs_in);
 
   __shared__ int64_t sm_row[kPrefillChunkTiles];  // pool row of each tile's first key
-  constexpr int K_BYTES = kStageKeys * (F32 ? f32_pitch<D>() : 2 * D);
-  constexpr int V_BYTES = F32 ? kStageKeys * f32_pitch<D>() : (kStageTiles / 2) * vpair_bytes<D>();
+  // bf16 images: two stage buffers, one computed while the next is written
+  constexpr int K_STAGE = 16 * kBlockTiles * 2 * D, V_STAGE = (kBlockTiles / 2) * vpair_bytes<D>();
+  constexpr int K_BYTES = F32 ? kStageKeys * f32_pitch<D>() : 2 * K_STAGE;
+  constexpr int V_BYTES = F32 ? kStageKeys * f32_pitch<D>() : 2 * V_STAGE;
   __shared__ __attribute__((aligned(16))) char sm_k[K_BYTES];
   __shared__ __attribute__((aligned(16))) char sm_v[V_BYTES];
   static_assert(K_BYTES >= 4 * (kRankBuckets + 16), "ranking scratch");
@@ -503,42 +511,52 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
           }
         }
       } else {
-        // Waves 0-3 stage V, waves 4-7 stage K.  V unit (pair pp, quad qd,
-        // 16-byte column col): keys 4qd..4qd+3 of both tiles of the pair at one
-        // column, so the thread holds the 8 keys of each 16-byte piece of the
-        // transposed image.  K: the stage's 16-byte pieces, 1 of every 256.
-        constexpr int E = 16 / EB;  // elements per 16-byte piece
-        constexpr int VUNITS = (kStageTiles / 2) * 4 * PER_ROW;
-        constexpr int KPIECES = kStageKeys * PER_ROW / 256;
-        static_assert(VUNITS <= 256 && KPIECES <= 8 && NW == 8, "staging split");
+        // Stages of one softmax block (kBlockTiles tiles).  Waves 0-3 stage V,
+        // waves 4-7 stage K.  V unit (pair pp, quad qd, 8-byte half column
+        // hcol): keys 4qd..4qd+3 of both tiles of the pair at those 8 bytes,
+        // so the thread holds the 8 keys of every 16-byte piece of the
+        // transposed image it writes; lanes are ordered so that 16 of them
+        // write 256 contiguous bytes.  K: the stage's 16-byte pieces.
+        constexpr int NT = kBlockTiles;
+        constexpr int SK = 16 * NT;       // keys per stage
+        constexpr int HPR = RB / 8;       // 8-byte half columns per key row
+        constexpr int EH = 8 / EB;        // elements per half column
+        constexpr int SUBS = VE > EH ? VE / EH : 1;  // half columns per MFMA row m
+        constexpr int VUNITS = (NT / 2) * 4 * HPR;
+        constexpr int KPIECES = SK * PER_ROW / 256;
+        static_assert(VUNITS <= 256 && KPIECES >= 1 && KPIECES <= 4 && NW == 8, "staging split");
+        static_assert(SUBS == 1 || (SUBS == 2 && HPR == 32), "half-column order");
         const bool v_stager = threadIdx.x < VUNITS;
         const bool k_stager = threadIdx.x >= 256;
         const int u = threadIdx.x, uk = threadIdx.x - 256;
-        const int col = u % PER_ROW, qd = (u / PER_ROW) & 3, pp = u / (4 * PER_ROW);
-        u32x4 pre[8];  // V: keys 4qd+i of tile a (i), then of tile b (4+i); K: pieces
+        const int hcol = SUBS == 2 ? 2 * (u & 15) + ((u >> 4) & 1) : u % HPR;
+        const int vrest = SUBS == 2 ? u >> 5 : u / HPR;
+        const int qd = vrest & 3, pp = vrest >> 2;
+        // V: pre[i] = key 4qd+i of tile a (dwords 0-1) and of tile b (dwords 2-3);
+        // K: pre[i] = piece i
+        u32x4 pre[4];
         int nva = 0, nvb = 0;  // V keys of tiles a, b inside the context and the range
-        auto pool_row = [&](int t) {  // pool row of the first key of tile t (< c1)
-          return sm_row[t - c0];
-        };
         auto fetch = [&](int tile0) {
           if (v_stager) {
+            const int ta = tile0 + 2 * pp, tb = ta + 1;
+            // past the end: a valid tile, its V zeroed
+            const char* va = static_cast<const char*>(a.vc) + (sm_row[min(ta, c1 - 1) - c0] + 4 * qd) * RB + hcol * 8;
+            const char* vb = static_cast<const char*>(a.vc) + (sm_row[min(tb, c1 - 1) - c0] + 4 * qd) * RB + hcol * 8;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int t = tile0 + 2 * pp + h;
-              const int tc = min(t, c1 - 1);  // past the end: a valid tile, its V zeroed
-              const char* vp = static_cast<const char*>(a.vc) + (pool_row(tc) + 4 * qd) * RB + col * 16;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) pre[4 * h + i] = *reinterpret_cast<const u32x4*>(vp + i * RB);
-              const int n = t < c1 ? min(4, max(0, ctx - (t * 16 + 4 * qd))) : 0;
-              (h ? nvb : nva) = n;
+            for (int i = 0; i < 4; ++i) {
+              const u32x2 x = *reinterpret_cast<const u32x2*>(va + i * RB);
+              const u32x2 y = *reinterpret_cast<const u32x2*>(vb + i * RB);
+              pre[i] = u32x4{x[0], x[1], y[0], y[1]};
             }
+            nva = ta < c1 ? min(4, max(0, ctx - (ta * 16 + 4 * qd))) : 0;
+            nvb = tb < c1 ? min(4, max(0, ctx - (tb * 16 + 4 * qd))) : 0;
           } else if (k_stager) {
 #pragma unroll
             for (int i = 0; i < KPIECES; ++i) {
               const int p = uk + 256 * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
               const int tc = min(tile0 + key / 16, c1 - 1);
               pre[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) +
-                                                       (pool_row(tc) + (key & 15)) * RB + kcol * 16);
+                                                       (sm_row[tc - c0] + (key & 15)) * RB + kcol * 16);
             }
           }
         };
@@ -547,46 +565,48 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
           ko[c] = (lane & 15) * 2 * D + (((lane >> 4) + 4 * c) ^ k_swizzle<D>(lane & 15)) * 16;
-        fetch(c0);
-        for (int t0s = c0; t0s < c1; t0s += kStageTiles) {
-          __syncthreads();  // every wave has finished reading the previous stage
+        // the fetched stage (tiles t0s .. t0s + NT - 1) into the buffers kd0 / vd0
+        auto stage_write = [&](int t0s, char* kd0, char* vd0) {
           if (v_stager) {
             // V of keys past the context or the range: zero, as its
             // probabilities are, so that no stray bits reach the sums
             if (nva < 4 || nvb < 4) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                pre[i] = i < nva ? pre[i] : u32x4{0, 0, 0, 0};
-                pre[4 + i] = i < nvb ? pre[4 + i] : u32x4{0, 0, 0, 0};
-              }
+              for (int i = 0; i < 4; ++i)
+                pre[i] = u32x4{i < nva ? pre[i][0] : 0u, i < nva ? pre[i][1] : 0u, i < nvb ? pre[i][2] : 0u,
+                               i < nvb ? pre[i][3] : 0u};
             }
-            char* vd = sm_v + pp * vpair_bytes<D>() + 256 * qd;
+            char* vd = vd0 + pp * vpair_bytes<D>() + 256 * qd;
             if constexpr (CT == PKV_BF16) {
 #pragma unroll
-              for (int e = 0; e < E; ++e) {
-                const int d = E * col + e, m = d / VE, r = d % VE, w = e >> 1;
+              for (int e = 0; e < EH; ++e) {
+                const int d = EH * hcol + e, m = d / VE, r = d % VE, w = e >> 1;
                 const uint32_t sel = (e & 1) ? kSelHi : kSelLo;
                 *reinterpret_cast<u32x4*>(vd + 1024 * r + 16 * m) =
                     u32x4{__builtin_amdgcn_perm(pre[1][w], pre[0][w], sel),
                           __builtin_amdgcn_perm(pre[3][w], pre[2][w], sel),
-                          __builtin_amdgcn_perm(pre[5][w], pre[4][w], sel),
-                          __builtin_amdgcn_perm(pre[7][w], pre[6][w], sel)};
+                          __builtin_amdgcn_perm(pre[1][2 + w], pre[0][2 + w], sel),
+                          __builtin_amdgcn_perm(pre[3][2 + w], pre[2][2 + w], sel)};
               }
             } else {  // E4M3 codes -> bf16 (exact)
 #pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                float f[8][4];  // f[i][b]: key i (4..7: tile b), element 4w + b
+              for (int w = 0; w < 2; ++w) {
+                float f[8][4];  // f[i][b]: key i of tile a (i < 4) or b, element 4w + b
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                  const f32x2 x = fp8x2_lo(pre[i][w]), y = fp8x2_hi(pre[i][w]);
-                  f[i][0] = x[0];
-                  f[i][1] = x[1];
-                  f[i][2] = y[0];
-                  f[i][3] = y[1];
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                  for (int h = 0; h < 2; ++h) {
+                    const uint32_t word = pre[i][2 * h + w];
+                    const f32x2 x = fp8x2_lo(word), y = fp8x2_hi(word);
+                    f[4 * h + i][0] = x[0];
+                    f[4 * h + i][1] = x[1];
+                    f[4 * h + i][2] = y[0];
+                    f[4 * h + i][3] = y[1];
+                  }
                 }
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                  const int d = E * col + 4 * w + b, m = d / VE, r = d % VE;
+                  const int d = EH * hcol + 4 * w + b, m = d / VE, r = d % VE;
                   *reinterpret_cast<u32x4*>(vd + 1024 * r + 16 * m) =
                       u32x4{pack_exact(f[0][b], f[1][b]), pack_exact(f[2][b], f[3][b]),
                             pack_exact(f[4][b], f[5][b]), pack_exact(f[6][b], f[7][b])};
@@ -596,7 +616,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
           } else if (k_stager) {
             // K of keys past the context or the range: zero (finite), so that
             // a score accumulator started at -inf stays -inf
-            if (t0s * 16 + kStageKeys > ctx || t0s + kStageTiles > c1) {  // workgroup-uniform
+            if (t0s * 16 + SK > ctx || t0s + NT > c1) {  // workgroup-uniform
 #pragma unroll
               for (int i = 0; i < KPIECES; ++i) {
                 const int key = (uk + 256 * i) / PER_ROW, t = t0s + key / 16;
@@ -606,7 +626,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
 #pragma unroll
             for (int i = 0; i < KPIECES; ++i) {
               const int p = uk + 256 * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
-              char* kd = sm_k + key * 2 * D;
+              char* kd = kd0 + key * 2 * D;
               const int sw = k_swizzle<D>(key);
               if constexpr (CT == PKV_BF16) {
                 *reinterpret_cast<u32x4*>(kd + ((kcol ^ sw) * 16)) = pre[i];
@@ -623,25 +643,31 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
               }
             }
           }
-          __syncthreads();
-          if (t0s + kStageTiles < c1) fetch(t0s + kStageTiles);  // in flight during the compute
-          constexpr int NT = kBlockTiles;
-#pragma unroll
-          for (int j = 0; j < kStageTiles; j += NT) {
-            const int tile = t0s + j;
-            if (tile >= k_hi_w) break;  // wave-uniform
-            const int t0 = tile * 16;
-            const char* kt = sm_k + j * 32 * D;
-            const char* vt = sm_v + (j >> 1) * vpair_bytes<D>() + (lane >> 4) * 256 + (lane & 15) * 16;
+        };
+        // stage n sits in buffer n % 2; the write of stage n + 1 and the loads
+        // of stage n + 2 overlap the compute of stage n, one barrier per stage
+        fetch(c0);
+        stage_write(c0, sm_k, sm_v);
+        if (c0 + NT < c1) fetch(c0 + NT);
+        __syncthreads();
+        for (int t0s = c0, cur = 0; t0s < c1; t0s += NT, cur ^= 1) {
+          if (t0s + NT < c1) {
+            stage_write(t0s + NT, sm_k + (cur ^ 1) * K_STAGE, sm_v + (cur ^ 1) * V_STAGE);
+            if (t0s + 2 * NT < c1) fetch(t0s + 2 * NT);  // in flight during the compute
+          }
+          if (t0s < k_hi_w) {  // wave-uniform
+            const int t0 = t0s * 16;
+            const char* vt = sm_v + cur * V_STAGE + (lane >> 4) * 256 + (lane & 15) * 16;
             int lim[R];
 #pragma unroll
             for (int rb = 0; rb < R; ++rb) lim[rb] = pos4[rb] - t0;
-            // wave-uniform: a block reaching past the first row's position, or
-            // with tiles past the wavefront's range, takes the masked update
-            const int live_tiles = k_hi_w - tile;
-            const bool masked = (JOB == kPrefillJob && t0 + 16 * NT - 1 > minpos_w) || live_tiles < NT;
-            update_block<D, R, NT>(kt, ko, qf, st, vt, masked, lim, live_tiles, qs);
+            // a block reaching past the first row's position, or with tiles
+            // past the wavefront's range, is masked
+            const int live_tiles = k_hi_w - t0s;
+            const bool masked = (JOB == kPrefillJob && t0 + SK - 1 > minpos_w) || live_tiles < NT;
+            update_block<D, R, NT>(sm_k + cur * K_STAGE, ko, qf, st, vt, masked, lim, live_tiles, qs);
           }
+          __syncthreads();  // stage n read and stage n + 1 written by every wave
         }
       }
     }
