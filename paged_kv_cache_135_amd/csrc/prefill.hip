@@ -341,7 +341,7 @@ enum RowsJob : int { kPrefillJob = 0, kPrefixJob = 1 };
 // The next stage's global loads are issued before the current stage is
 // computed, so they are in flight meanwhile.
 template <int CT, int D, int R, int JOB, typename Args>
-__global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
+__global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_kernel(Args a) {
   constexpr bool F32 = CT == PKV_F32;
   using T = Tile<F32 ? PKV_F32 : PKV_BF16, D>;  // fragments read from LDS
   constexpr int VE = D / 16;
@@ -511,8 +511,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
           }
         }
       } else {
-        // Stages of one softmax block (kBlockTiles tiles).  Waves 0-3 stage V,
-        // waves 4-7 stage K.  V unit (pair pp, quad qd, 8-byte half column
+        // Stages of one softmax block (kBlockTiles tiles).  The first half of
+        // the wavefronts stages V, the second half K.  V unit (pair pp, quad qd, 8-byte half column
         // hcol): keys 4qd..4qd+3 of both tiles of the pair at those 8 bytes,
         // so the thread holds the 8 keys of every 16-byte piece of the
         // transposed image it writes; lanes are ordered so that 16 of them
@@ -522,13 +522,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
         constexpr int HPR = RB / 8;       // 8-byte half columns per key row
         constexpr int EH = 8 / EB;        // elements per half column
         constexpr int SUBS = VE > EH ? VE / EH : 1;  // half columns per MFMA row m
+        constexpr int HALF = NW * 32;  // threads per staging role
         constexpr int VUNITS = (NT / 2) * 4 * HPR;
-        constexpr int KPIECES = SK * PER_ROW / 256;
-        static_assert(VUNITS <= 256 && KPIECES >= 1 && KPIECES <= 4 && NW == 8, "staging split");
+        constexpr int KTOTAL = SK * PER_ROW;  // 16-byte K pieces per stage
+        constexpr int KPIECES = (KTOTAL + HALF - 1) / HALF;
+        static_assert(VUNITS <= HALF && KPIECES <= 4 && (KTOTAL % HALF == 0 || KTOTAL < HALF), "staging split");
         static_assert(SUBS == 1 || (SUBS == 2 && HPR == 32), "half-column order");
         const bool v_stager = threadIdx.x < VUNITS;
-        const bool k_stager = threadIdx.x >= 256;
-        const int u = threadIdx.x, uk = threadIdx.x - 256;
+        const bool k_stager = threadIdx.x >= HALF;
+        const int u = threadIdx.x, uk = threadIdx.x - HALF;
         const int hcol = SUBS == 2 ? 2 * (u & 15) + ((u >> 4) & 1) : u % HPR;
         const int vrest = SUBS == 2 ? u >> 5 : u / HPR;
         const int qd = vrest & 3, pp = vrest >> 2;
@@ -553,7 +555,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
           } else if (k_stager) {
 #pragma unroll
             for (int i = 0; i < KPIECES; ++i) {
-              const int p = uk + 256 * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
+              const int p = uk + HALF * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
+              if (KTOTAL < HALF && p >= KTOTAL) break;  // fewer pieces than threads
               const int tc = min(tile0 + key / 16, c1 - 1);
               pre[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) +
                                                        (sm_row[tc - c0] + (key & 15)) * RB + kcol * 16);
@@ -619,13 +622,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void rows_kernel(Args a) {
             if (t0s * 16 + SK > ctx || t0s + NT > c1) {  // workgroup-uniform
 #pragma unroll
               for (int i = 0; i < KPIECES; ++i) {
-                const int key = (uk + 256 * i) / PER_ROW, t = t0s + key / 16;
+                if (KTOTAL < HALF && uk + HALF * i >= KTOTAL) break;
+                const int key = (uk + HALF * i) / PER_ROW, t = t0s + key / 16;
                 if (t >= c1 || t * 16 + (key & 15) >= ctx) pre[i] = u32x4{0, 0, 0, 0};
               }
             }
 #pragma unroll
             for (int i = 0; i < KPIECES; ++i) {
-              const int p = uk + 256 * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
+              const int p = uk + HALF * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
+              if (KTOTAL < HALF && p >= KTOTAL) break;
               char* kd = kd0 + key * 2 * D;
               const int sw = k_swizzle<D>(key);
               if constexpr (CT == PKV_BF16) {
