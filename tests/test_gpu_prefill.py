@@ -159,3 +159,34 @@ def test_largest_block_size_and_long_chunk():
     ref = _oracle(case, case.key_cache, case.value_cache)
     for rpw in (16, 32):
         gu.assert_close(gu.host(_run(g, case, qs, rpw)), ref, "bf16", f"bs 256 rows/wave {rpw}")
+
+
+def test_many_short_sequences():
+    """600 sequences (more than a workgroup has threads, so each thread of the
+    job ranking walks several sequences), zero-length chunks among them."""
+    rng = np.random.default_rng(71)
+    pre = [int(x) for x in rng.integers(0, 200, 600)]
+    chk = [int(x) for x in rng.integers(0, 13, 600)]
+    case = workloads.build_prefill_case("many", seed=71, prefix_lens=pre, chunk_lens=chk,
+                                        num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                        block_size=16, cache_dtype="bf16", std=0.5,
+                                        scale=1.0 / math.sqrt(64))
+    g = gu.GpuCase(case)
+    qs = gu.dev(case.query_start)
+    ref = _oracle(case, case.key_cache, case.value_cache)
+    gu.assert_close(gu.host(_run(g, case, qs)), ref, "bf16", "600 sequences")
+
+
+@pytest.mark.parametrize("scale", [-0.9 / math.sqrt(128), 0.0])
+def test_negative_and_zero_scale(scale):
+    """The kernel folds a positive factor into the exponent: a negative scale
+    flips q's sign bits, a zero scale averages the visible V rows."""
+    case = workloads.build_prefill_case("scale", seed=5, prefix_lens=[90, 0, 33],
+                                        chunk_lens=[40, 70, 1], num_q_heads=16,
+                                        num_kv_heads=4, head_dim=128, block_size=16,
+                                        cache_dtype="bf16", std=0.5, scale=scale)
+    g = gu.GpuCase(case)
+    qs = gu.dev(case.query_start)
+    ref = _oracle(case, case.key_cache, case.value_cache)
+    for rpw in (16, 32):
+        gu.assert_close(gu.host(_run(g, case, qs, rpw)), ref, "bf16", f"scale {scale} rows/wave {rpw}")
