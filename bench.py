@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    p.add_argument("--kv-hint", default="auto", choices=["auto", "stream", "cached"],
+                   help="pool reads: stream (PKV_DECODE_STREAM_KV, for batches whose tables share "
+                        "no block), cached, or auto = stream exactly when the tables share none")
     p.add_argument("--step", default="auto", choices=["auto", "append", "split"],
                    help="append: one call per step; split: KV write then decode; auto: append "
                         "when the step writes one token per sequence at position len-1")
@@ -440,9 +443,14 @@ def main():
             except pkv.PagedKVError:
                 pass
     append = step == "append"
+    # the streaming hint is for calls that read every block once: decided from
+    # the tables (past the shared prefix when it is computed apart)
+    shared = pkv.tables_share_blocks(case.block_tables, case.context_lens, case.block_size,
+                                     skip_blocks=prefix_len // case.block_size)
+    stream_kv = args.kv_hint == "stream" or (args.kv_hint == "auto" and not shared)
     dkw = dict(k_scale=case.k_scale, v_scale=case.v_scale, mode=args.mode,
                partition_size=args.partition, waves_per_group=args.waves,
-               num_workers=args.workers, workspace=ws)
+               num_workers=args.workers, workspace=ws, stream_kv=stream_kv)
 
     if prefix_len:
         dkw["mode"] = "auto"
@@ -581,6 +589,8 @@ def main():
             "graph": bool(args.graph),
             "step": step,
             "shared_prefix_tokens": prefix_len or None,
+            "tables_share_blocks": bool(shared),
+            "kv_stream_hint": bool(stream_kv),
         },
         "kv_bytes_per_step": kv,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

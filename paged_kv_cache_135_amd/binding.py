@@ -29,8 +29,9 @@ EXPORTED = (
     "pkv_validate_block_ids", "paged_attention_decode_shared_prefix",
     "paged_attention_decode_shared_prefix_workspace_bytes", "pkv_validate_shared_prefix",
 )
-ABI_VERSION = 5
+ABI_VERSION = 6
 DECODE_DEFER_MERGE = 1
+DECODE_STREAM_KV = 2
 
 
 class PagedKVError(RuntimeError):
@@ -70,8 +71,13 @@ DECODE_MODES = {"single": 0, "partitioned": 1, "balanced": 2, "auto": 3}
 
 
 def decode_opts(mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
-                num_workers: int = 0, defer_merge: bool = False) -> PkvDecodeOpts:
-    """Options struct; mode None means "partitioned" if partition_size > 0, else "auto"."""
+                num_workers: int = 0, defer_merge: bool = False,
+                stream_kv: bool = False) -> PkvDecodeOpts:
+    """Options struct; mode None means "partitioned" if partition_size > 0, else "auto".
+
+    stream_kv: the batch shares no block between sequences (every refcount 1,
+    see BlockPool.shares_blocks), so the pool reads may stream past the caches
+    (PKV_DECODE_STREAM_KV); results are bit-identical either way."""
     if mode is None:
         mode = "partitioned" if partition_size > 0 else "auto"
     o = PkvDecodeOpts()
@@ -79,7 +85,7 @@ def decode_opts(mode: str | None = None, partition_size: int = 0, waves_per_grou
     o.partition_size = int(partition_size)
     o.waves_per_group = int(waves_per_group)
     o.num_workers = int(num_workers)
-    o.flags = DECODE_DEFER_MERGE if defer_merge else 0
+    o.flags = (DECODE_DEFER_MERGE if defer_merge else 0) | (DECODE_STREAM_KV if stream_kv else 0)
     return o
 
 
@@ -246,15 +252,16 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
                            scale: float, block_size: int, *, k_scale: float = 1.0,
                            v_scale: float = 1.0, mode: str | None = None, partition_size: int = 0,
                            waves_per_group: int = 0, num_workers: int = 0, workspace=None,
-                           stream=None):
+                           stream_kv: bool = False, stream=None):
     """Decode attention over the paged pools into ``out`` [S, Hq, D].
 
     mode: "single", "partitioned" (needs partition_size), "balanced" or "auto";
     None picks "partitioned" when partition_size > 0, else "auto".  The split
     modes need a workspace (a uint8 device tensor of at least
-    decode_workspace_bytes(...)); it is allocated here when not given."""
+    decode_workspace_bytes(...)); it is allocated here when not given.
+    stream_kv: see decode_opts."""
     _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
-    opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
+    opts = decode_opts(mode, partition_size, waves_per_group, num_workers, stream_kv=stream_kv)
     ws = _workspace_for(opts, q, key_cache, block_tables, block_size, workspace)
     dout, dq = describe(out), describe(q)
     dkc, dvc = describe(key_cache, k_scale), describe(value_cache, v_scale)
@@ -273,13 +280,13 @@ def paged_attention_decode_append(out, q, k, v, slot_mapping, key_cache, value_c
                                   k_scale: float = 1.0, v_scale: float = 1.0,
                                   mode: str | None = None, partition_size: int = 0,
                                   waves_per_group: int = 0, num_workers: int = 0, workspace=None,
-                                  stream=None):
+                                  stream_kv: bool = False, stream=None):
     """One decode step in one call: write each sequence's new token (k, v
     [S, Hkv, D] at slot_mapping [S]) and attend (see include/pagedkv.h).
     Equal to paged_kv_write followed by paged_attention_decode when every
     slot is position context_lens[s]-1 of its own sequence."""
     _same_device(out, q, k, v, slot_mapping, key_cache, value_cache, block_tables, context_lens)
-    opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
+    opts = decode_opts(mode, partition_size, waves_per_group, num_workers, stream_kv=stream_kv)
     ws = _workspace_for(opts, q, key_cache, block_tables, block_size, workspace)
     d = [describe(out), describe(q), describe(k), describe(v), describe(slot_mapping),
          describe(key_cache, k_scale), describe(value_cache, v_scale), describe(block_tables),
@@ -314,12 +321,13 @@ def paged_attention_decode_shared_prefix(out, q, key_cache, value_cache, block_t
                                          context_lens, prefix_len: int, scale: float,
                                          block_size: int, *, k_scale: float = 1.0,
                                          v_scale: float = 1.0, num_workers: int = 0,
-                                         workspace=None, stream=None):
+                                         workspace=None, stream_kv: bool = False, stream=None):
     """Decode for sequences whose first ``prefix_len`` tokens are the same shared
     blocks: the prefix part once for all sequences, the tails through the
-    balanced split, merged (see include/pagedkv.h)."""
+    balanced split, merged (see include/pagedkv.h).  stream_kv (see
+    decode_opts) applies to the tails' reads: the tails must share no block."""
     _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
-    opts = decode_opts("auto", 0, 0, num_workers)
+    opts = decode_opts("auto", 0, 0, num_workers, stream_kv=stream_kv)
     ws = _workspace_for(opts, q, key_cache, block_tables, block_size, workspace, prefix_len)
     d = [describe(out), describe(q), describe(key_cache, k_scale), describe(value_cache, v_scale),
          describe(block_tables), describe(context_lens)]
@@ -329,6 +337,18 @@ def paged_attention_decode_shared_prefix(out, q, key_cache, value_cache, block_t
     if ws is not None and workspace is None and stream is not None:
         ws.record_stream(stream)
     return out
+
+
+def tables_share_blocks(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
+                        skip_blocks: int = 0) -> bool:
+    """True if a physical block is listed by two of the sequences (host tables),
+    counting each sequence's blocks from column skip_blocks up to its length.
+    False means a decode reads every block once and may pass stream_kv=True."""
+    t = np.asarray(block_tables)
+    n = -(-np.asarray(context_lens, dtype=np.int64) // int(block_size))
+    ids = np.concatenate([t[s, skip_blocks:max(skip_blocks, int(n[s]))] for s in range(t.shape[0])]
+                         + [np.zeros(0, t.dtype)])
+    return np.unique(ids).size != ids.size
 
 
 def validate_shared_prefix(block_tables: np.ndarray, context_lens: np.ndarray, num_blocks: int,
@@ -535,19 +555,21 @@ class DecodeLaunch:
 
     append=(k, v, slot_mapping) makes it the one-call decode step
     (paged_attention_decode_append).  defer_merge=True launches only the
-    streaming kernel; call merge() next on the same stream."""
+    streaming kernel; call merge() next on the same stream.  stream_kv: see
+    decode_opts."""
 
     def __init__(self, out, q, key_cache, value_cache, block_tables, context_lens, scale: float,
                  block_size: int, *, k_scale: float = 1.0, v_scale: float = 1.0,
                  mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
                  num_workers: int = 0, workspace=None, append=None, defer_merge: bool = False,
-                 prefix_len: int = 0):
+                 prefix_len: int = 0, stream_kv: bool = False):
         _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
         if prefix_len and (append is not None or defer_merge):
             raise ValueError("a shared-prefix decode takes no appended tokens and no deferred merge")
         if prefix_len and mode is None:
             mode = "auto"
-        self._opts = decode_opts(mode, partition_size, waves_per_group, num_workers, defer_merge)
+        self._opts = decode_opts(mode, partition_size, waves_per_group, num_workers, defer_merge,
+                                 stream_kv)
         self._merge_opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
         self.workspace = _workspace_for(self._opts, q, key_cache, block_tables, block_size,
                                         workspace, prefix_len)

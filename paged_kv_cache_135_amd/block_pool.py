@@ -118,6 +118,14 @@ class BlockPool:
     def num_tokens(self, seq) -> int:
         return self._seqs[seq].num_tokens
 
+    def shares_blocks(self, seqs) -> bool:
+        """True if some physical block sits in the tables of two of these
+        sequences (a prefix or a fork).  A decode over them then reads that
+        block more than once and should keep it cached; otherwise every block
+        is read once and the call may stream the pool (stream_kv=True)."""
+        ids = [b for s in seqs for b in self._seqs[s].table]
+        return len(ids) != len(set(ids))
+
     def blocks_needed(self, n_tokens: int) -> int:
         return -(-int(n_tokens) // self.block_size)
 

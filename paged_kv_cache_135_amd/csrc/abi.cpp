@@ -624,6 +624,8 @@ pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
     return fail(PKV_ERR_SHAPE, "prefix_len %d: must be a multiple of block_size in [0, %lld]",
                 prefix_len, (long long)(maxb * bs));
 
+  if (opts && (opts->flags & ~(PKV_DECODE_DEFER_MERGE | PKV_DECODE_STREAM_KV)) != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "opts->flags 0x%x: unknown PKV_DECODE_* bits", (unsigned)opts->flags);
   Plan p;
   PKV_TRY(plan(opts, S, Hq, Hkv, maxb, bs, &p, prefix_len));
   pkv::DecodeArgs a{};
@@ -670,6 +672,7 @@ pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
   a.qk_scale = (float)((double)scale * log2e * kscale);
   a.v_scale = ct == PKV_FP8_E4M3 ? value_cache->scale : 1.0f;
   a.phase = phase;
+  a.stream_kv = opts && (opts->flags & PKV_DECODE_STREAM_KV) ? 1 : 0;
   if (app) {
     a.append = 1;
     a.kn = app->k->data;

@@ -133,7 +133,7 @@ __device__ __forceinline__ void process_tile(Tile<CT, D>& t, const typename Tile
   st.m = m_new;
 }
 
-template <int CT, int D, int NW, int NBUF, bool APPEND>
+template <int CT, int D, int NW, int NBUF, bool APPEND, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a) {
   using T = Tile<CT, D>;
   constexpr int VE = T::VE;
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
         const int64_t row = (int64_t)blk * block_rows + head_rows + ((t * 16) % bs);
         const int rsub = owns_last && k + j < n_my && t == ntiles - 1 &&
                                  (int64_t)blk * bs + off_new == slot_new ? r_new : -1;
-        buf[j].load_sub(a.kc, a.vc, row, lane, rsub, kn, vn, a.inv_k, a.inv_v);
+        buf[j].template load_sub<NT>(a.kc, a.vc, row, lane, rsub, kn, vn, a.inv_k, a.inv_v);
       }
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
@@ -355,7 +355,7 @@ __device__ void write_zero_rows(const DecodeArgs& a, int s, int lane) {
   for (int i = lane; i < n16; i += 64) reinterpret_cast<u32x4*>(o)[i] = u32x4{0, 0, 0, 0};
 }
 
-template <int CT, int D, int NBUF, bool APPEND>
+template <int CT, int D, int NBUF, bool APPEND, bool NT>
 __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3) void decode_balanced_kernel(DecodeArgs a) {
   using T = Tile<CT, D>;
   constexpr int VE = T::VE;
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
         const int64_t row = (int64_t)blk * block_rows + head_rows + ((t * 16) % bs);
         const int rsub =
             slot_new >= 0 && k + j == n - 1 && (int64_t)blk * bs + off_new == slot_new ? r_new : -1;
-        buf[j].load_sub(a.kc, a.vc, row, lane, rsub, kn, vn, a.inv_k, a.inv_v);
+        buf[j].template load_sub<NT>(a.kc, a.vc, row, lane, rsub, kn, vn, a.inv_k, a.inv_v);
       }
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
@@ -669,12 +669,16 @@ template <int CT, int D, int NW>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
   if (a.phase != kMergePhase) {
     const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    if (a.append)
-      hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, ring_depth<CT, D>(), true>), grid,
-                         dim3(NW * 64), 0, stream, a);
+    constexpr int B = ring_depth<CT, D>();
+    const dim3 block(NW * 64);
+    if (a.append && a.stream_kv)
+      hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, B, true, true>), grid, block, 0, stream, a);
+    else if (a.append)
+      hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, B, true, false>), grid, block, 0, stream, a);
+    else if (a.stream_kv)
+      hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, B, false, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, ring_depth<CT, D>(), false>), grid,
-                         dim3(NW * 64), 0, stream, a);
+      hipLaunchKernelGGL((decode_partition_kernel<CT, D, NW, B, false, false>), grid, block, 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -688,12 +692,15 @@ template <int CT, int D>
 hipError_t launch_balanced(const DecodeArgs& a, hipStream_t stream) {
   if (a.phase != kMergePhase) {
     const dim3 grid((unsigned)((a.num_workers + 3) / 4));
-    if (a.append)
-      hipLaunchKernelGGL((decode_balanced_kernel<CT, D, ring_depth<CT, D>(), true>), grid,
-                         dim3(256), 0, stream, a);
+    constexpr int B = ring_depth<CT, D>();
+    if (a.append && a.stream_kv)
+      hipLaunchKernelGGL((decode_balanced_kernel<CT, D, B, true, true>), grid, dim3(256), 0, stream, a);
+    else if (a.append)
+      hipLaunchKernelGGL((decode_balanced_kernel<CT, D, B, true, false>), grid, dim3(256), 0, stream, a);
+    else if (a.stream_kv)
+      hipLaunchKernelGGL((decode_balanced_kernel<CT, D, B, false, true>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_balanced_kernel<CT, D, ring_depth<CT, D>(), false>), grid,
-                         dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_balanced_kernel<CT, D, B, false, false>), grid, dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

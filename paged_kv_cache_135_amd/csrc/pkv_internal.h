@@ -69,6 +69,7 @@ struct DecodeArgs {
   // prefix_slot0 + pair * num_prefix_splits.
   int32_t len_offset;
   int32_t cascade;
+  int32_t stream_kv;    // pool tile reads carry the non-temporal hint
   int32_t num_prefix_splits;
   int64_t prefix_slot0;
   // Append (write folded into the decode): sequence s's new token, rows

@@ -63,6 +63,15 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// K/V tile reads from the pool.  NT: every block is read once in the call,
+// so the loads carry the non-temporal hint and stream past L2 and the MALL,
+// which keep the small per-call data (lengths, block tables, q) instead.
+template <bool NT, typename V>
+__device__ __forceinline__ V pool_load(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(static_cast<const V*>(p));
+  else return *static_cast<const V*>(p);
+}
+
 // ---------------------------------------------------------------------------
 // Per-element-type tile fragments.  `row0` is the pool row (token row of one
 // KV head) of the tile's first token; rows are D elements long.
@@ -92,29 +101,31 @@ struct Tile<PKV_BF16, D> {
     for (int j = 0; j < 4; ++j)
       v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * pitch + 2 * VE * (lane & 15));
   }
+  template <bool NT = false>
   __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t row0, int lane) {
     const uint16_t* kb = static_cast<const uint16_t*>(kc) + row0 * D;
     const uint16_t* vb = static_cast<const uint16_t*>(vc) + row0 * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      k[c] = *reinterpret_cast<const u32x4*>(kb + (lane & 15) * D + c * 32 + (lane >> 4) * 8);
+      k[c] = pool_load<NT, u32x4>(kb + (lane & 15) * D + c * 32 + (lane >> 4) * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * D + VE * (lane & 15));
+      v[j] = pool_load<NT, VRow>(vb + (4 * (lane >> 4) + j) * D + VE * (lane & 15));
   }
   // load() with token r of the tile read from the rows kn / vn instead (r < 0: none)
+  template <bool NT = false>
   __device__ __forceinline__ void load_sub(const void* kc, const void* vc, int64_t row0, int lane,
                                            int r, const void* kn, const void* vn, float, float) {
     const uint16_t* kb = static_cast<const uint16_t*>(kc) + row0 * D;
     const uint16_t* vb = static_cast<const uint16_t*>(vc) + row0 * D;
     const uint16_t* kr = (lane & 15) == r ? static_cast<const uint16_t*>(kn) : kb + (lane & 15) * D;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) k[c] = *reinterpret_cast<const u32x4*>(kr + c * 32 + (lane >> 4) * 8);
+    for (int c = 0; c < KC; ++c) k[c] = pool_load<NT, u32x4>(kr + c * 32 + (lane >> 4) * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = 4 * (lane >> 4) + j;
       const uint16_t* vr = t == r ? static_cast<const uint16_t*>(vn) : vb + t * D;
-      v[j] = *reinterpret_cast<const VRow*>(vr + VE * (lane & 15));
+      v[j] = pool_load<NT, VRow>(vr + VE * (lane & 15));
     }
   }
   // B operand of the q.K MFMAs: Q row g = lane % 16 with the same d mapping as k[]
@@ -222,22 +233,24 @@ struct Tile<PKV_FP8_E4M3, D> {
     for (int j = 0; j < 4; ++j)
       v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * pitch + VE * (lane & 15));
   }
+  template <bool NT = false>
   __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t row0, int lane) {
     const uint8_t* kb = static_cast<const uint8_t*>(kc) + row0 * D;
     const uint8_t* vb = static_cast<const uint8_t*>(vc) + row0 * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      k[c] = *reinterpret_cast<const u32x4*>(kb + (lane & 15) * D + 16 * ((lane >> 4) + 4 * c));
+      k[c] = pool_load<NT, u32x4>(kb + (lane & 15) * D + 16 * ((lane >> 4) + 4 * c));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * D + VE * (lane & 15));
+      v[j] = pool_load<NT, VRow>(vb + (4 * (lane >> 4) + j) * D + VE * (lane & 15));
   }
   // load() with token r replaced by the bf16 rows kn / vn, quantized as the
   // KV write quantizes them (the conversion waits for those loads); r < 0: none
+  template <bool NT = false>
   __device__ __forceinline__ void load_sub(const void* kc, const void* vc, int64_t row0, int lane,
                                            int r, const void* kn, const void* vn, float inv_k,
                                            float inv_v) {
-    load(kc, vc, row0, lane);
+    load<NT>(kc, vc, row0, lane);
     if (r < 0) return;
     if ((lane & 15) == r) {
 #pragma unroll
@@ -420,32 +433,34 @@ struct Tile<PKV_F32, D> {
         v[j][w] = *reinterpret_cast<const f32x4*>(vb + (4 * (lane >> 4) + j) * pitch +
                                                   4 * (VE * (lane & 15) + 4 * w));
   }
+  template <bool NT = false>
   __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t row0, int lane) {
     const float* kb = static_cast<const float*>(kc) + row0 * D;
     const float* vb = static_cast<const float*>(vc) + row0 * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      k[c] = *reinterpret_cast<const f32x4*>(kb + (lane & 15) * D + 4 * (4 * c + (lane >> 4)));
+      k[c] = pool_load<NT, f32x4>(kb + (lane & 15) * D + 4 * (4 * c + (lane >> 4)));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int w = 0; w < VE / 4; ++w)
-        v[j][w] = *reinterpret_cast<const f32x4*>(vb + (4 * (lane >> 4) + j) * D + VE * (lane & 15) + 4 * w);
+        v[j][w] = pool_load<NT, f32x4>(vb + (4 * (lane >> 4) + j) * D + VE * (lane & 15) + 4 * w);
   }
+  template <bool NT = false>
   __device__ __forceinline__ void load_sub(const void* kc, const void* vc, int64_t row0, int lane,
                                            int r, const void* kn, const void* vn, float, float) {
     const float* kb = static_cast<const float*>(kc) + row0 * D;
     const float* vb = static_cast<const float*>(vc) + row0 * D;
     const float* kr = (lane & 15) == r ? static_cast<const float*>(kn) : kb + (lane & 15) * D;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) k[c] = *reinterpret_cast<const f32x4*>(kr + 4 * (4 * c + (lane >> 4)));
+    for (int c = 0; c < KC; ++c) k[c] = pool_load<NT, f32x4>(kr + 4 * (4 * c + (lane >> 4)));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = 4 * (lane >> 4) + j;
       const float* vr = t == r ? static_cast<const float*>(vn) : vb + t * D;
 #pragma unroll
       for (int w = 0; w < VE / 4; ++w)
-        v[j][w] = *reinterpret_cast<const f32x4*>(vr + VE * (lane & 15) + 4 * w);
+        v[j][w] = pool_load<NT, f32x4>(vr + VE * (lane & 15) + 4 * w);
     }
   }
   struct QFrag {

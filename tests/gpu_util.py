@@ -72,19 +72,20 @@ class GpuCase:
         if c.k_new is not None:
             self.write(c.k_new, c.v_new, c.slot_mapping)
 
-    def decode(self, partition_size=0, waves=0, out=None, mode=None, workers=0):
+    def decode(self, partition_size=0, waves=0, out=None, mode=None, workers=0, stream_kv=False):
         c = self.case
         out = self.out if out is None else out
         pkv.paged_attention_decode(out, self.q, self.kc, self.vc, self.tables, self.lens, c.scale,
                                    c.block_size, k_scale=c.k_scale, v_scale=c.v_scale, mode=mode,
                                    partition_size=partition_size, waves_per_group=waves,
-                                   num_workers=workers)
+                                   num_workers=workers, stream_kv=stream_kv)
         return out
 
-    def decode_mode(self, m):
+    def decode_mode(self, m, stream_kv=False):
         """m = (mode, partition_size, waves_per_group, num_workers)."""
         mode, part, waves, workers = m
-        return self.decode(partition_size=part, waves=waves, mode=mode, workers=workers)
+        return self.decode(partition_size=part, waves=waves, mode=mode, workers=workers,
+                           stream_kv=stream_kv)
 
 
 def oracle_caches(case: PagedCase, tokens_mask=None):

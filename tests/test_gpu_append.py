@@ -184,3 +184,17 @@ def test_deferred_merge_is_bit_identical(mode):
     launch.merge()
     torch.cuda.synchronize()
     assert np.array_equal(_bits(gu.host(out)), _bits(ref))
+
+
+@pytest.mark.parametrize("m", [("single", 0, 4, 0), ("balanced", 0, 0, 0)], ids=_mid)
+def test_append_with_stream_kv_hint_is_bit_identical(m):
+    case = _small("g7_d128_bf16")
+    k, v, slots = _rows_per_sequence(case)
+    g1, g2 = _pre_step(case), _pre_step(case)
+    a = gu.host(_append(g1, k, v, slots, m)).copy()
+    out = torch.empty_like(g2.q)
+    pkv.paged_attention_decode_append(out, g2.q, gu.dev(k), gu.dev(v), gu.dev(slots), g2.kc, g2.vc,
+                                      g2.tables, g2.lens, case.scale, case.block_size,
+                                      stream_kv=True, **_kw(case, m))
+    assert np.array_equal(a, gu.host(out))
+    assert _same_pools(g2, gu.host(g1.kc), gu.host(g1.vc))

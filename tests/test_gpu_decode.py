@@ -190,3 +190,24 @@ def test_largest_block_size(dtype):
     ref = gu.oracle_decode(case, kc, vc)
     for m in [("single", 0, 2, 0), ("partitioned", 512, 4, 0), ("balanced", 0, 0, 9)]:
         gu.assert_close(gu.host(g.decode_mode(m)), ref, dtype, f"bs 256 {_mid(m)}")
+
+
+# ------------------------------------------------- streaming-load hint
+@pytest.mark.parametrize("mode", [("single", 0, 4, 0), ("partitioned", 64, 2, 0),
+                                  ("balanced", 0, 0, 0), ("auto", 0, 0, 0)], ids=_mid)
+@pytest.mark.parametrize("name", ["g7_d128_bf16", "g4_d128_e4m3", "g2_d64_f32", "empty_rows_bf16"])
+def test_stream_kv_hint_changes_no_bit(name, mode):
+    """PKV_DECODE_STREAM_KV only changes the cache policy of the pool reads."""
+    case, g, ref = _prepared(name)
+    plain = gu.host(g.decode_mode(mode)).copy()
+    streamed = gu.host(g.decode_mode(mode, stream_kv=True))
+    assert np.array_equal(plain.view(np.uint8), streamed.view(np.uint8))
+    gu.assert_close(streamed, ref, case.cache_dtype, f"{name} {_mid(mode)} stream_kv")
+
+
+def test_stream_kv_hint_on_the_full_qwen_batch():
+    case, got, ref, _ = _full("c2", workloads.c2_qwen_decode, ("balanced", 0, 0, 0))
+    g = gu.GpuCase(case)
+    g.fill_and_step_writes()
+    streamed = gu.host(g.decode_mode(("balanced", 0, 0, 0), stream_kv=True))
+    assert np.array_equal(got.view(np.uint8), streamed.view(np.uint8))

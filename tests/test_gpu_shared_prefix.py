@@ -93,3 +93,13 @@ def test_full_shared_prefix_batch():
     # and the plain decode of the same batch agrees with it within rounding
     plain = gu.host(g.decode(mode="auto"))
     gu.assert_close(plain, ref, case.cache_dtype, "plain decode")
+
+
+def test_stream_kv_hint_on_the_tails_is_bit_identical():
+    case, g, prefix, _ = _prepared("g4_d128_bf16")
+    a = gu.host(_run(g, case, prefix)).copy()
+    out = torch.empty_like(g.q)
+    pkv.paged_attention_decode_shared_prefix(out, g.q, g.kc, g.vc, g.tables, g.lens, prefix,
+                                             case.scale, case.block_size, k_scale=case.k_scale,
+                                             v_scale=case.v_scale, stream_kv=True)
+    assert np.array_equal(a, gu.host(out))
