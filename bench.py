@@ -88,8 +88,11 @@ def measured_traffic(workload: str):
     import glob
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
-    src = os.path.join(here, "paged_kv_cache_135_amd", "csrc", "decode.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    csrc = os.path.join(here, "paged_kv_cache_135_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("decode.hip", "tile.h"):  # the decode kernels' sources
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    sha = h.hexdigest()
     for path in sorted(glob.glob(os.path.join(here, "profiles", "*_pmc_traffic.md"))):
         fields = {}
         with open(path) as f:
@@ -98,7 +101,7 @@ def measured_traffic(workload: str):
                 if ":" in line:
                     k, v = line.split(":", 1)
                     fields[k.strip()] = v.strip()
-        if workload in first and fields.get("decode.hip sha256") == sha:
+        if workload in first and fields.get("decode.hip+tile.h sha256") == sha:
             return int(fields["traffic_bytes_per_launch"]), fields.get("kernel", "")
     return None, None
 
