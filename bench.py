@@ -106,6 +106,29 @@ def measured_traffic(workload: str):
     return None, None
 
 
+def read_ceiling(stream, gib: int = 2, reps: int = 20) -> dict:
+    """The box's attainable streaming-read rate: the library's read probe over a
+    fresh device buffer (larger than L2 and the MALL), back to back between
+    two events, after two untimed passes."""
+    import torch
+
+    import paged_kv_cache_135_amd as pkv
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = pkv.read_probe(buf, stream=stream)
+    pkv.read_probe(buf, sink, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        pkv.read_probe(buf, sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / reps
+    del buf
+    return {"value": round((gib << 30) / s / 1e9, 1), "unit": "GB/s", "bytes": gib << 30,
+            "kernel": "read_probe_kernel (one pass, 16-byte non-temporal loads)"}
+
+
 def cpu_baseline(case, seconds):
     """The fp64 oracle (write + decode of one step) on this host's cores."""
     import oracle
@@ -553,6 +576,7 @@ def main():
 
     kv = case.kv_bytes()
     traffic, traffic_kernel = measured_traffic(case.name)
+    ceiling = read_ceiling(stream)
     value = kv / (ms_per_step / 1e3) / 1e9
     # HBM roofline: bytes that must come from memory; a shared prefix counts once
     roof_bytes = case.unique_kv_bytes() if case.shared_blocks else kv
@@ -616,6 +640,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
         },
+        # the same kernel's rate against what one plain streaming pass reaches on this machine
+        "read_ceiling": dict(ceiling, frac_of_ceiling=round(achieved / ceiling["value"], 4)),
     }
     if case.cache_dtype != "bf16" or case.shared_blocks:
         res["unique_kv_bytes_per_step"] = case.unique_kv_bytes()

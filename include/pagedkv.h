@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 6
+#define PKV_ABI_VERSION 7
 #define PKV_MAX_DIMS 4
 
 typedef enum {
@@ -372,6 +372,19 @@ pkv_status paged_kv_gather_blocks(const pkv_tensor* key_cache, const pkv_tensor*
 pkv_status paged_kv_scatter_blocks(const pkv_tensor* in_k, const pkv_tensor* in_v,
                                    const pkv_tensor* block_ids, pkv_tensor* key_cache,
                                    pkv_tensor* value_cache, void* hip_stream);
+
+/* Measurement support, not a step of the method: the device's attainable
+ * streaming-read rate, against which the decode kernels' byte rates are
+ * reported next to the datasheet peak.  Reads `bytes` of device memory at
+ * `buf` once (16-byte non-temporal loads, pkv_read_probe_blocks() workgroups
+ * of 256 threads) and writes to sink[b] the XOR of the 32-bit words that
+ * workgroup b read, so the XOR of all sink words is the XOR of the buffer's
+ * words.  buf and sink: device memory (PKV_ERR_LAYOUT otherwise), buf 16-byte
+ * aligned and bytes a multiple of 16 (PKV_ERR_SHAPE); sink holds at least
+ * pkv_read_probe_blocks() words.  bytes 0: nothing is launched.  Asynchronous
+ * on hip_stream. */
+int32_t pkv_read_probe_blocks(void);
+pkv_status pkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream);
 
 /* Workspace bytes paged_attention_decode needs with these sizes and options
  * (0 when none is needed: single pass, or one partition per sequence).

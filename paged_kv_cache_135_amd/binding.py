@@ -28,8 +28,9 @@ EXPORTED = (
     "pkv_validate_block_pairs", "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
     "pkv_validate_block_ids", "paged_attention_decode_shared_prefix",
     "paged_attention_decode_shared_prefix_workspace_bytes", "pkv_validate_shared_prefix",
+    "pkv_read_probe_blocks", "pkv_read_probe",
 )
-ABI_VERSION = 6
+ABI_VERSION = 7
 DECODE_DEFER_MERGE = 1
 DECODE_STREAM_KV = 2
 
@@ -108,6 +109,9 @@ def load():
         raise RuntimeError(f"{LIB_PATH} has ABI version {lib.pkv_abi_version()}, this binding "
                            f"expects {ABI_VERSION}: rebuild it")
     lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_read_probe_blocks.restype = ctypes.c_int32
+    lib.pkv_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.pkv_read_probe.restype = ctypes.c_int
     lib.paged_kv_write.argtypes = [T, T, T, T, T, P]
     lib.paged_kv_write.restype = ctypes.c_int
     lib.paged_attention_decode.argtypes = [T, T, T, T, T, T, ctypes.c_float, ctypes.c_int32,
@@ -399,6 +403,21 @@ def paged_kv_scatter_blocks(in_k, in_v, block_ids, key_cache, value_cache, *,
          describe(value_cache)]
     _check(load().paged_kv_scatter_blocks(*[ctypes.byref(x) for x in d],
                                           _stream_of(key_cache, stream)))
+
+
+def read_probe(buf, sink=None, *, stream=None):
+    """Measurement support: one streaming pass over the device tensor ``buf``
+    (the attainable read rate the decode byte rates are set against).  Returns
+    the sink, a uint32 device tensor whose XOR is the XOR of buf's 32-bit words."""
+    import torch
+    lib = load()
+    if sink is None:
+        sink = torch.empty(lib.pkv_read_probe_blocks(), dtype=torch.int32, device=buf.device)
+    s = stream if stream is not None else torch.cuda.current_stream(buf.device)
+    _check(lib.pkv_read_probe(ctypes.c_void_p(buf.data_ptr()),
+                              buf.numel() * buf.element_size(),
+                              ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
+    return sink
 
 
 def swap_out_to_host(key_cache, value_cache, block_ids, host_k, host_v, *, staging=None,

@@ -517,6 +517,21 @@ pkv_status paged_kv_scatter_blocks(const pkv_tensor* in_k, const pkv_tensor* in_
                     false, hip_stream);
 }
 
+int32_t pkv_read_probe_blocks(void) { return 4 * device_cus(); }
+
+pkv_status pkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream) {
+  if (bytes == 0) return ok();  // nothing to read, nothing launched
+  if (!buf || !sink) return fail(PKV_ERR_NULL, "pkv_read_probe: null buffer");
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(PKV_ERR_SHAPE, "pkv_read_probe: buf must be 16-byte aligned and bytes a multiple of 16");
+  if (!device_memory(buf) || !device_memory(sink))
+    return fail(PKV_ERR_LAYOUT, "pkv_read_probe: buf and sink must be device memory");
+  const hipError_t e = pkv::launch_read_probe(buf, (int64_t)bytes, sink, pkv_read_probe_blocks(),
+                                              static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_read_probe: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim,
                                               int32_t max_blocks_per_seq, int32_t block_size,

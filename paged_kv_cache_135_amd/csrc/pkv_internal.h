@@ -151,6 +151,8 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_shared_prefix(const PrefixArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks,
+                             hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -414,3 +414,16 @@ def test_shared_prefix_validator():
         B.validate_shared_prefix(np.array([[4, 2, 7], [4, 3, 1], [4, 2, 9]], np.int32), lens, 10, 16, 32)
     with pytest.raises(B.PagedKVError):
         B.validate_shared_prefix(tables, lens, 10, 16, 24)
+
+
+def test_read_probe_validates_before_any_launch():
+    lib = B.load()
+    buf = (ctypes.c_uint8 * 64)()
+    sink = (ctypes.c_uint32 * 4)()
+    addr = ctypes.addressof(buf)
+    assert lib.pkv_read_probe(None, 64, ctypes.addressof(sink), None) == 1  # PKV_ERR_NULL
+    assert lib.pkv_read_probe(addr + (16 - addr % 16) % 16 + 4, 32, ctypes.addressof(sink), None) == 3
+    assert lib.pkv_read_probe(addr + (16 - addr % 16) % 16, 40, ctypes.addressof(sink), None) == 3
+    # host memory is refused: the kernel would dereference it
+    assert lib.pkv_read_probe(addr + (16 - addr % 16) % 16, 32, ctypes.addressof(sink), None) == 4
+    assert b"device memory" in lib.pkv_last_error()
