@@ -129,10 +129,9 @@ def read_ceiling(stream, gib: int = 2, reps: int = 20) -> dict:
             "kernel": "read_probe_kernel (one pass, 16-byte non-temporal loads)"}
 
 
-def cpu_baseline(case, seconds):
-    """The fp64 oracle (write + decode of one step) on this host's cores."""
+def _oracle_steps(case, seconds):
+    """Repeat the oracle's whole step (write + decode) for about `seconds`."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     kc, vc = case.key_cache.copy(), case.value_cache.copy()
     reps = 0
     t0 = time.perf_counter()
@@ -145,7 +144,27 @@ def cpu_baseline(case, seconds):
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
+            return reps, el
+
+
+def cpu_baseline(case, seconds):
+    """The fp64 oracle (write + decode of one step) on this host's cores, and
+    a shorter sample of it on one thread (OpenMP's thread count set through
+    libgomp, then restored)."""
+    import ctypes
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    reps, el = _oracle_steps(case, seconds)
+    single = None
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        r1, e1 = _oracle_steps(case, seconds / 2)
+        gomp.omp_set_num_threads(threads)
+        single = {"value": case.kv_bytes() * r1 / e1 / 1e9, "unit": "GB/s", "cores": 1,
+                  "tokens_per_s_per_layer": case.num_seqs * r1 / e1,
+                  "sample": f"the same step, {r1} times in {e1:.1f} s"}
+    except OSError:
+        pass
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -164,6 +183,7 @@ def cpu_baseline(case, seconds):
                   f"sequences), repeated {reps} times in {el:.1f} s",
         "tokens_per_s_per_layer": case.num_seqs * reps / el,
         "cpu_model": model,
+        "single_thread": single,
     }
 
 
