@@ -78,10 +78,11 @@ __device__ __forceinline__ float raise_max(RowState<VE>& st, float local_max, fl
   return m_new;
 }
 
-// Keys are staged in LDS kStageKeys at a time.
+// Keys pass through LDS in stages: kStageKeys at a time for f32 caches, one
+// softmax block (kBlockTiles tiles, double-buffered) for the bf16 images.
 constexpr int kStageKeys = 128;
 constexpr int kStageTiles = kStageKeys / 16;
-constexpr int kBlockTiles = 4;  // tiles per softmax block (bf16 images)
+constexpr int kBlockTiles = 4;
 
 // f32 caches: K and V rows copied as they are, padded by 32 bytes so that the
 // lanes reading one 16-byte column of 16 different rows meet the fewest bank
@@ -336,10 +337,10 @@ enum RowsJob : int { kPrefillJob = 0, kPrefixJob = 1 };
 //     causal, final outputs (PrefillArgs).
 //   kPrefixJob: rows = every sequence's query heads of one KV head against one
 //     key split of a shared prefix, no mask, partial states (PrefixArgs).
-// Per stage the workgroup's threads copy kStageKeys keys of K and V from the
-// pool into LDS, then every wavefront reads its MFMA fragments from there.
-// The next stage's global loads are issued before the current stage is
-// computed, so they are in flight meanwhile.
+// Per stage the workgroup's threads copy the stage's K and V from the pool
+// into LDS, then every wavefront reads its MFMA fragments from there.  The
+// next stage's global loads are issued before the current stage is computed,
+// so they are in flight meanwhile.
 template <int CT, int D, int R, int JOB, typename Args>
 __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_kernel(Args a) {
   constexpr bool F32 = CT == PKV_F32;

@@ -10,7 +10,9 @@
 // 4 * (lane / 16) + i in each lane, which is the B-operand layout of the P.V
 // product, so probabilities never leave their registers.  V arrives row-major;
 // pairs of tokens are packed with v_perm into the A operand of
-// out^T = V^T . P with MFMA row m standing for d = VE * m + r.
+// out^T = V^T . P with MFMA row m standing for d = VE * m + r.  The f32 tile
+// also reads from a padded LDS copy (load_pitched) for the chunked prefill,
+// whose bf16 and E4M3 path builds its own operand images in LDS instead.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -91,16 +93,6 @@ struct Tile<PKV_BF16, D> {
   u32x4 k[KC];
   VRow v[4];
 
-  // The same fragments from rows `pitch` bytes apart starting at kb / vb (an
-  // LDS copy of the tile, rows padded against bank conflicts).
-  __device__ __forceinline__ void load_pitched(const char* kb, const char* vb, int pitch, int lane) {
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-      k[c] = *reinterpret_cast<const u32x4*>(kb + (lane & 15) * pitch + 2 * (c * 32 + (lane >> 4) * 8));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * pitch + 2 * VE * (lane & 15));
-  }
   template <bool NT = false>
   __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t row0, int lane) {
     const uint16_t* kb = static_cast<const uint16_t*>(kc) + row0 * D;
@@ -152,55 +144,6 @@ struct Tile<PKV_BF16, D> {
 #pragma unroll
       for (int w = 0; w < VE / 2; ++w) v[j][w] = ok[j] ? v[j][w] : 0u;
   }
-  // The P.V A operands packed once, for tiles used by several query blocks.
-  struct PV {
-    u32x2 a[VE];
-  };
-  __device__ __forceinline__ PV pack_v() const {
-    PV o;
-#pragma unroll
-    for (int r = 0; r < VE; ++r) {
-      const uint32_t sel = (r & 1) ? kSelHi : kSelLo;
-      o.a[r] = u32x2{__builtin_amdgcn_perm(v[1][r >> 1], v[0][r >> 1], sel),
-                     __builtin_amdgcn_perm(v[3][r >> 1], v[2][r >> 1], sel)};
-    }
-    return o;
-  }
-  __device__ static __forceinline__ float pv_packed(const PV& o, const float p[4], f32x4 acc[VE]) {
-    const uint32_t p01 = pack_bf16(p[0], p[1]);
-    const uint32_t p23 = pack_bf16(p[2], p[3]);
-    const u32x2 pb = {p01, p23};
-#pragma unroll
-    for (int r = 0; r < VE; ++r) acc[r] = mfma_bf16_k16(o.a[r], pb, acc[r]);
-    return (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-  }
-  // Two tiles a (keys 0..15) and b (16..31) as one K=32 operand of the
-  // double-rate MFMA: lane group q = lane / 16 carries keys 4q..4q+3 of a, then
-  // of b, in P and in V^T alike, which is how both fragments already sit.
-  struct PV2 {
-    u32x4 a[VE];
-  };
-  __device__ static __forceinline__ PV2 pack_v2(const Tile& ta, const Tile& tb) {
-    PV2 o;
-#pragma unroll
-    for (int r = 0; r < VE; ++r) {
-      const uint32_t sel = (r & 1) ? kSelHi : kSelLo;
-      o.a[r] = u32x4{__builtin_amdgcn_perm(ta.v[1][r >> 1], ta.v[0][r >> 1], sel),
-                     __builtin_amdgcn_perm(ta.v[3][r >> 1], ta.v[2][r >> 1], sel),
-                     __builtin_amdgcn_perm(tb.v[1][r >> 1], tb.v[0][r >> 1], sel),
-                     __builtin_amdgcn_perm(tb.v[3][r >> 1], tb.v[2][r >> 1], sel)};
-    }
-    return o;
-  }
-  __device__ static __forceinline__ float pv2(const PV2& o, const float pa[4], const float pb[4],
-                                              f32x4 acc[VE]) {
-    const u32x4 pk = {pack_bf16(pa[0], pa[1]), pack_bf16(pa[2], pa[3]), pack_bf16(pb[0], pb[1]),
-                      pack_bf16(pb[2], pb[3])};
-#pragma unroll
-    for (int r = 0; r < VE; ++r) acc[r] = mfma_bf16_k32(o.a[r], pk, acc[r]);
-    return ((bf16_lo(pk[0]) + bf16_hi(pk[0])) + (bf16_lo(pk[1]) + bf16_hi(pk[1]))) +
-           ((bf16_lo(pk[2]) + bf16_hi(pk[2])) + (bf16_lo(pk[3]) + bf16_hi(pk[3])));
-  }
   // acc[r] += V^T(rows d = VE*m + r) . P ; returns the sum of the rounded p
   __device__ __forceinline__ float pv(const float p[4], f32x4 acc[VE]) const {
     const uint32_t p01 = pack_bf16(p[0], p[1]);
@@ -225,14 +168,6 @@ struct Tile<PKV_FP8_E4M3, D> {
   u32x4 k[KC];
   VRow v[4];
 
-  __device__ __forceinline__ void load_pitched(const char* kb, const char* vb, int pitch, int lane) {
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-      k[c] = *reinterpret_cast<const u32x4*>(kb + (lane & 15) * pitch + 16 * ((lane >> 4) + 4 * c));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      v[j] = *reinterpret_cast<const VRow*>(vb + (4 * (lane >> 4) + j) * pitch + VE * (lane & 15));
-  }
   template <bool NT = false>
   __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t row0, int lane) {
     const uint8_t* kb = static_cast<const uint8_t*>(kc) + row0 * D;
@@ -316,77 +251,6 @@ struct Tile<PKV_FP8_E4M3, D> {
         v[j] = ok[j] ? v[j] : 0u;
       }
     }
-  }
-  struct PV {
-    u32x2 a[VE];
-  };
-  __device__ __forceinline__ PV pack_v() const {
-    float fv[4][VE];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int w = 0; w < VE / 4; ++w) {
-        uint32_t word;
-        if constexpr (VE == 8) word = v[j][w]; else word = v[j];
-        const f32x2 a = fp8x2_lo(word), b = fp8x2_hi(word);
-        fv[j][4 * w + 0] = a[0];
-        fv[j][4 * w + 1] = a[1];
-        fv[j][4 * w + 2] = b[0];
-        fv[j][4 * w + 3] = b[1];
-      }
-    }
-    PV o;
-#pragma unroll
-    for (int r = 0; r < VE; ++r)
-      o.a[r] = u32x2{pack_exact(fv[0][r], fv[1][r]), pack_exact(fv[2][r], fv[3][r])};
-    return o;
-  }
-  __device__ static __forceinline__ float pv_packed(const PV& o, const float p[4], f32x4 acc[VE]) {
-    const uint32_t p01 = pack_bf16(p[0], p[1]);
-    const uint32_t p23 = pack_bf16(p[2], p[3]);
-    const u32x2 pb = {p01, p23};
-#pragma unroll
-    for (int r = 0; r < VE; ++r) acc[r] = mfma_bf16_k16(o.a[r], pb, acc[r]);
-    return (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-  }
-  struct PV2 {
-    u32x4 a[VE];
-  };
-  // the V rows of one tile as f32 (exact), fv[j][e]: token 4q+j, d = VE*m + e
-  __device__ __forceinline__ void v_f32(float fv[4][VE]) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int w = 0; w < VE / 4; ++w) {
-        uint32_t word;
-        if constexpr (VE == 8) word = v[j][w]; else word = v[j];
-        const f32x2 a = fp8x2_lo(word), b = fp8x2_hi(word);
-        fv[j][4 * w + 0] = a[0];
-        fv[j][4 * w + 1] = a[1];
-        fv[j][4 * w + 2] = b[0];
-        fv[j][4 * w + 3] = b[1];
-      }
-    }
-  }
-  __device__ static __forceinline__ PV2 pack_v2(const Tile& ta, const Tile& tb) {
-    float fa[4][VE], fb[4][VE];
-    ta.v_f32(fa);
-    tb.v_f32(fb);
-    PV2 o;
-#pragma unroll
-    for (int r = 0; r < VE; ++r)
-      o.a[r] = u32x4{pack_exact(fa[0][r], fa[1][r]), pack_exact(fa[2][r], fa[3][r]),
-                     pack_exact(fb[0][r], fb[1][r]), pack_exact(fb[2][r], fb[3][r])};
-    return o;
-  }
-  __device__ static __forceinline__ float pv2(const PV2& o, const float pa[4], const float pb[4],
-                                              f32x4 acc[VE]) {
-    const u32x4 pk = {pack_bf16(pa[0], pa[1]), pack_bf16(pa[2], pa[3]), pack_bf16(pb[0], pb[1]),
-                      pack_bf16(pb[2], pb[3])};
-#pragma unroll
-    for (int r = 0; r < VE; ++r) acc[r] = mfma_bf16_k32(o.a[r], pk, acc[r]);
-    return ((bf16_lo(pk[0]) + bf16_hi(pk[0])) + (bf16_lo(pk[1]) + bf16_hi(pk[1]))) +
-           ((bf16_lo(pk[2]) + bf16_hi(pk[2])) + (bf16_lo(pk[3]) + bf16_hi(pk[3])));
   }
   __device__ __forceinline__ float pv(const float p[4], f32x4 acc[VE]) const {
     const uint32_t p01 = pack_bf16(p[0], p[1]);
