@@ -143,7 +143,8 @@ __device__ __forceinline__ void update_tile_f32(const Tile<PKV_F32, D>& tl,
 
 // bf16 images (bf16 and E4M3 caches): a block of NT tiles (keys t0 ..
 // t0 + 16 NT - 1) for the R row blocks, with one max and one rescale per row
-// block for the whole block.  Scores come from the K image (kt: the block's
+// block for the whole block, in two halves: block_probs (scores, max,
+// rescale, probabilities) and block_pv (P.V and the row sums).  Scores come from the K image (kt: the block's
 // first tile, ko: the lane's chunk offsets); P.V runs per tile pair a, b on the
 // double-rate K=32 MFMA, lane group q carrying keys 4q..4q+3 of a, then of b,
 // in P and in V^T alike.  V^T is read from its LDS image one MFMA row group r
@@ -154,11 +155,10 @@ __device__ __forceinline__ void update_tile_f32(const Tile<PKV_F32, D>& tl,
 // t0 - 4 * lane group) are dropped (score -inf); the staging zeroes V past
 // the context, so no stray bits reach the sums.
 template <int D, int R, int NT>
-__device__ __forceinline__ void update_block(const char* kt, const int (&ko)[D / 32],
-                                             const typename Tile<PKV_BF16, D>::QFrag (&qf)[R],
-                                             RowState<D / 16> (&st)[R], const char* vt, bool masked,
-                                             const int (&lim)[R], int live, float qs) {
-  constexpr int VE = D / 16;
+__device__ __forceinline__ void block_probs(const char* kt, const int (&ko)[D / 32],
+                                            const typename Tile<PKV_BF16, D>::QFrag (&qf)[R],
+                                            RowState<D / 16> (&st)[R], bool masked, const int (&lim)[R],
+                                            int live, float qs, u32x4 (&pk)[R][NT / 2]) {
   f32x4 sc[R][NT];
 #pragma unroll
   for (int rb = 0; rb < R; ++rb)
@@ -182,7 +182,6 @@ __device__ __forceinline__ void update_block(const char* kt, const int (&ko)[D /
         for (int i = 0; i < 4; ++i)
           if (!(t < live && 16 * t + i <= lim[rb])) sc[rb][t][i] = kNegInf;
   }
-  u32x4 pk[R][NT / 2];
 #pragma unroll
   for (int rb = 0; rb < R; ++rb) {
     float x[4 * NT], p[4 * NT];
@@ -196,6 +195,14 @@ __device__ __forceinline__ void update_block(const char* kt, const int (&ko)[D /
       pk[rb][h] = u32x4{pack_bf16(p[8 * h], p[8 * h + 1]), pack_bf16(p[8 * h + 2], p[8 * h + 3]),
                         pack_bf16(p[8 * h + 4], p[8 * h + 5]), pack_bf16(p[8 * h + 6], p[8 * h + 7])};
   }
+}
+
+// P.V of one block: V^T from its LDS image (vt: the block's first pair, this
+// lane's offset) against the probabilities pk, plus the row sums.
+template <int D, int R, int NT>
+__device__ __forceinline__ void block_pv(const char* vt, const u32x4 (&pk)[R][NT / 2],
+                                         RowState<D / 16> (&st)[R]) {
+  constexpr int VE = D / 16;
   constexpr uint32_t kOnes = 0x3f803f80u;  // two bf16 1.0
 #pragma unroll
   for (int h = 0; h < NT / 2; ++h) {
@@ -363,10 +370,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
   const float qs = q_zero ? 1.f : fabsf(qs_in);
 
   __shared__ int64_t sm_row[kPrefillChunkTiles];  // pool row of each tile's first key
-  // bf16 images: two stage buffers, one computed while the next is written
+  // bf16 images: stage buffers for K (two: one read, the next written) and V
+  // (three: the lagging half of the wavefronts still reads the previous one)
   constexpr int K_STAGE = 16 * kBlockTiles * 2 * D, V_STAGE = (kBlockTiles / 2) * vpair_bytes<D>();
   constexpr int K_BYTES = F32 ? kStageKeys * f32_pitch<D>() : 2 * K_STAGE;
-  constexpr int V_BYTES = F32 ? kStageKeys * f32_pitch<D>() : 2 * V_STAGE;
+  constexpr int V_BYTES = F32 ? kStageKeys * f32_pitch<D>() : 3 * V_STAGE;
   __shared__ __attribute__((aligned(16))) char sm_k[K_BYTES];
   __shared__ __attribute__((aligned(16))) char sm_v[V_BYTES];
   static_assert(K_BYTES >= 4 * (kRankBuckets + 16), "ranking scratch");
@@ -650,20 +658,33 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
             }
           }
         };
-        // stage n sits in buffer n % 2; the write of stage n + 1 and the loads
-        // of stage n + 2 overlap the compute of stage n, one barrier per stage
+        // Stage n's K sits in K buffer n % 2 and its V in V buffer n % 3; the
+        // write of stage n + 1 and the loads of stage n + 2 overlap the compute
+        // of stage n, one barrier per stage.  The second half of the
+        // wavefronts runs each block's P.V one stage late (ping-pong): while
+        // the first half issues a block's score MFMAs, the second half issues
+        // the previous block's P.V MFMAs, and each half's softmax VALU work then
+        // meets the other half's MFMAs instead of its own partner's softmax.
+        const bool lagging = wave >= NW / 2;
+        const int voff = (lane >> 4) * 256 + (lane & 15) * 16;
+        u32x4 pk[R][NT / 2];  // a block's probabilities (lagging waves: until the next stage)
+        int late_buf = -1;    // lagging waves: the V buffer pk goes with (-1: none)
         fetch(c0);
         stage_write(c0, sm_k, sm_v);
         if (c0 + NT < c1) fetch(c0 + NT);
         __syncthreads();
-        for (int t0s = c0, cur = 0; t0s < c1; t0s += NT, cur ^= 1) {
+        for (int t0s = c0, n = 0; t0s < c1; t0s += NT, ++n) {
+          const int kb = n & 1, vb = n % 3;
           if (t0s + NT < c1) {
-            stage_write(t0s + NT, sm_k + (cur ^ 1) * K_STAGE, sm_v + (cur ^ 1) * V_STAGE);
+            stage_write(t0s + NT, sm_k + (kb ^ 1) * K_STAGE, sm_v + ((n + 1) % 3) * V_STAGE);
             if (t0s + 2 * NT < c1) fetch(t0s + 2 * NT);  // in flight during the compute
+          }
+          if (lagging && late_buf >= 0) {  // wave-uniform
+            block_pv<D, R, NT>(sm_v + late_buf * V_STAGE + voff, pk, st);
+            late_buf = -1;
           }
           if (t0s < k_hi_w) {  // wave-uniform
             const int t0 = t0s * 16;
-            const char* vt = sm_v + cur * V_STAGE + (lane >> 4) * 256 + (lane & 15) * 16;
             int lim[R];
 #pragma unroll
             for (int rb = 0; rb < R; ++rb) lim[rb] = pos4[rb] - t0;
@@ -671,10 +692,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
             // past the wavefront's range, is masked
             const int live_tiles = k_hi_w - t0s;
             const bool masked = (JOB == kPrefillJob && t0 + SK - 1 > minpos_w) || live_tiles < NT;
-            update_block<D, R, NT>(sm_k + cur * K_STAGE, ko, qf, st, vt, masked, lim, live_tiles, qs);
+            block_probs<D, R, NT>(sm_k + kb * K_STAGE, ko, qf, st, masked, lim, live_tiles, qs, pk);
+            if (lagging)
+              late_buf = vb;
+            else
+              block_pv<D, R, NT>(sm_v + vb * V_STAGE + voff, pk, st);
           }
           __syncthreads();  // stage n read and stage n + 1 written by every wave
         }
+        if (late_buf >= 0) block_pv<D, R, NT>(sm_v + late_buf * V_STAGE + voff, pk, st);
       }
     }
 
