@@ -136,11 +136,10 @@ struct Plan {
   }
 };
 
-// Key splits of a shared prefix: about one (128 query rows, KV head, split)
-// unit per compute unit, at least four tiles per split.  The prefix kernel's
-// workgroups hold 256 rows, so this leaves about half the compute units to
-// it; more splits cost more in the merge than they save (256-sequence batch,
-// whole call: 4 splits 114.9 us, 8: 116.8, 12: 131.4, 16: 134.4).
+// Key splits of a shared prefix: about one (128-row workgroup, KV head, split)
+// unit per compute unit, at least four tiles per split; more splits cost more
+// in the merge than they save (256-sequence batch, whole call: 2 splits
+// 111.9 us, 4: 110.5, 8: 119.2).
 int32_t prefix_splits(int64_t S, int64_t G, int64_t Hkv, int64_t prefix_len) {
   const int64_t tiles = prefix_len / 16;
   const int64_t row_groups = (S * G + 127) / 128;

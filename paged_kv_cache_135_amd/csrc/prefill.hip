@@ -744,11 +744,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
 
 template <int CT, int D>
 hipError_t launch_prefix_d(const PrefixArgs& a, hipStream_t stream) {
-  constexpr int ROWS_G = 32 * kPrefillWaves;
+  // 16 rows per wavefront (128 per workgroup): each workgroup sees only its
+  // key split, so more, smaller workgroups beat fuller ones (measured on the
+  // 256-sequence batch: 110.5 us per call against 115.3 us with 32 rows)
+  constexpr int ROWS_G = 16 * kPrefillWaves;
   int64_t gz = ((int64_t)a.num_seqs * a.group + ROWS_G - 1) / ROWS_G;
   gz = gz < 1 ? 1 : gz > 65535 ? 65535 : gz;
   const dim3 grid((unsigned)a.num_kv_heads, (unsigned)a.splits, (unsigned)gz);
-  hipLaunchKernelGGL((rows_kernel<CT, D, 2, kPrefixJob, PrefixArgs>), grid, dim3(kPrefillWaves * 64), 0,
+  hipLaunchKernelGGL((rows_kernel<CT, D, 1, kPrefixJob, PrefixArgs>), grid, dim3(kPrefillWaves * 64), 0,
                      stream, a);
   return hipGetLastError();
 }
