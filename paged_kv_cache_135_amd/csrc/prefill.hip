@@ -260,17 +260,28 @@ __device__ int block_exclusive_scan(int v, int* scratch, int& total) {
 // 2^shift tiles, at most kRankBuckets of them), then by s, then by rg, so the
 // long jobs start first and the short ones fill in behind them.  Every
 // workgroup computes the same counting sort over the lengths and keeps the
-// job of its own rank; false: no job of that rank.  scratch: kRankBuckets + 16
-// ints of LDS.
+// job of its own rank.
 constexpr int kRankBuckets = 2 * kPrefillWaves * 64;
-__device__ bool ranked_job(const PrefillArgs& a, int rows_g, int rank, int* scratch, int& s_out, int& rg_out) {
+
+struct PrefillJob {
+  int s, rg;        // sequence, row group
+  int q0, nq, ctx;  // its first query token, query count and context length
+};
+
+__device__ __forceinline__ int job_cost(int first, int rows, int rg, int rows_g, int G) {
+  return (first + (min(rows, (rg + 1) * rows_g) - 1) / G) / 16 + 1;
+}
+
+// The ranking for any batch size: thread t owns a contiguous run of sequences
+// and reads their lengths from global memory in every pass.  false: no job of
+// that rank.  scratch: kRankBuckets + 16 ints of LDS.
+__device__ bool ranked_job_by_seq(const PrefillArgs& a, int rows_g, int rank, int* scratch, int& s_out,
+                                  int& rg_out) {
   constexpr int NT = kPrefillWaves * 64;
   const int S = a.num_seqs, G = a.group, tid = threadIdx.x;
   int* hist = scratch;
   int* tmp = scratch + kRankBuckets;  // [0, 8): scan, [8, 12): results
-  auto cost = [&](int first, int rows, int rg) {
-    return (first + (min(rows, (rg + 1) * rows_g) - 1) / G) / 16 + 1;
-  };
+  auto cost = [&](int first, int rows, int rg) { return job_cost(first, rows, rg, rows_g, G); };
   // the largest cost (every sequence's last row group) sets the bucket width
   int mx = 0;
   for (int s = tid; s < S; s += NT) {
@@ -337,6 +348,133 @@ __device__ bool ranked_job(const PrefillArgs& a, int rows_g, int rank, int* scra
   return true;
 }
 
+// The ranking for batches whose sequence table fits the scratch: the
+// sequences' lengths are read from global memory once, into LDS with each
+// sequence's first job index, and the passes split the flat job list evenly
+// over the threads (a batch of a few long chunks has many row groups per
+// sequence; one thread per sequence would walk them alone).  Same order as
+// ranked_job_by_seq.  false: no job of that rank.  scratch: kRankBuckets + 16
+// + 4 * num_seqs + 1 ints of LDS.
+template <int NT>
+__device__ bool ranked_job_staged(const PrefillArgs& a, int rows_g, int rank, int* scratch, PrefillJob& job) {
+  const int S = a.num_seqs, G = a.group, tid = threadIdx.x;
+  int* hist = scratch;
+  int* tmp = scratch + kRankBuckets;  // [0, 8): scans, [8, 16): maxima, then results
+  int* seq = tmp + 16;                // q0, nq, ctx of sequence s at 3 s
+  int* joff = seq + 3 * S;            // first job index of sequence s; joff[S]: job count
+  for (int i = tid; i < kRankBuckets; i += NT) hist[i] = 0;
+  // pass 1: per-sequence data, job counts and the largest cost
+  const int ps = (S + NT - 1) / NT, s_lo = min(S, tid * ps), s_hi = min(S, s_lo + ps);
+  int njobs = 0, mx = 0;
+  for (int s = s_lo; s < s_hi; ++s) {
+    const int q0 = a.qstart[s], nq = a.qstart[s + 1] - q0, ctx = a.lens[s];
+    seq[3 * s] = q0;
+    seq[3 * s + 1] = nq;
+    seq[3 * s + 2] = ctx;
+    const int rows = nq * G, n = (rows + rows_g - 1) / rows_g;
+    if (n > 0) mx = max(mx, job_cost(ctx - nq, rows, n - 1, rows_g, G));
+    njobs += n;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+  if ((tid & 63) == 0) tmp[8 + (tid >> 6)] = mx;
+  int J;
+  int j = block_exclusive_scan<NT>(njobs, tmp, J);  // its syncs publish seq and the maxima
+  for (int s = s_lo; s < s_hi; ++s) {
+    joff[s] = j;
+    j += (seq[3 * s + 1] * G + rows_g - 1) / rows_g;
+  }
+  if (tid == 0) joff[S] = J;
+  mx = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) mx = max(mx, tmp[8 + i]);
+  int shift = 0;
+  while ((mx >> shift) >= kRankBuckets) ++shift;
+  __syncthreads();
+  if (rank >= J) return false;  // workgroup-uniform
+  // this thread's jobs [j_lo, j_hi) and the sequence holding j_lo
+  const int pj = (J + NT - 1) / NT, j_lo = min(J, tid * pj), j_hi = min(J, j_lo + pj);
+  int s0 = 0;
+  if (j_lo < j_hi) {
+    int lo = 0, hi = S - 1;  // the last s with joff[s] <= j_lo
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (joff[mid] <= j_lo) lo = mid; else hi = mid - 1;
+    }
+    s0 = lo;
+  }
+  // fn(s, rg, bucket) over this thread's jobs in order; stops when fn is false
+  auto walk = [&](auto&& fn) {
+    int s = s0, first = 0, rows = 0, end = 0, rg = 0;
+    for (int jj = j_lo; jj < j_hi; ++jj, ++rg) {
+      if (jj == j_lo || jj == end) {
+        while (joff[s + 1] <= jj) ++s;
+        rg = jj - joff[s];
+        end = joff[s + 1];
+        rows = seq[3 * s + 1] * G;
+        first = seq[3 * s + 2] - seq[3 * s + 1];
+      }
+      if (!fn(s, rg, job_cost(first, rows, rg, rows_g, G) >> shift)) return;
+    }
+  };
+  walk([&](int, int, int b) {
+    atomicAdd(&hist[b], 1);
+    return true;
+  });
+  __syncthreads();
+  // thread t owns buckets kRankBuckets-1-2t and kRankBuckets-2-2t (descending)
+  const int b0 = kRankBuckets - 1 - 2 * tid, h0 = hist[b0], h1 = hist[b0 - 1];
+  int total;
+  const int above = block_exclusive_scan<NT>(h0 + h1, tmp, total);
+  if (rank >= above && rank < above + h0) {
+    tmp[8] = b0;
+    tmp[9] = rank - above;
+  } else if (rank >= above + h0 && rank < above + h0 + h1) {
+    tmp[8] = b0 - 1;
+    tmp[9] = rank - above - h0;
+  }
+  __syncthreads();
+  const int bucket = tmp[8], off = tmp[9];
+  // the off-th job of that bucket in (s, rg) order
+  int cnt = 0;
+  walk([&](int, int, int b) {
+    cnt += b == bucket;
+    return true;
+  });
+  int total2;
+  const int before = block_exclusive_scan<NT>(cnt, tmp, total2);
+  if (off >= before && off < before + cnt) {
+    int k = off - before;
+    walk([&](int s, int rg, int b) {
+      if (b != bucket) return true;
+      if (k-- > 0) return true;
+      tmp[10] = s;
+      tmp[11] = rg;
+      tmp[12] = seq[3 * s];
+      tmp[13] = seq[3 * s + 1];
+      tmp[14] = seq[3 * s + 2];
+      return false;
+    });
+  }
+  __syncthreads();
+  job = PrefillJob{tmp[10], tmp[11], tmp[12], tmp[13], tmp[14]};
+  return true;
+}
+
+// The job of the given rank.  scratch_ints: LDS ints available at scratch (at
+// least kRankBuckets + 16).
+__device__ bool ranked_job(const PrefillArgs& a, int rows_g, int rank, int* scratch, int scratch_ints,
+                           PrefillJob& job) {
+  constexpr int NT = kPrefillWaves * 64;
+  if ((int64_t)kRankBuckets + 17 + 4 * (int64_t)a.num_seqs <= scratch_ints)
+    return ranked_job_staged<NT>(a, rows_g, rank, scratch, job);
+  if (!ranked_job_by_seq(a, rows_g, rank, scratch, job.s, job.rg)) return false;
+  job.q0 = a.qstart[job.s];
+  job.nq = a.qstart[job.s + 1] - job.q0;
+  job.ctx = a.lens[job.s];
+  return true;
+}
+
 enum RowsJob : int { kPrefillJob = 0, kPrefixJob = 1 };
 
 // Query rows against paged keys on the matrix cores, K/V streamed through LDS.
@@ -400,16 +538,16 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
     int rg;
     if constexpr (JOB == kPrefillJob) {
       __syncthreads();  // the ranking scratch aliases the K stage
-      int s;
+      PrefillJob job;
       if (!ranked_job(a, ROWS_G, (int)(blockIdx.x / Hkv) + it * (int)(gridDim.x / Hkv),
-                      reinterpret_cast<int*>(sm_k), s, rg))
+                      reinterpret_cast<int*>(sm_k), K_BYTES / 4, job))
         break;
-      q0 = a.qstart[s];
-      const int nq = a.qstart[s + 1] - q0;
-      rows = nq * G;
-      ctx = a.lens[s];
-      first_pos = ctx - nq;
-      table = a.tables + (int64_t)s * a.max_blocks;
+      rg = job.rg;
+      q0 = job.q0;
+      rows = job.nq * G;
+      ctx = job.ctx;
+      first_pos = ctx - job.nq;
+      table = a.tables + (int64_t)job.s * a.max_blocks;
     } else {
       rg = (int)(gridDim.z - 1 - blockIdx.z) + it * (int)gridDim.z;
       if (rg * ROWS_G >= rows) break;

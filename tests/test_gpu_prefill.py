@@ -161,12 +161,15 @@ def test_largest_block_size_and_long_chunk():
         gu.assert_close(gu.host(_run(g, case, qs, rpw)), ref, "bf16", f"bs 256 rows/wave {rpw}")
 
 
-def test_many_short_sequences():
-    """600 sequences (more than a workgroup has threads, so each thread of the
-    job ranking walks several sequences), zero-length chunks among them."""
+@pytest.mark.parametrize("num_seqs", [600, 900])
+def test_many_short_sequences(num_seqs):
+    """Hundreds of sequences, zero-length chunks among them.  At head dim 64
+    the job ranking holds up to 763 sequences' lengths in LDS: 600 takes that
+    path (each thread of the ranking owns a run of the sequences), 900 the
+    one that reads the lengths from global memory in every pass."""
     rng = np.random.default_rng(71)
-    pre = [int(x) for x in rng.integers(0, 200, 600)]
-    chk = [int(x) for x in rng.integers(0, 13, 600)]
+    pre = [int(x) for x in rng.integers(0, 200, num_seqs)]
+    chk = [int(x) for x in rng.integers(0, 13, num_seqs)]
     case = workloads.build_prefill_case("many", seed=71, prefix_lens=pre, chunk_lens=chk,
                                         num_q_heads=8, num_kv_heads=2, head_dim=64,
                                         block_size=16, cache_dtype="bf16", std=0.5,
@@ -174,7 +177,7 @@ def test_many_short_sequences():
     g = gu.GpuCase(case)
     qs = gu.dev(case.query_start)
     ref = _oracle(case, case.key_cache, case.value_cache)
-    gu.assert_close(gu.host(_run(g, case, qs)), ref, "bf16", "600 sequences")
+    gu.assert_close(gu.host(_run(g, case, qs)), ref, "bf16", f"{num_seqs} sequences")
 
 
 @pytest.mark.parametrize("scale", [-0.9 / math.sqrt(128), 0.0])
