@@ -379,6 +379,7 @@ pkv_status paged_attention_prefill(pkv_tensor* out, const pkv_tensor* q,
   a.max_query_len = max_query_len;
   a.rows_per_wave = rpw;
   a.cache_dtype = ct;
+  a.workgroups = device_cus();
   const double log2e = 1.4426950408889634;
   const double kscale = ct == PKV_FP8_E4M3 ? (double)key_cache->scale : 1.0;
   a.qk_scale = (float)((double)scale * log2e * kscale);

@@ -121,6 +121,7 @@ struct PrefillArgs {
   int32_t max_query_len;  // sizes the grid only; longer chunks are covered by a stride loop
   int32_t rows_per_wave;  // 16, 32 or 64 (query, head) rows per wavefront
   int32_t cache_dtype;
+  int32_t workgroups;     // at most this many workgroups (one per compute unit)
   float qk_scale;         // scale * log2(e) (* k scale for E4M3)
   float v_scale;
 };

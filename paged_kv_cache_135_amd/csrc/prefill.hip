@@ -29,8 +29,11 @@
 //   context are zeroed in the staging.  Tiles are visited in increasing order,
 //   so key 0 (visible to every row) comes first and every running max is
 //   finite from the first tile on.
-// * Workgroups take (sequence, row group) jobs longest first (ranked_job), so
-//   the long rows of sequences with long cached prefixes do not start last.
+// * One workgroup per compute unit takes (sequence, row group, KV head) jobs
+//   longest first, in snake order over the rounds (round_item), so the long
+//   rows of sequences with long cached prefixes do not start last and short
+//   jobs fill in behind them; one ranking in LDS plans several rounds
+//   (plan_jobs).
 // * Each row's result is finalised in place: no workspace, no second kernel.
 // * The same machinery serves the shared-prefix part of a cascade decode
 //   (shared_prefix_kernel): all sequences' query heads against one prefix,
@@ -264,8 +267,9 @@ __device__ int block_exclusive_scan(int v, int* scratch, int& total) {
 constexpr int kRankBuckets = 2 * kPrefillWaves * 64;
 
 struct PrefillJob {
-  int s, rg;        // sequence, row group
+  int s, rg;        // sequence (-1: none), row group
   int q0, nq, ctx;  // its first query token, query count and context length
+  int hk;           // KV head
 };
 
 __device__ __forceinline__ int job_cost(int first, int rows, int rg, int rows_g, int G) {
@@ -348,20 +352,37 @@ __device__ bool ranked_job_by_seq(const PrefillArgs& a, int rows_g, int rank, in
   return true;
 }
 
-// The ranking for batches whose sequence table fits the scratch: the
-// sequences' lengths are read from global memory once, into LDS with each
-// sequence's first job index, and the passes split the flat job list evenly
-// over the threads (a batch of a few long chunks has many row groups per
-// sequence; one thread per sequence would walk them alone).  Same order as
-// ranked_job_by_seq.  false: no job of that rank.  scratch: kRankBuckets + 16
-// + 4 * num_seqs + 1 ints of LDS.
+// Item i of the prefill grid: the job of rank i / Hkv on KV head i % Hkv.  Of
+// W workgroups, workgroup w takes item it * W + w in even rounds it and
+// (it + 1) * W - 1 - w in odd ones (snake order), so the one that drew the
+// shortest job of a round draws the longest of the next.  Items only grow
+// from round to round.
+__device__ __forceinline__ int64_t round_item(int it) {
+  const int64_t W = gridDim.x;
+  return (it & 1) ? (int64_t)(it + 1) * W - 1 - blockIdx.x : (int64_t)it * W + blockIdx.x;
+}
+
+// Rounds ranked together: one ranking serves this many of a workgroup's jobs.
+constexpr int kPlanRounds = 4;
+
+// This workgroup's jobs of rounds it0 .. it0 + kPlanRounds - 1 into jobs[]
+// (LDS; s = -1: no job), for batches whose sequence table fits the scratch.
+// The sequences' lengths are read from global memory once, into LDS with each
+// sequence's first job index; the passes split the flat job list evenly over
+// the threads (a batch of a few long chunks has many row groups per sequence;
+// one thread per sequence would walk them alone).  Up to one job per thread,
+// every job's rank is counted directly against the others' buckets; beyond
+// that the counting sort finds each round's rank.  Same order as
+// ranked_job_by_seq.  scratch: kRankBuckets + 16 + 4 * num_seqs + 1 + NT
+// ints of LDS.
 template <int NT>
-__device__ bool ranked_job_staged(const PrefillArgs& a, int rows_g, int rank, int* scratch, PrefillJob& job) {
-  const int S = a.num_seqs, G = a.group, tid = threadIdx.x;
+__device__ void plan_staged(const PrefillArgs& a, int rows_g, int it0, int* scratch, PrefillJob* jobs) {
+  const int S = a.num_seqs, G = a.group, Hkv = a.num_kv_heads, tid = threadIdx.x;
   int* hist = scratch;
   int* tmp = scratch + kRankBuckets;  // [0, 8): scans, [8, 16): maxima, then results
   int* seq = tmp + 16;                // q0, nq, ctx of sequence s at 3 s
   int* joff = seq + 3 * S;            // first job index of sequence s; joff[S]: job count
+  int* ord = joff + S + 1;            // job index of each rank (one job per thread)
   for (int i = tid; i < kRankBuckets; i += NT) hist[i] = 0;
   // pass 1: per-sequence data, job counts and the largest cost
   const int ps = (S + NT - 1) / NT, s_lo = min(S, tid * ps), s_hi = min(S, s_lo + ps);
@@ -391,18 +412,66 @@ __device__ bool ranked_job_staged(const PrefillArgs& a, int rows_g, int rank, in
   int shift = 0;
   while ((mx >> shift) >= kRankBuckets) ++shift;
   __syncthreads();
-  if (rank >= J) return false;  // workgroup-uniform
-  // this thread's jobs [j_lo, j_hi) and the sequence holding j_lo
-  const int pj = (J + NT - 1) / NT, j_lo = min(J, tid * pj), j_hi = min(J, j_lo + pj);
-  int s0 = 0;
-  if (j_lo < j_hi) {
-    int lo = 0, hi = S - 1;  // the last s with joff[s] <= j_lo
+  // the last s with joff[s] <= j (j < J)
+  auto seq_of = [&](int jj) {
+    int lo = 0, hi = S - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (joff[mid] <= j_lo) lo = mid; else hi = mid - 1;
+      if (joff[mid] <= jj) lo = mid; else hi = mid - 1;
     }
-    s0 = lo;
+    return lo;
+  };
+  auto put = [&](int k, int s, int rg, int hk) {
+    jobs[k] = PrefillJob{s, rg, seq[3 * s], seq[3 * s + 1], seq[3 * s + 2], hk};
+  };
+  // rank of round it0 + k (-1: none)
+  auto round_rank = [&](int k) {
+    const int64_t r = round_item(it0 + k) / Hkv;
+    return r < J ? (int)r : -1;
+  };
+
+  if (J <= NT) {
+    // one job per thread: its rank is the number of jobs of a larger bucket,
+    // or of the same bucket and a smaller index
+    int b = 0;
+    if (tid < J) {
+      const int s = seq_of(tid);
+      b = job_cost(seq[3 * s + 2] - seq[3 * s + 1], seq[3 * s + 1] * G, tid - joff[s], rows_g, G) >> shift;
+    }
+    hist[tid] = tid < J ? b : -1;  // -1: no job, below every bucket
+    __syncthreads();
+    if (tid < J) {
+      int r = 0;
+      for (int j0 = 0; j0 < J; j0 += 16) {  // 16 buckets a step, 4 reads in flight
+        int4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const int4*>(hist + j0 + 4 * u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int jj = j0 + 4 * u;
+          r += (v[u].x > b || (v[u].x == b && jj < tid)) + (v[u].y > b || (v[u].y == b && jj + 1 < tid)) +
+               (v[u].z > b || (v[u].z == b && jj + 2 < tid)) + (v[u].w > b || (v[u].w == b && jj + 3 < tid));
+        }
+      }
+      ord[r] = tid;
+    }
+    __syncthreads();
+    if (tid < kPlanRounds) {
+      const int r = round_rank(tid);
+      if (r < 0) {
+        jobs[tid].s = -1;
+      } else {
+        const int jj = ord[r], s = seq_of(jj);
+        put(tid, s, jj - joff[s], (int)(round_item(it0 + tid) % Hkv));
+      }
+    }
+    __syncthreads();
+    return;
   }
+
+  // this thread's jobs [j_lo, j_hi) and the sequence holding j_lo
+  const int pj = (J + NT - 1) / NT, j_lo = min(J, tid * pj), j_hi = min(J, j_lo + pj);
+  const int s0 = j_lo < j_hi ? seq_of(j_lo) : 0;
   // fn(s, rg, bucket) over this thread's jobs in order; stops when fn is false
   auto walk = [&](auto&& fn) {
     int s = s0, first = 0, rows = 0, end = 0, rg = 0;
@@ -417,8 +486,8 @@ __device__ bool ranked_job_staged(const PrefillArgs& a, int rows_g, int rank, in
       if (!fn(s, rg, job_cost(first, rows, rg, rows_g, G) >> shift)) return;
     }
   };
-  walk([&](int, int, int b) {
-    atomicAdd(&hist[b], 1);
+  walk([&](int, int, int bk) {
+    atomicAdd(&hist[bk], 1);
     return true;
   });
   __syncthreads();
@@ -426,53 +495,66 @@ __device__ bool ranked_job_staged(const PrefillArgs& a, int rows_g, int rank, in
   const int b0 = kRankBuckets - 1 - 2 * tid, h0 = hist[b0], h1 = hist[b0 - 1];
   int total;
   const int above = block_exclusive_scan<NT>(h0 + h1, tmp, total);
-  if (rank >= above && rank < above + h0) {
-    tmp[8] = b0;
-    tmp[9] = rank - above;
-  } else if (rank >= above + h0 && rank < above + h0 + h1) {
-    tmp[8] = b0 - 1;
-    tmp[9] = rank - above - h0;
-  }
-  __syncthreads();
-  const int bucket = tmp[8], off = tmp[9];
-  // the off-th job of that bucket in (s, rg) order
-  int cnt = 0;
-  walk([&](int, int, int b) {
-    cnt += b == bucket;
-    return true;
-  });
-  int total2;
-  const int before = block_exclusive_scan<NT>(cnt, tmp, total2);
-  if (off >= before && off < before + cnt) {
-    int k = off - before;
-    walk([&](int s, int rg, int b) {
-      if (b != bucket) return true;
-      if (k-- > 0) return true;
-      tmp[10] = s;
-      tmp[11] = rg;
-      tmp[12] = seq[3 * s];
-      tmp[13] = seq[3 * s + 1];
-      tmp[14] = seq[3 * s + 2];
-      return false;
+  for (int k = 0; k < kPlanRounds; ++k) {
+    const int rank = round_rank(k);  // workgroup-uniform
+    if (rank < 0) {
+      if (tid == 0) jobs[k].s = -1;
+      continue;
+    }
+    if (rank >= above && rank < above + h0) {
+      tmp[8] = b0;
+      tmp[9] = rank - above;
+    } else if (rank >= above + h0 && rank < above + h0 + h1) {
+      tmp[8] = b0 - 1;
+      tmp[9] = rank - above - h0;
+    }
+    __syncthreads();
+    const int bucket = tmp[8], off = tmp[9];
+    // the off-th job of that bucket in (s, rg) order
+    int cnt = 0;
+    walk([&](int, int, int bk) {
+      cnt += bk == bucket;
+      return true;
     });
+    int total2;
+    const int before = block_exclusive_scan<NT>(cnt, tmp, total2);  // its first sync: tmp[8, 10) read
+    if (off >= before && off < before + cnt) {
+      int left = off - before;
+      const int hk = (int)(round_item(it0 + k) % Hkv);
+      walk([&](int s, int rg, int bk) {
+        if (bk != bucket) return true;
+        if (left-- > 0) return true;
+        put(k, s, rg, hk);
+        return false;
+      });
+    }
   }
   __syncthreads();
-  job = PrefillJob{tmp[10], tmp[11], tmp[12], tmp[13], tmp[14]};
-  return true;
 }
 
-// The job of the given rank.  scratch_ints: LDS ints available at scratch (at
-// least kRankBuckets + 16).
-__device__ bool ranked_job(const PrefillArgs& a, int rows_g, int rank, int* scratch, int scratch_ints,
-                           PrefillJob& job) {
+// This workgroup's jobs from round it0 on into jobs[] (LDS; s = -1: no job);
+// returns how many rounds were planned.  scratch_ints: LDS ints available at
+// scratch (at least kRankBuckets + 16).
+__device__ int plan_jobs(const PrefillArgs& a, int rows_g, int it0, int* scratch, int scratch_ints,
+                         PrefillJob* jobs) {
   constexpr int NT = kPrefillWaves * 64;
-  if ((int64_t)kRankBuckets + 17 + 4 * (int64_t)a.num_seqs <= scratch_ints)
-    return ranked_job_staged<NT>(a, rows_g, rank, scratch, job);
-  if (!ranked_job_by_seq(a, rows_g, rank, scratch, job.s, job.rg)) return false;
-  job.q0 = a.qstart[job.s];
-  job.nq = a.qstart[job.s + 1] - job.q0;
-  job.ctx = a.lens[job.s];
-  return true;
+  if ((int64_t)kRankBuckets + 17 + 4 * (int64_t)a.num_seqs + NT <= scratch_ints) {
+    plan_staged<NT>(a, rows_g, it0, scratch, jobs);
+    return kPlanRounds;
+  }
+  const int64_t item = round_item(it0), rank = item / a.num_kv_heads;
+  int s = -1, rg = 0;
+  if (rank > 0x7fffffff || !ranked_job_by_seq(a, rows_g, (int)rank, scratch, s, rg)) s = -1;
+  if (threadIdx.x == 0) {
+    if (s < 0) {
+      jobs[0].s = -1;
+    } else {
+      const int q0 = a.qstart[s];
+      jobs[0] = PrefillJob{s, rg, q0, a.qstart[s + 1] - q0, a.lens[s], (int)(item % a.num_kv_heads)};
+    }
+  }
+  __syncthreads();
+  return 1;
 }
 
 enum RowsJob : int { kPrefillJob = 0, kPrefixJob = 1 };
@@ -517,11 +599,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
   __shared__ __attribute__((aligned(16))) char sm_v[V_BYTES];
   static_assert(K_BYTES >= 4 * (kRankBuckets + 16), "ranking scratch");
 
-  // Jobs: prefill: grid x = job slots x KV heads, job of rank x / Hkv (then +
-  // gridDim.x / Hkv while jobs remain); prefix: x = KV head, y = key split,
-  // z = row group, from the last row group down.
-  const int hk = JOB == kPrefillJob ? (int)(blockIdx.x % Hkv) : (int)blockIdx.x;
-  const int64_t head_rows = (int64_t)hk * bs;
+  // Jobs: prefill: items in round_item's order, ranked kPlanRounds rounds at
+  // a time into sm_jobs; prefix: x = KV head, y = key split, z = row group,
+  // from the last row group down.
+  __shared__ PrefillJob sm_jobs[kPlanRounds];
+  int plan0 = 0, planned = 0;  // sm_jobs holds rounds plan0 .. plan0 + planned - 1
+  int hk = JOB == kPrefillJob ? 0 : (int)blockIdx.x;
+  int64_t head_rows = (int64_t)hk * bs;
   int rows = 0, ctx = 0, first_pos = 0, q0 = 0, k_lo = 0, k_hi_all = 0;
   const int32_t* table = nullptr;
   if constexpr (JOB == kPrefixJob) {
@@ -537,11 +621,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
   for (int it = 0;; ++it) {
     int rg;
     if constexpr (JOB == kPrefillJob) {
-      __syncthreads();  // the ranking scratch aliases the K stage
-      PrefillJob job;
-      if (!ranked_job(a, ROWS_G, (int)(blockIdx.x / Hkv) + it * (int)(gridDim.x / Hkv),
-                      reinterpret_cast<int*>(sm_k), K_BYTES / 4, job))
-        break;
+      if (it == plan0 + planned) {
+        __syncthreads();  // the ranking scratch aliases the K stage
+        plan0 = it;
+        planned = plan_jobs(a, ROWS_G, it, reinterpret_cast<int*>(sm_k), K_BYTES / 4, sm_jobs);
+      }
+      const PrefillJob job = sm_jobs[it - plan0];
+      if (job.s < 0) break;  // workgroup-uniform; items only grow from round to round
+      hk = job.hk;
+      head_rows = (int64_t)hk * bs;
       rg = job.rg;
       q0 = job.q0;
       rows = job.nq * G;
@@ -904,13 +992,12 @@ hipError_t launch_prefix_ct(const PrefixArgs& a, hipStream_t stream) {
 template <int CT, int D, int R>
 hipError_t launch_r(const PrefillArgs& a, hipStream_t stream) {
   constexpr int ROWS_G = 16 * R * kPrefillWaves;
-  // job slots for max_query_len-long chunks; any further jobs are taken by
-  // the same workgroups in later rounds
+  // one workgroup per compute unit, fewer if max_query_len-long chunks have
+  // fewer items; every workgroup keeps taking items while jobs remain
   const int64_t per_seq = ((int64_t)a.max_query_len * a.group + ROWS_G - 1) / ROWS_G;
-  int64_t slots = (int64_t)a.num_seqs * (per_seq < 1 ? 1 : per_seq);
-  const int64_t cap = 0x7fffffff / a.num_kv_heads;
-  slots = slots > cap ? cap : slots;
-  const dim3 grid((unsigned)(slots * a.num_kv_heads));
+  const int64_t items = (int64_t)a.num_seqs * (per_seq < 1 ? 1 : per_seq) * a.num_kv_heads;
+  const int64_t cap = a.workgroups > 0 ? a.workgroups : 256;
+  const dim3 grid((unsigned)(items < cap ? items : cap));
   hipLaunchKernelGGL((rows_kernel<CT, D, R, kPrefillJob, PrefillArgs>), grid, dim3(kPrefillWaves * 64), 0,
                      stream, a);
   return hipGetLastError();

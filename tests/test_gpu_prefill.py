@@ -164,8 +164,9 @@ def test_largest_block_size_and_long_chunk():
 @pytest.mark.parametrize("num_seqs", [600, 900])
 def test_many_short_sequences(num_seqs):
     """Hundreds of sequences, zero-length chunks among them.  At head dim 64
-    the job ranking holds up to 763 sequences' lengths in LDS: 600 takes that
-    path (each thread of the ranking owns a run of the sequences), 900 the
+    the job ranking holds up to 635 sequences' lengths in LDS: 600 takes that
+    path (each thread of the ranking owns a run of the sequences, and with
+    more jobs than threads the counting sort finds each round's job), 900 the
     one that reads the lengths from global memory in every pass."""
     rng = np.random.default_rng(71)
     pre = [int(x) for x in rng.integers(0, 200, num_seqs)]
