@@ -62,7 +62,8 @@ def parse():
                         "no block), cached, or auto = stream exactly when the tables share none")
     p.add_argument("--step", default="auto", choices=["auto", "append", "split"],
                    help="append: one call per step; split: KV write then decode; auto: append "
-                        "when the step writes one token per sequence at position len-1")
+                        "when the step writes one token per sequence at position len-1 "
+                        "(split with --shared-prefix)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (scales PMC byte counters)")
     return p.parse_args()
@@ -127,6 +128,33 @@ def read_ceiling(stream, gib: int = 2, reps: int = 20) -> dict:
     del buf
     return {"value": round((gib << 30) / s / 1e9, 1), "unit": "GB/s", "bytes": gib << 30,
             "kernel": "read_probe_kernel (one pass, 16-byte non-temporal loads)"}
+
+
+def read_ceiling_same_size(stream, nbytes: int, regions: int = 4, reps: int = 20) -> dict:
+    """The read probe over as many bytes as the measured kernel reads per
+    launch, rotating over `regions` buffers of that size (as the bench rotates
+    layer pools) so that no pass finds its data in the last-level cache: the
+    streaming-read rate a launch of that size can reach, start-up and drain
+    included."""
+    import torch
+
+    import paged_kv_cache_135_amd as pkv
+    n = (int(nbytes) + 15) // 16 * 16
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(regions)]
+    sink = pkv.read_probe(bufs[0], stream=stream)
+    for b in bufs:
+        pkv.read_probe(b, sink, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        pkv.read_probe(bufs[i % regions], sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / reps
+    del bufs
+    return {"value": round(n / s / 1e9, 1), "unit": "GB/s", "bytes": n, "regions": regions,
+            "us_per_pass": round(s * 1e6, 2)}
 
 
 def _oracle_steps(case, seconds):
@@ -478,10 +506,13 @@ def main():
             print("--shared-prefix needs a workload with shared prefix blocks (c3)", file=sys.stderr)
             return 2
         prefix_len = case.shared_blocks * case.block_size
-        step = "split"  # the shared-prefix decode takes no appended tokens
     if step == "auto":
         step = "split"
-        if case.slot_mapping.shape[0] == case.num_seqs:
+        # one call per step when every new token is its sequence's last position.
+        # Not for a shared prefix: there the tails' launch with the write folded
+        # in is as much slower as the write launch it saves (115.2 vs 114.8 us
+        # per step on the 256-sequence batch); --step append selects it.
+        if case.slot_mapping.shape[0] == case.num_seqs and not prefix_len:
             try:
                 pkv.validate_append_slots(case.slot_mapping, case.block_tables, case.context_lens,
                                           case.key_cache.shape[0], case.block_size)
@@ -505,6 +536,7 @@ def main():
     def decode_launch(kc, vc, defer):
         if prefix_len:  # its kernels launch together: time the whole call
             return pkv.DecodeLaunch(out, q, kc, vc, tables, lens, case.scale, case.block_size,
+                                    append=(knew, vnew, slots) if append else None,
                                     prefix_len=prefix_len, **dkw)
         return pkv.DecodeLaunch(out, q, kc, vc, tables, lens, case.scale, case.block_size,
                                 append=(knew, vnew, slots) if append else None,
@@ -601,6 +633,8 @@ def main():
     # HBM roofline: bytes that must come from memory; a shared prefix counts once
     roof_bytes = case.unique_kv_bytes() if case.shared_blocks else kv
     achieved = roof_bytes / main_s / 1e9
+    same = read_ceiling_same_size(stream, roof_bytes)
+    ceiling["same_size"] = dict(same, frac_of_ceiling=round(achieved / same["value"], 4))
     print(f"[bench] step {step}: streaming kernel {main_s*1e6:.1f} us per launch back to back "
           f"({main_ms.mean()*1e3:.1f} us between events around each, p10 "
           f"{np.percentile(main_ms,10)*1e3:.1f}, p90 {np.percentile(main_ms,90)*1e3:.1f}), "

@@ -32,6 +32,8 @@
  *                           token per sequence.
  *   paged_attention_decode_shared_prefix   decode for sequences that share a
  *                           prefix: the shared part computed once (cascade).
+ *   paged_attention_decode_shared_prefix_append   the same with each
+ *                           sequence's new token written in the tails' launch.
  *   paged_attention_prefill chunked prefill: many new query tokens per
  *                           sequence, causal, the cached prefix read through
  *                           the block table.
@@ -78,7 +80,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 7
+#define PKV_ABI_VERSION 8
 #define PKV_MAX_DIMS 4
 
 typedef enum {
@@ -290,6 +292,31 @@ pkv_status paged_attention_decode_append(pkv_tensor* out, const pkv_tensor* q,
                                          const pkv_tensor* context_lens, float scale,
                                          int32_t block_size, const pkv_decode_opts* opts,
                                          void* hip_stream);
+
+/*
+ * One decode step for sequences that share a prefix, in one call: each
+ * sequence's new token is written by the launch that attends its tail
+ * (paged_attention_decode_append's folding), and the shared part is computed
+ * once (paged_attention_decode_shared_prefix).  Same sources as the two.  The
+ * new token is private to its sequence: a block shared by several sequences
+ * is copied before it is written (paged_kv_copy_blocks), so the token lies in
+ * the tail.
+ *   k, v, slot_mapping  as paged_attention_decode_append
+ *   prefix_len, the rest  as paged_attention_decode_shared_prefix, and every
+ *                 context_len > prefix_len (a sequence whose new token would
+ *                 fall inside the prefix gets an undefined result)
+ * Result: the same cache bytes and, bit for bit, the same `out` as
+ * paged_kv_write(k, v, slot_mapping, ...) followed by
+ * paged_attention_decode_shared_prefix with the same options, under the slot
+ * conditions of paged_attention_decode_append (pkv_validate_append_slots).
+ * Errors: as paged_attention_decode_shared_prefix, and those of
+ * paged_attention_decode_append for k, v and slot_mapping.
+ */
+pkv_status paged_attention_decode_shared_prefix_append(
+    pkv_tensor* out, const pkv_tensor* q, const pkv_tensor* k, const pkv_tensor* v,
+    const pkv_tensor* slot_mapping, pkv_tensor* key_cache, pkv_tensor* value_cache,
+    const pkv_tensor* block_tables, const pkv_tensor* context_lens, int32_t prefix_len, float scale,
+    int32_t block_size, const pkv_decode_opts* opts, void* hip_stream);
 
 typedef struct {
   int32_t rows_per_wave;  /* (query token, query head) rows per wavefront: 0 = library

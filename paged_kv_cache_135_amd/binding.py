@@ -28,9 +28,9 @@ EXPORTED = (
     "pkv_validate_block_pairs", "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
     "pkv_validate_block_ids", "paged_attention_decode_shared_prefix",
     "paged_attention_decode_shared_prefix_workspace_bytes", "pkv_validate_shared_prefix",
-    "pkv_read_probe_blocks", "pkv_read_probe",
+    "pkv_read_probe_blocks", "pkv_read_probe", "paged_attention_decode_shared_prefix_append",
 )
-ABI_VERSION = 7
+ABI_VERSION = 8
 DECODE_DEFER_MERGE = 1
 DECODE_STREAM_KV = 2
 
@@ -154,6 +154,9 @@ def load():
                                                          ctypes.c_float, ctypes.c_int32,
                                                          ctypes.POINTER(PkvDecodeOpts), P]
     lib.paged_attention_decode_shared_prefix.restype = ctypes.c_int
+    lib.paged_attention_decode_shared_prefix_append.argtypes = [T] * 9 + [
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.POINTER(PkvDecodeOpts), P]
+    lib.paged_attention_decode_shared_prefix_append.restype = ctypes.c_int
     lib.paged_attention_decode_shared_prefix_workspace_bytes.argtypes = [ctypes.c_int32] * 7 + [
         ctypes.POINTER(PkvDecodeOpts)]
     lib.paged_attention_decode_shared_prefix_workspace_bytes.restype = ctypes.c_size_t
@@ -336,6 +339,30 @@ def paged_attention_decode_shared_prefix(out, q, key_cache, value_cache, block_t
     d = [describe(out), describe(q), describe(key_cache, k_scale), describe(value_cache, v_scale),
          describe(block_tables), describe(context_lens)]
     _check(load().paged_attention_decode_shared_prefix(
+        *[ctypes.byref(x) for x in d], int(prefix_len), float(scale), int(block_size),
+        ctypes.byref(opts), _stream(q, stream)))
+    if ws is not None and workspace is None and stream is not None:
+        ws.record_stream(stream)
+    return out
+
+
+def paged_attention_decode_shared_prefix_append(out, q, k, v, slot_mapping, key_cache,
+                                                value_cache, block_tables, context_lens,
+                                                prefix_len: int, scale: float, block_size: int, *,
+                                                k_scale: float = 1.0, v_scale: float = 1.0,
+                                                num_workers: int = 0, workspace=None,
+                                                stream_kv: bool = False, stream=None):
+    """One shared-prefix decode step in one call: write each sequence's new
+    token (k, v [S, Hkv, D] at slot_mapping [S], inside its own tail) and
+    attend as paged_attention_decode_shared_prefix (see include/pagedkv.h).
+    Every context_lens[s] must exceed prefix_len."""
+    _same_device(out, q, k, v, slot_mapping, key_cache, value_cache, block_tables, context_lens)
+    opts = decode_opts("auto", 0, 0, num_workers, stream_kv=stream_kv)
+    ws = _workspace_for(opts, q, key_cache, block_tables, block_size, workspace, prefix_len)
+    d = [describe(out), describe(q), describe(k), describe(v), describe(slot_mapping),
+         describe(key_cache, k_scale), describe(value_cache, v_scale), describe(block_tables),
+         describe(context_lens)]
+    _check(load().paged_attention_decode_shared_prefix_append(
         *[ctypes.byref(x) for x in d], int(prefix_len), float(scale), int(block_size),
         ctypes.byref(opts), _stream(q, stream)))
     if ws is not None and workspace is None and stream is not None:
@@ -573,7 +600,8 @@ class DecodeLaunch:
     """A decode call with descriptors, options and workspace prepared once.
 
     append=(k, v, slot_mapping) makes it the one-call decode step
-    (paged_attention_decode_append).  defer_merge=True launches only the
+    (paged_attention_decode_append; with prefix_len,
+    paged_attention_decode_shared_prefix_append).  defer_merge=True launches only the
     streaming kernel; call merge() next on the same stream.  stream_kv: see
     decode_opts."""
 
@@ -583,8 +611,8 @@ class DecodeLaunch:
                  num_workers: int = 0, workspace=None, append=None, defer_merge: bool = False,
                  prefix_len: int = 0, stream_kv: bool = False):
         _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
-        if prefix_len and (append is not None or defer_merge):
-            raise ValueError("a shared-prefix decode takes no appended tokens and no deferred merge")
+        if prefix_len and defer_merge:
+            raise ValueError("a shared-prefix decode takes no deferred merge")
         if prefix_len and mode is None:
             mode = "auto"
         self._opts = decode_opts(mode, partition_size, waves_per_group, num_workers, defer_merge,
@@ -617,7 +645,11 @@ class DecodeLaunch:
         return ctypes.c_void_p(s.cuda_stream)
 
     def __call__(self, stream=None):
-        if self._prefix:
+        if self._prefix and self._app_refs is not None:
+            _check(self._lib.paged_attention_decode_shared_prefix_append(
+                *self._app_refs, self._prefix, self._scale, self._bs, ctypes.byref(self._opts),
+                self._s(stream)))
+        elif self._prefix:
             _check(self._lib.paged_attention_decode_shared_prefix(
                 *self._refs, self._prefix, self._scale, self._bs, ctypes.byref(self._opts),
                 self._s(stream)))

@@ -790,6 +790,22 @@ pkv_status paged_attention_decode_append(pkv_tensor* out, const pkv_tensor* q, c
                      context_lens, scale, block_size, opts, &app, phase_of(opts), hip_stream);
 }
 
+pkv_status paged_attention_decode_shared_prefix_append(
+    pkv_tensor* out, const pkv_tensor* q, const pkv_tensor* k, const pkv_tensor* v,
+    const pkv_tensor* slot_mapping, pkv_tensor* key_cache, pkv_tensor* value_cache,
+    const pkv_tensor* block_tables, const pkv_tensor* context_lens, int32_t prefix_len, float scale,
+    int32_t block_size, const pkv_decode_opts* opts, void* hip_stream) {
+  if (!k || !v || !slot_mapping) return fail(PKV_ERR_NULL, "k, v and slot_mapping must not be NULL");
+  if (prefix_len <= 0) return fail(PKV_ERR_SHAPE, "prefix_len must be positive");
+  if (opts && (opts->flags & PKV_DECODE_DEFER_MERGE))
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode launches its kernels together: "
+                                     "PKV_DECODE_DEFER_MERGE is not supported");
+  const AppendIn app{k, v, slot_mapping};
+  return decode_impl("paged_attention_decode_shared_prefix_append", out, q, key_cache, value_cache,
+                     block_tables, context_lens, scale, block_size, opts, &app, phase_of(opts),
+                     hip_stream, prefix_len);
+}
+
 pkv_status pkv_validate_slots(const int32_t* slots, int64_t num_tokens, int64_t num_blocks,
                               int32_t block_size) {
   if (num_tokens < 0 || num_blocks < 0 || block_size <= 0)

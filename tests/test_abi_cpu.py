@@ -404,6 +404,26 @@ def test_shared_prefix_workspace_and_refusals():
     assert call(16, None) == 6                     # needs a workspace
 
 
+def test_shared_prefix_append_refusals():
+    lib = B.load()
+    a = _decode_args()
+    k, v, s = _new_rows()
+    ref = lambda d: ctypes.byref(d) if d is not None else None
+    call = lambda kk, plen, opts: lib.paged_attention_decode_shared_prefix_append(
+        ref(a["out"]), ref(a["q"]), ref(kk), ref(v), ref(s), ref(a["kc"]), ref(a["vc"]),
+        ref(a["tables"]), ref(a["lens"]), plen, 0.1, 16, ref(opts), None)
+    assert call(None, 16, None) == 1               # no new rows
+    assert call(k, 0, None) == 3                   # no prefix
+    assert call(k, 8, None) == 3                   # not a multiple of the block size
+    d = _opts(mode=2)
+    d.flags = B.DECODE_DEFER_MERGE
+    assert call(k, 16, d) == 5
+    bad_k, _, _ = _new_rows(D=64)
+    assert call(bad_k, 16, None) == 3              # new rows of another head dim
+    assert call(k, 16, None) == 6                  # needs a workspace
+    assert B.load().pkv_last_error()
+
+
 def test_shared_prefix_validator():
     tables = np.array([[4, 2, 7], [4, 2, 1], [4, 2, 9]], np.int32)
     lens = np.array([40, 33, 32], np.int32)

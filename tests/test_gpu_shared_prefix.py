@@ -3,7 +3,8 @@
 The oracle knows nothing of the sharing: it decodes every sequence over its
 whole context.  Covered: every element type, both head dims, several group
 sizes and block sizes, tails of 0, 1 and many tokens, few and many workers,
-determinism, and the full 256-sequence shared-prefix batch."""
+determinism, the full 256-sequence shared-prefix batch, and the one-call
+step that writes each sequence's new token in the tails' launch."""
 import math
 
 import numpy as np
@@ -103,3 +104,48 @@ def test_stream_kv_hint_on_the_tails_is_bit_identical():
                                              case.scale, case.block_size, k_scale=case.k_scale,
                                              v_scale=case.v_scale, stream_kv=True)
     assert np.array_equal(a, gu.host(out))
+
+
+def _bits(t) -> np.ndarray:
+    """Device tensor -> host bit patterns (NaN poison compares equal to itself)."""
+    a = gu.host(t)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+@pytest.mark.parametrize("name", ["g4_d128_bf16", "g7_d128_bs32_bf16", "g2_d64_f32", "g4_d128_e4m3"])
+def test_append_step_equals_write_then_cascade(name):
+    """paged_attention_decode_shared_prefix_append against the step's KV write
+    followed by the cascade decode: the same cache bytes and, bit for bit, the
+    same output; and the oracle's result.  Every sequence's new token is its
+    last position, which lies in its own tail (tails of 0 tokens get one more
+    here, so the token is never inside the shared prefix)."""
+    tails, nsh, Hq, Hkv, D, bs, dt = CASES[name]
+    lens = [nsh * bs + max(t, 1) for t in tails]
+    case = workloads.build_case(name + "_append", seed=23, context_lens=lens, num_q_heads=Hq,
+                                num_kv_heads=Hkv, head_dim=D, block_size=bs, cache_dtype=dt,
+                                std=0.5 if dt != "f32" else 1.0, scale=1.0 / math.sqrt(D),
+                                shared_prefix_blocks=nsh)
+    prefix = nsh * bs
+    pkv.validate_shared_prefix(case.block_tables, case.context_lens, case.num_blocks, bs, prefix)
+    assert case.slot_mapping.shape == (case.num_seqs,)  # one new token per sequence
+    pkv.validate_append_slots(case.slot_mapping, case.block_tables, case.context_lens,
+                              case.key_cache.shape[0], bs)
+    # path A: the pool with the step's write, then the cascade
+    ga = gu.GpuCase(case)
+    ga.fill_and_step_writes()
+    out_a = _run(ga, case, prefix)
+    # path B: the pool before the step's write, then the one-call step
+    gb = gu.GpuCase(case)
+    if case.fill_k is not None:
+        gb.write(case.fill_k, case.fill_v, case.fill_slots)
+    out_b = torch.empty_like(gb.q)
+    pkv.paged_attention_decode_shared_prefix_append(
+        out_b, gb.q, gu.dev(case.k_new), gu.dev(case.v_new), gu.dev(case.slot_mapping), gb.kc,
+        gb.vc, gb.tables, gb.lens, prefix, case.scale, bs, k_scale=case.k_scale,
+        v_scale=case.v_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(ga.kc), _bits(gb.kc)), "key pools differ"
+    assert np.array_equal(_bits(ga.vc), _bits(gb.vc)), "value pools differ"
+    assert np.array_equal(_bits(out_a), _bits(out_b)), "append step != write + cascade"
+    kc, vc = gu.oracle_caches(case)
+    gu.assert_close(gu.host(out_b), gu.oracle_decode(case, kc, vc), dt, name + " append step")
