@@ -181,6 +181,24 @@ def test_many_short_sequences(num_seqs):
     gu.assert_close(gu.host(_run(g, case, qs)), ref, "bf16", f"{num_seqs} sequences")
 
 
+def test_more_rounds_than_one_plan_covers():
+    """400 one-job sequences on 4 KV heads: 1,600 items, seven rounds of a
+    256-workgroup grid.  Each ranking plans four rounds, so every workgroup
+    ranks again mid-kernel; with at most 512 jobs the ranks are counted
+    directly.  Chunks of 1..20 tokens over prefixes of 0..300 tokens."""
+    rng = np.random.default_rng(83)
+    pre = [int(x) for x in rng.integers(0, 301, 400)]
+    chk = [int(x) for x in rng.integers(1, 21, 400)]
+    case = workloads.build_prefill_case("rounds", seed=83, prefix_lens=pre, chunk_lens=chk,
+                                        num_q_heads=16, num_kv_heads=4, head_dim=128,
+                                        block_size=16, cache_dtype="bf16", std=0.5,
+                                        scale=1.0 / math.sqrt(128))
+    g = gu.GpuCase(case)
+    qs = gu.dev(case.query_start)
+    ref = _oracle(case, case.key_cache, case.value_cache)
+    gu.assert_close(gu.host(_run(g, case, qs)), ref, "bf16", "400 sequences x 4 KV heads")
+
+
 @pytest.mark.parametrize("scale", [-0.9 / math.sqrt(128), 0.0])
 def test_negative_and_zero_scale(scale):
     """The kernel folds a positive factor into the exponent: a negative scale
