@@ -83,9 +83,10 @@ def build_workload(name):
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch of the dominant decode kernel from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE summary for this workload, or None when the
-    kernel source changed since the counters were taken."""
+    """HBM bytes per launch of the measured decode kernel(s) from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary whose title names exactly this
+    workload key ("<case>" or "<case>+cascade"), or None when the kernel
+    sources changed since the counters were taken."""
     import glob
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
@@ -102,7 +103,9 @@ def measured_traffic(workload: str):
                 if ":" in line:
                     k, v = line.split(":", 1)
                     fields[k.strip()] = v.strip()
-        if workload in first and fields.get("decode.hip+tile.h sha256") == sha:
+        key = first.split(":", 1)[-1].strip()
+        key = key[:-len(" decode step")] if key.endswith(" decode step") else key
+        if key == workload and fields.get("decode.hip+tile.h sha256") == sha:
             return int(fields["traffic_bytes_per_launch"]), fields.get("kernel", "")
     return None, None
 
@@ -627,7 +630,7 @@ def main():
     main_s = e0.elapsed_time(e1) / 1e3 / K
 
     kv = case.kv_bytes()
-    traffic, traffic_kernel = measured_traffic(case.name)
+    traffic, traffic_kernel = measured_traffic(case.name + ("+cascade" if prefix_len else ""))
     ceiling = read_ceiling(stream)
     value = kv / (ms_per_step / 1e3) / 1e9
     # HBM roofline: bytes that must come from memory; a shared prefix counts once
