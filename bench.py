@@ -82,15 +82,16 @@ def build_workload(name):
     return workloads.c5_fp8()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, root: str | None = None):
     """HBM bytes per launch of the measured decode kernel(s) from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary whose title names exactly this
     workload key ("<case>" or "<case>+cascade"), or None when the kernel
-    sources changed since the counters were taken."""
+    sources changed since the counters were taken.  root: the directory with
+    profiles/ (default: this file's)."""
     import glob
     import hashlib
-    here = os.path.dirname(os.path.abspath(__file__))
-    csrc = os.path.join(here, "paged_kv_cache_135_amd", "csrc")
+    here = root or os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_135_amd", "csrc")
     h = hashlib.sha256()
     for name in ("decode.hip", "tile.h"):  # the decode kernels' sources
         h.update(open(os.path.join(csrc, name), "rb").read())
