@@ -90,11 +90,11 @@ def test_single_token_contexts_return_the_value_row_exactly():
 
 
 # ------------------------------------------------------------ full sizes
-def _full(name, builder, mode, row_mask=None, tokens_mask_fn=None):
+def _full(name, builder, mode, row_mask=None, tokens_mask_fn=None, stream_kv=False):
     case = builder()
     g = gu.GpuCase(case)
     g.fill_and_step_writes()
-    got = gu.host(g.decode_mode(mode))
+    got = gu.host(g.decode_mode(mode, stream_kv=stream_kv))
     tm = tokens_mask_fn(case) if tokens_mask_fn else None
     kc, vc = gu.oracle_caches(case, tokens_mask=tm)
     rm = row_mask(case) if row_mask else None
@@ -123,20 +123,24 @@ def test_c3_shared_prefix_full(mode):
     gu.assert_close(got, ref, "bf16", "c3")
 
 
-@pytest.mark.parametrize("bs", [16, 32])
-def test_c4_long_context_sampled_rows(bs):
+# the split-K partitions the long-context workload is specified with, the
+# balanced split, and auto mode with streaming reads (what bench.py times)
+@pytest.mark.parametrize("bs,mode,stream", [(16, ("partitioned", 512, 4, 0), False),
+                                            (16, ("auto", 0, 0, 0), True),
+                                            (32, ("balanced", 0, 0, 0), False)])
+def test_c4_long_context_sampled_rows(bs, mode, stream):
     def rows(case):
         m = np.zeros((case.num_seqs, case.num_q_heads), bool)
         m[[0, case.num_seqs - 1], :] = True
         return m
-    mode = ("partitioned", 512, 4, 0) if bs == 16 else ("balanced", 0, 0, 0)
     case, got, ref, rm = _full(f"c4_bs{bs}", lambda: workloads.c4_long_context(block_size=bs),
-                               mode, row_mask=rows)
-    gu.assert_close(got, ref, "bf16", f"c4 bs{bs}", mask=rm)
+                               mode, row_mask=rows, stream_kv=stream)
+    gu.assert_close(got, ref, "bf16", f"c4 bs{bs} {_mid(mode)}", mask=rm)
     assert np.all(np.isfinite(gu.as_f64(got)))
 
 
-def test_c5_e4m3_sampled_rows():
+@pytest.mark.parametrize("mode,stream", [(("balanced", 0, 0, 0), False), (("auto", 0, 0, 0), True)])
+def test_c5_e4m3_sampled_rows(mode, stream):
     rng = np.random.default_rng(5)
     pick = np.sort(rng.choice(512, size=32, replace=False))
 
@@ -151,9 +155,9 @@ def test_c5_e4m3_sampled_rows():
         m = np.zeros((case.num_seqs, case.num_q_heads), bool)
         m[pick, :] = True
         return m
-    case, got, ref, rm = _full("c5", workloads.c5_fp8, ("balanced", 0, 0, 0), row_mask=rows,
-                               tokens_mask_fn=tokens)
-    gu.assert_close(got, ref, "fp8_e4m3", "c5", mask=rm)
+    case, got, ref, rm = _full("c5", workloads.c5_fp8, mode, row_mask=rows, tokens_mask_fn=tokens,
+                               stream_kv=stream)
+    gu.assert_close(got, ref, "fp8_e4m3", f"c5 {_mid(mode)}", mask=rm)
 
 
 def test_many_sequences_take_the_long_scan_path():
