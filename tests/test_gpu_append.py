@@ -168,6 +168,23 @@ def test_append_full_qwen_batch_matches_two_launches():
     assert torch.equal(g1.vc.view(torch.int16), g2.vc.view(torch.int16))
 
 
+def test_bench_step_configuration_matches_the_oracle():
+    """The Qwen-shaped step exactly as bench.py times it (one call, auto mode,
+    streaming reads) against the oracle: the pools bit-exact, the output
+    within the bf16 tolerance."""
+    case = workloads.c2_qwen_decode()
+    k, v, slots = _rows_per_sequence(case)
+    okc, ovc, ref = _oracle(case, k, v, slots)
+    g = _pre_step(case)
+    out = torch.empty_like(g.q)
+    pkv.paged_attention_decode_append(out, g.q, gu.dev(k), gu.dev(v), gu.dev(slots), g.kc, g.vc,
+                                      g.tables, g.lens, case.scale, case.block_size, mode="auto",
+                                      stream_kv=True)
+    torch.cuda.synchronize()
+    assert _same_pools(g, okc, ovc)
+    gu.assert_close(gu.host(out), ref, "bf16", "c2 bench step")
+
+
 @pytest.mark.parametrize("mode", [("balanced", 0, 0, 0), ("balanced", 0, 0, 3),
                                   ("partitioned", 64, 2, 0), ("single", 0, 4, 0)], ids=_mid)
 def test_deferred_merge_is_bit_identical(mode):
