@@ -218,8 +218,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   float m_run = st.m, l_run = st.l;
   f32x4* acc = st.acc;
   // per-lane sums cover tokens 4*(lane/16)+i only; add the four lane groups
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_over_lane_groups(l_run);
 
   if constexpr (NW > 1) {
     // Merge the wavefronts' states in wave order.  Lane-indexed layout: every
@@ -332,20 +331,6 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
 // piece leaves its partial state in slot (worker + segment) and the merge
 // kernel combines the pieces in worker order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
 
 template <int CT, int D>
 __device__ void write_zero_rows(const DecodeArgs& a, int s, int lane) {
@@ -385,7 +370,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
     const int ctx = s < S ? max(0, a.lens[s] - a.len_offset) : 0;
     const uint32_t n = (uint32_t)((ctx + 15) >> 4);
     if (r < kScanRegs) creg[r] = ctx;
-    total += wave_sum(units(n));
+    total += wave_sum_u32(units(n));
     uint64_t zmask = __ballot(s < S && ctx == 0 && s % W == w);
     while (zmask) {
       const int l = __builtin_ctzll(zmask);
@@ -423,13 +408,13 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
       if (r < kScanRegs) n = (uint32_t)((creg[r] + 15) >> 4);
       else n = s < S ? (uint32_t)((max(0, a.lens[s] - a.len_offset) + 15) >> 4) : 0u;
       const uint32_t u = units(n);
-      const uint32_t incl = wave_incl_scan(u, lane);
-      const int64_t tot = (int64_t)Hkv * __shfl(incl, 63);
+      const uint32_t incl = wave_incl_scan_u32(u);
+      const int64_t tot = (int64_t)Hkv * __builtin_amdgcn_readlane(incl, 63);
       if (x0 < base + tot) {
         const uint64_t hit = __ballot(x0 < base + (int64_t)Hkv * incl);
         const int l = __builtin_ctzll(hit);
         s_cur = c + l;
-        p_cur = base + (int64_t)Hkv * __shfl(incl - u, l);
+        p_cur = base + (int64_t)Hkv * __builtin_amdgcn_readlane(incl - u, l);
         break;
       }
       base += tot;
@@ -534,8 +519,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
     }
     if (slot_new >= 0) nrow.store(a, slot_new, h, lane);
     float l_run = st.l;
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = sum_over_lane_groups(l_run);
 
     const bool whole = tl == 0 && te == n && !a.cascade;  // cascade: always pieces
     if (whole || te == n) {
@@ -615,12 +599,10 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
 
   float M = kNegInf;
   for (int p = lane; p < np; p += 64) M = fmaxf(M, ml(p)[0]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  M = wave_max_f32(M);
   float L = 0.f;
   for (int p = lane; p < np; p += 64) L += __builtin_amdgcn_exp2f(ml(p)[0] - M) * ml(p)[1];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+  L = wave_sum_f32(L);
 
   float o[VE];
 #pragma unroll
@@ -646,8 +628,7 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
   }
 #pragma unroll
   for (int e = 0; e < VE; ++e) {
-    o[e] += __shfl_xor(o[e], 16);
-    o[e] += __shfl_xor(o[e], 32);
+    o[e] = sum_over_lane_groups(o[e]);
   }
   if (p4 != 0) return;
   const float inv = a.v_scale / L;

@@ -237,12 +237,7 @@ __device__ __forceinline__ void condition_q(f32x4& q, uint32_t sign, bool zero) 
 template <int NT>
 __device__ int block_exclusive_scan(int v, int* scratch, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = (int)wave_incl_scan_u32((uint32_t)v);
   if (lane == 63) scratch[w] = x;
   __syncthreads();
   int base = 0, tot = 0;
@@ -292,8 +287,7 @@ __device__ bool ranked_job_by_seq(const PrefillArgs& a, int rows_g, int rank, in
     const int nq = a.qstart[s + 1] - a.qstart[s];
     if (nq > 0) mx = max(mx, cost(a.lens[s] - nq, nq * G, (nq * G - 1) / rows_g));
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+  mx = (int)wave_all_reduce((uint32_t)mx, [](uint32_t u, uint32_t v) { return u > v ? u : v; });  // mx >= 0
   if ((tid & 63) == 0) tmp[tid >> 6] = mx;
   for (int i = tid; i < kRankBuckets; i += NT) hist[i] = 0;
   __syncthreads();
@@ -396,8 +390,7 @@ __device__ void plan_staged(const PrefillArgs& a, int rows_g, int it0, int* scra
     if (n > 0) mx = max(mx, job_cost(ctx - nq, rows, n - 1, rows_g, G));
     njobs += n;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+  mx = (int)wave_all_reduce((uint32_t)mx, [](uint32_t u, uint32_t v) { return u > v ? u : v; });  // mx >= 0
   if ((tid & 63) == 0) tmp[8 + (tid >> 6)] = mx;
   int J;
   int j = block_exclusive_scan<NT>(njobs, tmp, J);  // its syncs publish seq and the maxima
@@ -935,8 +928,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
       for (int rb = 0; rb < R; ++rb) {
         float l_run = st[rb].l[0];
         if constexpr (F32) {  // lane shares -> column sum
-          l_run += __shfl_xor(l_run, 16);
-          l_run += __shfl_xor(l_run, 32);
+          l_run = sum_over_lane_groups(l_run);
         }
         const int rr = row_w0 + 16 * rb + (lane & 15);
         if (rr >= rows) continue;

@@ -412,6 +412,61 @@ __device__ __forceinline__ float max_over_lane_groups(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Whole-wavefront reductions and scans in VALU: DPP moves within each row of
+// 16 lanes (quad permutes, mirrors, row shifts), then across rows either the
+// gfx950 row-swap permutes or the row broadcasts.  No LDS round trip.
+// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_shr:n = 0x110 + n, row_mirror = 0x140, row_half_mirror = 0x141,
+// row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND = false>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, BOUND);
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_all_reduce(uint32_t x, Op op) {
+  x = op(x, dpp_u32<0xB1>(x));   // lane ^ 1
+  x = op(x, dpp_u32<0x4E>(x));   // lane ^ 2
+  x = op(x, dpp_u32<0x141>(x));  // lane i with 7 - i of its half row
+  x = op(x, dpp_u32<0x140>(x));  // lane i with 15 - i of its row
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);  // lane ^ 16
+  x = op(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);  // lane ^ 32
+  return op(b[0], b[1]);
+}
+// Sum over the 64 lanes, in every lane.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return wave_all_reduce(x, [](uint32_t u, uint32_t v) { return u + v; });
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  return __uint_as_float(wave_all_reduce(__float_as_uint(x), [](uint32_t u, uint32_t v) {
+    return __float_as_uint(__uint_as_float(u) + __uint_as_float(v));
+  }));
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+  return __uint_as_float(wave_all_reduce(__float_as_uint(x), [](uint32_t u, uint32_t v) {
+    return __float_as_uint(fmaxf(__uint_as_float(u), __uint_as_float(v)));
+  }));
+}
+// x + the value of lane ^ 16, then + the value of lane ^ 32 (the four lane groups).
+__device__ __forceinline__ float sum_over_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// Inclusive prefix sum over the 64 lanes: row shifts by 1, 2, 4, 8 (lanes
+// past a row's start add 0), then rows 1 and 3 add the total of the row
+// before them and rows 2 and 3 the total of rows 0 and 1.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += dpp_u32<0x111, 0xF, true>(x);
+  x += dpp_u32<0x112, 0xF, true>(x);
+  x += dpp_u32<0x114, 0xF, true>(x);
+  x += dpp_u32<0x118, 0xF, true>(x);
+  x += dpp_u32<0x142, 0xA>(x);
+  x += dpp_u32<0x143, 0xC>(x);
+  return x;
+}
+
 // Online-softmax state of one wavefront: per lane, head g = lane % 16.
 template <int VE>
 struct Softmax {
