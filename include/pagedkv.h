@@ -129,7 +129,7 @@ typedef enum {
   PKV_DECODE_BALANCED = 2,
   /* the library picks from the sizes it can see (no context lengths): many
      (sequence, KV head) pairs (at least 16 per compute unit) -> single pass
-     with 8 wavefronts per workgroup; otherwise balanced, with 8 workers per
+     with 4 wavefronts per workgroup; otherwise balanced, with 8 workers per
      compute unit from 8 pairs per compute unit up, else 4 */
   PKV_DECODE_AUTO = 3
 } pkv_decode_mode;
