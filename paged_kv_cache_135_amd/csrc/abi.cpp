@@ -1,6 +1,7 @@
 // extern "C" entry points of libpagedkv.so: descriptor validation, launch
 // parameters and error reporting.  Declarations and contracts: include/pagedkv.h.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -98,18 +99,20 @@ int64_t num_partitions(int64_t max_blocks, int64_t block_size, int64_t partition
 }
 
 // Compute units of the current device (cached per device; 256 if unknown).
+// Host threads may race to fill an entry; they store the same value.
 int32_t device_cus() {
-  static int32_t cache[64] = {0};
+  static std::atomic<int32_t> cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    cache[dev] = cus;
+  int32_t cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
+    cache[dev].store(cus, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return cus;
 }
 
 // Default balanced worker count: 4 wavefronts per compute unit.
