@@ -460,7 +460,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the decode path needs no cross-GPU exchange; see DESIGN.md for sharding)",
+              "(decode shards by sequence or by KV head with no cross-GPU exchange)",
               file=sys.stderr)
         return 2
     import numpy as np
