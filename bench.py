@@ -38,7 +38,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
-    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--workload", default="c2",
                    choices=["c2", "c3", "c4", "c4bs32", "c5", "cow", "p1", "swap"],
                    help="cow: copy-on-write block copies of the Qwen-shaped pool; p1: chunked "
