@@ -1,4 +1,5 @@
-"""Host logic of bench.py: which committed traffic summary a run reports."""
+"""Host logic of bench.py: which committed traffic summary a run reports, and its
+command-line contract (one GPU only; the default run is the Qwen-shaped step)."""
 import importlib.util
 import os
 
@@ -45,3 +46,21 @@ def test_committed_summaries_name_distinct_workloads(bench):
             first = open(os.path.join(_ROOT, "profiles", name)).readline()
             keys.append(first.split(":", 1)[-1].strip())
     assert keys and len(keys) == len(set(keys))
+
+
+def test_more_than_one_gpu_is_refused():
+    """--gpus N > 1 exits at once (status 2) with a message; nothing touches a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(_ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_default_run_is_the_qwen_shaped_step(bench, monkeypatch):
+    monkeypatch.setattr("sys.argv", ["bench.py"])
+    args = bench.parse()
+    assert (args.gpus, args.workload) == (1, "c2")
+    assert args.steps > 0 and args.warmup > 0
