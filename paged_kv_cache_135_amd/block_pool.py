@@ -176,8 +176,9 @@ class BlockPool:
 
         ``token_ids`` (with prefix caching on): the prompt's token ids.  The
         longest run of leading full blocks whose chain hashes are cached is
-        reused; ``cached_tokens(seq)`` then tells how many prompt tokens need
-        no prefill."""
+        reused, short of the block holding the prompt's last token;
+        ``cached_tokens(seq)`` then tells how many prompt tokens need no
+        prefill (always fewer than ``n_tokens``)."""
         if seq in self._seqs or seq in self._swapped:
             raise KeyError(f"sequence {seq!r} exists")
         n_tokens = int(n_tokens)
@@ -199,7 +200,11 @@ class BlockPool:
                 raise ValueError("only filled blocks can be shared")
             shared = src.table[:prefix_blocks]
         elif hashes:
-            for h in hashes:
+            # reuse stops short of the prompt's last token: a full hit would
+            # leave the step that produces the first output token nothing to
+            # compute, and recomputing that token would write into a shared
+            # block.  The final block is then taken fresh (block-granular).
+            for h in hashes[:(n_tokens - 1) // bs]:
                 b = self._block_of.get(h)
                 if b is None:
                     break

@@ -179,12 +179,14 @@ def test_freed_blocks_stay_matchable_until_reused_for_other_tokens():
     first = pool.table("a")
     pool.free("a")
     pool.allocate("b", 64, token_ids=t)
-    assert pool.cached_tokens("b") == 64 and pool.table("b") == first
+    # the block holding the prompt's last token is never reused
+    assert pool.cached_tokens("b") == 48 and pool.table("b")[:3] == first[:3]
+    assert pool.table("b")[3] != first[3]
     pool.free("b")
     # 8 blocks never used come off the free list first (least recently freed) ...
     pool.allocate("c", 8 * 16, token_ids=list(range(5000, 5128)))
     pool.allocate("d", 64, token_ids=t)
-    assert pool.cached_tokens("d") == 64
+    assert pool.cached_tokens("d") == 48
     pool.free("d")
     pool.free("c")
     # ... then the cached ones are overwritten by new tokens and stop matching
@@ -203,8 +205,27 @@ def test_appended_tokens_fill_blocks_that_join_the_cache():
         pool.append("a", 1, token_ids=[tok])
     full = prompt + gen  # 50 tokens: 3 full blocks
     pool.allocate("b", 48, token_ids=full[:48])
+    assert pool.cached_tokens("b") == 32
+    assert pool.table("b")[:2] == pool.table("a")[:2]
+    pool.allocate("c", 49, token_ids=full[:49])
+    assert pool.cached_tokens("c") == 48
+    assert pool.table("c")[:3] == pool.table("a")[:3]
+
+
+def test_a_full_hit_still_leaves_the_last_prompt_token_to_compute():
+    """Every block of the prompt is cached: reuse stops one block short, so the
+    step that produces the first output token has a token to compute and
+    writes only into a block of its own."""
+    pool = BlockPool(20, 16, enable_prefix_caching=True)
+    t = list(range(64))
+    pool.allocate("a", 64, token_ids=t)
+    pool.allocate("b", 64, token_ids=t)
     assert pool.cached_tokens("b") == 48
-    assert pool.table("b") == pool.table("a")[:3]
+    last = pool.table("b")[3]
+    assert pool.refcount(last) == 1 and last != pool.table("a")[3]
+    for n in (1, 15, 16, 17):
+        pool.allocate(("s", n), n, token_ids=t[:n])
+        assert pool.cached_tokens(("s", n)) == ((n - 1) // 16) * 16 < n
 
 
 def test_prefix_caching_off_shares_nothing():
