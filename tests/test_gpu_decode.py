@@ -2,9 +2,9 @@
 
 Small cases span several tiles, ragged tails, empty contexts, every group size
 class and both head dims, in single-pass and split-K launches with 1-8
-wavefronts per workgroup.  The named workloads run at full size: every row for
-the 4-, 64-, 256- and 512-sequence batches, sampled rows for the 131072-token
-sequences."""
+wavefronts per workgroup.  The named workloads run at full size with every output
+row compared: the 4-, 64-, 256- and 512-sequence batches and the 8 x 131072-token
+sequences at block sizes 16 and 32."""
 import math
 
 import numpy as np
@@ -123,41 +123,67 @@ def test_c3_shared_prefix_full(mode):
     gu.assert_close(got, ref, "bf16", "c3")
 
 
-# the split-K partitions the long-context workload is specified with, the
-# balanced split, and auto mode with streaming reads (what bench.py times)
-@pytest.mark.parametrize("bs,mode,stream", [(16, ("partitioned", 512, 4, 0), False),
-                                            (16, ("auto", 0, 0, 0), True),
-                                            (32, ("balanced", 0, 0, 0), False)])
-def test_c4_long_context_sampled_rows(bs, mode, stream):
-    def rows(case):
-        m = np.zeros((case.num_seqs, case.num_q_heads), bool)
-        m[[0, case.num_seqs - 1], :] = True
-        return m
-    case, got, ref, rm = _full(f"c4_bs{bs}", lambda: workloads.c4_long_context(block_size=bs),
-                               mode, row_mask=rows, stream_kv=stream)
-    gu.assert_close(got, ref, "bf16", f"c4 bs{bs} {_mid(mode)}", mask=rm)
+# The long-context workload at both block sizes, every row: the split-K
+# partitions it is specified with (512 tokens plus the reduce kernel), the
+# balanced split, and auto mode with streaming reads (what bench.py times).
+# One pool (2.4 GB on the host) is held at a time; the oracle runs once per
+# block size.
+_long = {}
+
+
+def _long_case(bs):
+    if bs not in _long:
+        _long.clear()
+        case = workloads.c4_long_context(block_size=bs)
+        g = gu.GpuCase(case)
+        g.fill_and_step_writes()
+        kc, vc = gu.oracle_caches(case)
+        _long[bs] = (case, g, gu.oracle_decode(case, kc, vc))
+    return _long[bs]
+
+
+@pytest.mark.parametrize("bs,mode,stream", [
+    (16, ("partitioned", 512, 4, 0), False), (16, ("auto", 0, 0, 0), True),
+    (16, ("balanced", 0, 0, 0), False),
+    (32, ("partitioned", 512, 4, 0), False), (32, ("auto", 0, 0, 0), True),
+    (32, ("balanced", 0, 0, 0), False)])
+def test_c4_long_context_every_row(bs, mode, stream):
+    case, g, ref = _long_case(bs)
+    got = gu.host(g.decode_mode(mode, stream_kv=stream))
+    assert got.shape == (8, 28, 128)
+    gu.assert_close(got, ref, "bf16", f"c4 bs{bs} {_mid(mode)} stream={stream}")
     assert np.all(np.isfinite(gu.as_f64(got)))
 
 
-@pytest.mark.parametrize("mode,stream", [(("balanced", 0, 0, 0), False), (("auto", 0, 0, 0), True)])
-def test_c5_e4m3_sampled_rows(mode, stream):
-    rng = np.random.default_rng(5)
-    pick = np.sort(rng.choice(512, size=32, replace=False))
+# The E4M3 workload, every row of all 512 sequences, against the oracle's own
+# write of the whole pool (fill plus the 4,096-token prefill chunk).
+_fp8 = {}
 
-    def tokens(case):
-        starts = np.concatenate([[0], np.cumsum(case.context_lens)[:-1]])
-        mask = np.zeros(case.fill_slots.size, bool)
-        for s in pick:
-            mask[starts[s]:starts[s] + case.context_lens[s]] = True
-        return mask
 
-    def rows(case):
-        m = np.zeros((case.num_seqs, case.num_q_heads), bool)
-        m[pick, :] = True
-        return m
-    case, got, ref, rm = _full("c5", workloads.c5_fp8, mode, row_mask=rows, tokens_mask_fn=tokens,
-                               stream_kv=stream)
-    gu.assert_close(got, ref, "fp8_e4m3", f"c5 {_mid(mode)}", mask=rm)
+def _fp8_case():
+    if not _fp8:
+        case = workloads.c5_fp8()
+        g = gu.GpuCase(case)
+        g.fill_and_step_writes()
+        kc, vc = gu.oracle_caches(case)
+        _fp8["v"] = (case, g, kc, vc, gu.oracle_decode(case, kc, vc))
+    return _fp8["v"]
+
+
+def test_c5_e4m3_whole_pool_bit_exact():
+    case, g, kc, vc, _ = _fp8_case()
+    assert case.slot_mapping.size == 4096 and case.fill_slots.size == case.context_lens.sum()
+    assert np.array_equal(gu.host(g.kc), kc), "key pool differs from the oracle's write"
+    assert np.array_equal(gu.host(g.vc), vc), "value pool differs from the oracle's write"
+
+
+@pytest.mark.parametrize("mode,stream", [(("auto", 0, 0, 0), True), (("balanced", 0, 0, 0), False),
+                                         (("partitioned", 512, 4, 0), False)])
+def test_c5_e4m3_every_row(mode, stream):
+    case, g, _, _, ref = _fp8_case()
+    got = gu.host(g.decode_mode(mode, stream_kv=stream))
+    assert got.shape == (512, 32, 128)
+    gu.assert_close(got, ref, "fp8_e4m3", f"c5 {_mid(mode)} stream={stream}")
 
 
 def test_many_sequences_take_the_long_scan_path():

@@ -84,23 +84,12 @@ def test_e4m3_quantizing_write_over_every_bf16_value(scale, elem):
     _compare_pools(g, okc, ovc, f"e4m3 scale {scale}")
 
 
-def test_c5_prefill_chunk_and_sampled_fill_full_size():
-    # the 4096-token bf16 prefill chunk into random free slots (every byte
-    # compared) plus the whole-pool fill, compared on a sample of sequences
+def test_c5_prefill_chunk_and_whole_fill_full_size():
+    # the whole-pool fill (528k tokens quantized to E4M3) and the 4096-token
+    # bf16 prefill chunk into random free slots: every byte of both pools
     case = workloads.c5_fp8()
     g = gu.GpuCase(case)
     g.fill_and_step_writes()
-    rng = np.random.default_rng(11)
-    pick = np.sort(rng.choice(case.num_seqs, size=24, replace=False))
-    starts = np.concatenate([[0], np.cumsum(case.context_lens)[:-1]])
-    mask = np.zeros(case.fill_slots.size, bool)
-    for s in pick:
-        mask[starts[s]:starts[s] + case.context_lens[s]] = True
-    okc, ovc = gu.oracle_caches(case, tokens_mask=mask)
-    gk, gv = gu.host(g.kc), gu.host(g.vc)
-    sl = np.concatenate([case.fill_slots[mask], case.slot_mapping])
-    bs = case.block_size
-    view = lambda a: a.transpose(0, 2, 1, 3).reshape(-1, a.shape[1], a.shape[3])
-    assert np.array_equal(view(gk)[sl], view(okc)[sl])
-    assert np.array_equal(view(gv)[sl], view(ovc)[sl])
-    assert bs == 16 and case.slot_mapping.size == 4096
+    okc, ovc = gu.oracle_caches(case)
+    assert case.block_size == 16 and case.slot_mapping.size == 4096
+    _compare_pools(g, okc, ovc, "c5 fill + chunk")
