@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 8
+#define PKV_ABI_VERSION 9
 #define PKV_MAX_DIMS 4
 
 typedef enum {
@@ -218,6 +218,33 @@ pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q,
                                   const pkv_tensor* context_lens, float scale,
                                   int32_t block_size, const pkv_decode_opts* opts,
                                   void* hip_stream);
+
+/*
+ * paged_attention_decode for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, result and errors as paged_attention_decode, but the split
+ * workspace is the library's own scratch: one fixed device array of
+ * pkv_noalloc_scratch_bytes() (32 MiB) that each GPU holds from the library's
+ * load until the process ends.  The call allocates nothing and frees nothing.
+ *   opts->workspace / workspace_bytes   ignored (the scratch takes their place)
+ *   opts->flags                         PKV_DECODE_DEFER_MERGE is refused
+ * A call whose mode needs more split workspace than the scratch holds fails
+ * with PKV_ERR_WORKSPACE before anything is launched (e.g. 512-token partitions
+ * of 8 x 131072-token sequences need ~30 MB; the balanced split of a
+ * 64-sequence batch ~5 MB).  Nothing in the scratch has to start at zero.
+ * All calls on one GPU share its scratch: calls that overlap on one GPU (on
+ * different streams, not ordered by events) race and give wrong results.
+ */
+pkv_status paged_attention_decode_noalloc(pkv_tensor* out, const pkv_tensor* q,
+                                          const pkv_tensor* key_cache,
+                                          const pkv_tensor* value_cache,
+                                          const pkv_tensor* block_tables,
+                                          const pkv_tensor* context_lens, float scale,
+                                          int32_t block_size, const pkv_decode_opts* opts,
+                                          void* hip_stream);
+
+/* Bytes of scratch behind paged_attention_decode_noalloc (per GPU). */
+size_t pkv_noalloc_scratch_bytes(void);
 
 /*
  * Second half of a call made with PKV_DECODE_DEFER_MERGE: merges the partial

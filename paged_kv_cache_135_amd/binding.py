@@ -29,8 +29,9 @@ EXPORTED = (
     "pkv_validate_block_ids", "paged_attention_decode_shared_prefix",
     "paged_attention_decode_shared_prefix_workspace_bytes", "pkv_validate_shared_prefix",
     "pkv_read_probe_blocks", "pkv_read_probe", "paged_attention_decode_shared_prefix_append",
+    "paged_attention_decode_noalloc", "pkv_noalloc_scratch_bytes",
 )
-ABI_VERSION = 8
+ABI_VERSION = 9
 DECODE_DEFER_MERGE = 1
 DECODE_STREAM_KV = 2
 
@@ -119,6 +120,9 @@ def load():
     lib.paged_attention_decode.restype = ctypes.c_int
     lib.paged_attention_decode_merge.argtypes = lib.paged_attention_decode.argtypes
     lib.paged_attention_decode_merge.restype = ctypes.c_int
+    lib.paged_attention_decode_noalloc.argtypes = lib.paged_attention_decode.argtypes
+    lib.paged_attention_decode_noalloc.restype = ctypes.c_int
+    lib.pkv_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.paged_attention_decode_append.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_float,
                                                   ctypes.c_int32, ctypes.POINTER(PkvDecodeOpts), P]
     lib.paged_attention_decode_append.restype = ctypes.c_int
@@ -280,6 +284,31 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
     if ws is not None and workspace is None and stream is not None:
         ws.record_stream(stream)
     return out
+
+
+def paged_attention_decode_noalloc(out, q, key_cache, value_cache, block_tables, context_lens,
+                                   scale: float, block_size: int, *, k_scale: float = 1.0,
+                                   v_scale: float = 1.0, mode: str | None = None,
+                                   partition_size: int = 0, waves_per_group: int = 0,
+                                   num_workers: int = 0, stream_kv: bool = False, stream=None):
+    """paged_attention_decode with the library's fixed device scratch as the
+    split workspace: allocates nothing (see include/pagedkv.h; calls that
+    overlap on one GPU race)."""
+    _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
+    opts = decode_opts(mode, partition_size, waves_per_group, num_workers, stream_kv=stream_kv)
+    dout, dq = describe(out), describe(q)
+    dkc, dvc = describe(key_cache, k_scale), describe(value_cache, v_scale)
+    dt, dl = describe(block_tables), describe(context_lens)
+    _check(load().paged_attention_decode_noalloc(
+        ctypes.byref(dout), ctypes.byref(dq), ctypes.byref(dkc), ctypes.byref(dvc),
+        ctypes.byref(dt), ctypes.byref(dl), float(scale), int(block_size), ctypes.byref(opts),
+        _stream(q, stream)))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of device scratch behind paged_attention_decode_noalloc (per GPU)."""
+    return int(load().pkv_noalloc_scratch_bytes())
 
 
 def paged_attention_decode_append(out, q, k, v, slot_mapping, key_cache, value_cache,

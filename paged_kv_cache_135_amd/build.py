@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["abi.cpp", "kv_write.hip", "decode.hip", "copy_blocks.hip", "prefill.hip", "read_probe.hip"]
+SOURCES = ["abi.cpp", "kv_write.hip", "decode.hip", "copy_blocks.hip", "prefill.hip", "read_probe.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -755,6 +755,51 @@ pkv_status paged_attention_decode(pkv_tensor* out, const pkv_tensor* q, const pk
                      context_lens, scale, block_size, opts, nullptr, phase_of(opts), hip_stream);
 }
 
+pkv_status paged_attention_decode_noalloc(pkv_tensor* out, const pkv_tensor* q,
+                                          const pkv_tensor* key_cache,
+                                          const pkv_tensor* value_cache,
+                                          const pkv_tensor* block_tables,
+                                          const pkv_tensor* context_lens, float scale,
+                                          int32_t block_size, const pkv_decode_opts* opts,
+                                          void* hip_stream) {
+  // the split workspace is sized from the descriptors alone, before any device call
+  PKV_TRY(check_tensor(q, "q", 3));
+  PKV_TRY(check_tensor(key_cache, "key_cache", 4));
+  PKV_TRY(check_tensor(block_tables, "block_tables", 2));
+  if (opts && (opts->flags & PKV_DECODE_DEFER_MERGE))
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode_noalloc: PKV_DECODE_DEFER_MERGE is "
+                                     "not supported (the scratch is not the caller's)");
+  pkv_decode_opts o{};
+  if (opts) o = *opts;
+  o.workspace = nullptr;
+  o.workspace_bytes = 0;
+  const int64_t S = q->shape[0], Hq = q->shape[1], D = q->shape[2], Hkv = key_cache->shape[1];
+  const int64_t maxb = block_tables->shape[1];
+  size_t need = 0;
+  if (S > 0 && Hkv > 0 && Hq % Hkv == 0 && S <= INT32_MAX && Hq <= INT32_MAX && D <= INT32_MAX &&
+      maxb <= INT32_MAX)
+    need = paged_attention_decode_workspace_bytes((int32_t)S, (int32_t)Hq, (int32_t)Hkv, (int32_t)D,
+                                                  (int32_t)maxb, block_size, opts ? &o : nullptr);
+  if (need > pkv::kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE, "paged_attention_decode_noalloc: this call needs %zu bytes of "
+                                   "split workspace, more than the %zu bytes of scratch",
+                need, pkv::kScratchBytes);
+  if (need > 0) {
+    void* p = nullptr;
+    const hipError_t e = pkv::scratch_for_current_device(&p);
+    if (e != hipSuccess)
+      return fail(PKV_ERR_HIP, "paged_attention_decode_noalloc: scratch address: %s",
+                  hipGetErrorString(e));
+    o.workspace = p;
+    o.workspace_bytes = pkv::kScratchBytes;
+  }
+  return decode_impl("paged_attention_decode_noalloc", out, q, key_cache, value_cache, block_tables,
+                     context_lens, scale, block_size, opts ? &o : nullptr, nullptr,
+                     pkv::kBothPhases, hip_stream);
+}
+
+size_t pkv_noalloc_scratch_bytes(void) { return pkv::kScratchBytes; }
+
 pkv_status paged_attention_decode_merge(pkv_tensor* out, const pkv_tensor* q,
                                         const pkv_tensor* key_cache, const pkv_tensor* value_cache,
                                         const pkv_tensor* block_tables,

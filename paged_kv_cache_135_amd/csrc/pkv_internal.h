@@ -156,4 +156,9 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int
                              hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// The allocation-free decode's scratch: a fixed device array of kScratchBytes;
+// its device address on the current GPU (looked up once per device).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_for_current_device(void** ptr);
+
 }  // namespace pkv

@@ -447,3 +447,27 @@ def test_read_probe_validates_before_any_launch():
     # host memory is refused: the kernel would dereference it
     assert lib.pkv_read_probe(addr + (16 - addr % 16) % 16, 32, ctypes.addressof(sink), None) == 4
     assert b"device memory" in lib.pkv_last_error()
+
+
+# ------------------------------------------------- allocation-free decode
+def test_noalloc_refuses_what_the_scratch_cannot_hold():
+    """paged_attention_decode_noalloc sizes its split workspace from the
+    descriptors and refuses, before any device call, a mode that needs more than
+    the fixed scratch (512-token partitions of two 2M-token sequences x 8 heads:
+    2 x 8 x 4096 x 130 x 4 B = 34 MB > 32 MiB); it also refuses a deferred merge."""
+    lib = B.load()
+    assert lib.pkv_noalloc_scratch_bytes() == 32 << 20
+    mb = (2 << 20) // 16
+    a = _decode_args(tables=desc([2, mb], B.PKV_I32, FAKE + (4 << 20)),
+                     opts=_opts(mode=1, part=512))
+    ref = lambda d: ctypes.byref(d) if d is not None else None
+    call = lambda a: lib.paged_attention_decode_noalloc(
+        ref(a["out"]), ref(a["q"]), ref(a["kc"]), ref(a["vc"]), ref(a["tables"]), ref(a["lens"]),
+        a["scale"], a["bs"], ref(a["opts"]), None)
+    assert call(a) == 6  # PKV_ERR_WORKSPACE
+    assert b"scratch" in lib.pkv_last_error()
+    o = _opts(mode=2, workers=64)
+    o.flags = B.DECODE_DEFER_MERGE
+    assert call(_decode_args(opts=o)) == 5  # PKV_ERR_UNSUPPORTED
+    # validation errors come back as for paged_attention_decode
+    assert call(_decode_args(out=None)) == 1
