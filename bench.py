@@ -4,7 +4,8 @@
 One step = one decode step of one attention layer over one batch: the
 slot-mapped KV write of every sequence's new token, then paged decode
 attention over the whole context (by default the balanced split: equal runs
-of tiles per wavefront, then the merge of split (sequence, KV head) pairs).
+of tiles per wavefront, each split (sequence, KV head) pair merged by its last
+piece in the same launch).
 When the step's writes are one new token per sequence at position len-1, the
 step is one call (paged_attention_decode_append, the write folded into the
 decode launch); otherwise (a prefill chunk into free slots) it is the KV write
@@ -15,9 +16,8 @@ it is read again.
 
 Prints ONE JSON line:
   value  = KV bytes read per step / wall time per step (GB/s, decimal)
-  roofline = KV bytes / the streaming decode kernel's duration per launch
-             (HIP events around back-to-back launches of it alone; its merge
-             kernel is timed apart) vs 8 TB/s
+  roofline = KV bytes / the decode call's duration (HIP events around
+             back-to-back calls: every kernel the call launches) vs 8 TB/s
   cpu_baseline = the fp64 oracle timed on this host on the same workload
 """
 from __future__ import annotations
@@ -555,23 +555,18 @@ def main():
     stream = torch.cuda.current_stream()
 
     def run_steps(n, ev=None):
-        # ev[i]: events before the write, before the streaming kernel, before
-        # the merge kernel and after it (the decode is split only when timed)
+        # ev[i]: events before the write, before the decode call and after it
         for i in range(n):
             li = i % layers
             if ev is not None:
                 ev[i][0].record(stream)
             if not append:
                 writes[li]()
-            if ev is None:
-                decodes[li]()
-                continue
-            ev[i][1].record(stream)
-            split_decodes[li]()
-            ev[i][2].record(stream)
-            if not prefix_len:
-                split_decodes[li].merge()
-            ev[i][3].record(stream)
+            if ev is not None:
+                ev[i][1].record(stream)
+            decodes[li]()
+            if ev is not None:
+                ev[i][2].record(stream)
 
     if args.copy_calibration_mib:
         src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=q.device)
@@ -607,38 +602,39 @@ def main():
         wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
 
-    # timed region 2: per-launch HIP events on the launch stream; the decode
-    # call is made in its two halves so the streaming kernel is timed alone
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    # timed region 2: HIP events around each step's write and decode call
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     run_steps(K, ev)
     torch.cuda.synchronize()
     wr_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
-    main_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
-    merge_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])
-    dec_s = float((main_ms + merge_ms).mean()) / 1e3
+    call_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
 
-    # timed region 3: the streaming kernel alone, K launches back to back
-    # between one pair of events (an event pair around each launch also counts
-    # the launch's dispatch latency); its merge is not needed for timing
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(K):
-        split_decodes[i % layers]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    main_s = e0.elapsed_time(e1) / 1e3 / K
+    def back_to_back(launches, n):
+        # n launches between one pair of events on the launch stream (an event
+        # pair around each launch also counts its dispatch latency)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            launches[i % len(launches)]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
 
-    # hot cache, reported beside the cold figure: every launch reads the same
-    # layer's pool (above, the pools rotate so each launch reads from HBM)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(K):
-        split_decodes[0]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    hot_s = e0.elapsed_time(e1) / 1e3 / K
+    # timed region 3: the whole decode call (every kernel it launches: for the
+    # balanced split one launch that also merges) K times back to back
+    call_s = back_to_back(decodes, K)
+    # hot cache, reported beside the cold figure: every call reads the same
+    # layer's pool (above, the pools rotate so each call reads from HBM)
+    hot_s = back_to_back(decodes[:1], K)
+    # reference: the streaming kernel alone with its merge deferred to a
+    # second launch (the layout before the merge was fused), and that merge
+    unfused_s = merge_s = None
+    if not prefix_len and args.mode in ("auto", "balanced"):
+        unfused_s = back_to_back(split_decodes, K)
+        both = [lambda d=d: (d(), d.merge()) for d in split_decodes]
+        merge_s = max(0.0, back_to_back(both, K) - unfused_s)
 
     kv = case.kv_bytes()
     traffic, traffic_kernel = measured_traffic(case.name + ("+cascade" if prefix_len else ""))
@@ -646,14 +642,16 @@ def main():
     value = kv / (ms_per_step / 1e3) / 1e9
     # HBM roofline: bytes that must come from memory; a shared prefix counts once
     roof_bytes = case.unique_kv_bytes() if case.shared_blocks else kv
-    achieved = roof_bytes / main_s / 1e9
+    achieved = roof_bytes / call_s / 1e9
     same = read_ceiling_same_size(stream, roof_bytes)
     ceiling["same_size"] = dict(same, frac_of_ceiling=round(achieved / same["value"], 4))
-    print(f"[bench] step {step}: streaming kernel {main_s*1e6:.1f} us per launch back to back "
-          f"({main_ms.mean()*1e3:.1f} us between events around each, p10 "
-          f"{np.percentile(main_ms,10)*1e3:.1f}, p90 {np.percentile(main_ms,90)*1e3:.1f}), "
-          f"merge {merge_ms.mean()*1e3:.1f} us, write {wr_ms.mean()*1e3:.1f} us, "
-          f"wall step {ms_per_step*1e3:.1f} us", file=sys.stderr, flush=True)
+    ref = (f", deferred-merge reference: streaming kernel {unfused_s*1e6:.1f} + merge "
+           f"{merge_s*1e6:.1f} us" if unfused_s is not None else "")
+    print(f"[bench] step {step}: decode call {call_s*1e6:.1f} us back to back "
+          f"({call_ms.mean()*1e3:.1f} us between events around each, p10 "
+          f"{np.percentile(call_ms,10)*1e3:.1f}, p90 {np.percentile(call_ms,90)*1e3:.1f}), "
+          f"write {wr_ms.mean()*1e3:.1f} us, wall step {ms_per_step*1e3:.1f} us{ref}",
+          file=sys.stderr, flush=True)
 
     res = {
         "metric": "paged decode attn: KV GB/s read (% of MI355X HBM peak) + decode tokens/s per layer",
@@ -690,20 +688,21 @@ def main():
         "kv_bytes_per_step": kv,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s_per_layer": round(case.num_seqs / (ms_per_step / 1e3), 1),
-        "decode_us": round(dec_s * 1e6, 2),
-        "streaming_kernel_us": round(main_s * 1e6, 2),
-        "streaming_kernel_event_pair_us": round(float(main_ms.mean()) * 1e3, 2),
-        "streaming_kernel_event_pair_percentiles_us": {
-            f"p{p}": round(float(np.percentile(main_ms, p)) * 1e3, 2) for p in (10, 50, 90)},
-        "streaming_kernel_hot_cache_us": round(hot_s * 1e6, 2),
-        "merge_us": round(float(merge_ms.mean()) * 1e3, 2),
+        "decode_call_us": round(call_s * 1e6, 2),
+        "decode_call_event_pair_us": round(float(call_ms.mean()) * 1e3, 2),
+        "decode_call_event_pair_percentiles_us": {
+            f"p{p}": round(float(np.percentile(call_ms, p)) * 1e3, 2) for p in (10, 50, 90)},
+        "decode_call_hot_cache_us": round(hot_s * 1e6, 2),
+        "deferred_merge_reference_us": None if unfused_s is None else {
+            "streaming_kernel": round(unfused_s * 1e6, 2), "merge_kernel": round(merge_s * 1e6, 2)},
         "write_us": round(float(wr_ms.mean()) * 1e3, 2) if not append else 0.0,
         "roofline": {
-            "kernel": "shared-prefix decode call (prefix + tail + merge kernels)" if prefix_len
-            else "streaming decode kernel (" + (
+            "kernel": "shared-prefix decode call (prefix kernel + tail kernel with the merge fused)"
+            if prefix_len else "decode call (" + (
                 "append, " if append else "") + {
-                "single": "single pass", "partitioned": "partitions",
-                "balanced": "balanced split", "auto": "auto mode"}[args.mode] + ")",
+                "single": "single pass", "partitioned": "partitions + reduce kernel",
+                "balanced": "balanced split, merge fused",
+                "auto": "auto mode"}[args.mode] + "): every kernel the call launches",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,

@@ -48,6 +48,8 @@ namespace {
 #endif
 
 constexpr int kChunkTiles = 1024;  // block ids staged in LDS per pass (4 KiB)
+// Block tables read as constant memory (uniform indices: scalar loads).
+typedef const __attribute__((address_space(4))) int32_t* ctab;
 // Balanced split: work units charged for starting a piece, in tiles.  A piece
 // start (q rows, block ids, the partial write) costs about two bf16 tile times
 // on MI355X; an E4M3 tile streams in half the time, so the same start costs
@@ -340,8 +342,11 @@ __device__ void write_zero_rows(const DecodeArgs& a, int s, int lane) {
   for (int i = lane; i < n16; i += 64) reinterpret_cast<u32x4*>(o)[i] = u32x4{0, 0, 0, 0};
 }
 
+// At most two wavefronts per SIMD (the split runs 4 or 8 workers per CU): with
+// the tighter three-per-SIMD budget the loop lost its load scheduling (the
+// Qwen-shaped batch: 44.5 us per launch at two, 52 us when it spilled at three).
 template <int CT, int D, int NBUF, bool APPEND, bool NT>
-__global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3) void decode_balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
   using T = Tile<CT, D>;
   constexpr int VE = T::VE;
   const int lane = threadIdx.x & 63;
@@ -424,7 +429,7 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
   const int g = lane & 15;
   const bool g_ok = g < G;
   int64_t x = x0;
-  int32_t carry = 0;      // first-batch block ids of the next piece, loaded ahead
+  int32_t carry[NBUF] = {};  // first-batch block ids of the next piece, loaded ahead
   bool has_carry = false;
   // the run's sequences lie in the 64-sequence chunk of s_cur and, for runs
   // that cross it, the next one: keep those two registers
@@ -488,28 +493,61 @@ __global__ __launch_bounds__(256, (CT == PKV_F32 || NBUF > 2 || APPEND) ? 2 : 3)
     const void* vn = static_cast<const QElem<CT>*>(a.vn) + new_row * D;
     NewRow<CT, D> nrow;
     if (slot_new >= 0) nrow.load(a, s_cur, h, lane);
-    // Block ids of the next batch arrive one batch ahead (lane j holds tile k+j);
+    // Block ids of the next batch arrive one batch ahead, through scalar loads
+    // (the tables are read-only here, so they are read as constant memory:
+    // the ids never wait in the vector-memory queue behind the tile loads);
     // tiles past the piece clamp to its last tile (in bounds, result unused).
-    auto entry = [&](int t) { return table[(min(t, te - 1) * 16) / bs]; };
-    int32_t ent_next = has_carry ? carry : (lane < NBUF ? entry(tl + lane) : 0);
-    // When the run goes on with the next KV head of this sequence, that piece
-    // starts at tile 0 of the same table row: fetch its first block ids now.
+    const ctab ctable = (ctab)table;  // address-space cast: C-style only
+    auto entry = [&](int t) { return ctable[(min(t, te - 1) * 16) / bs]; };
+    int32_t ent_next[NBUF];
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) ent_next[j] = has_carry ? carry[j] : entry(tl + j);
+    // When the run goes on into the next pair (the next KV head of this
+    // sequence, or the next sequence with tokens), that piece starts at tile 0
+    // of its table row: fetch its first block ids now, so the piece change
+    // costs no dependent table read.
     const int64_t after = x + (ve - vt);
-    has_carry = ve == u && h + 1 < Hkv && x1 - after > kPieceCost;
-    const int te_next = has_carry ? (int)min((int64_t)n, x1 - after - kPieceCost) : 1;
+    has_carry = ve == u && x1 - after > kPieceCost;
+    int s_next = s_cur;
+    if (has_carry && h + 1 >= Hkv) {
+      do ++s_next; while (s_next < S && ctx_of(s_next) == 0);
+      has_carry = s_next < S;
+    }
+    const int te_next =
+        has_carry ? (int)min((int64_t)((ctx_of(s_next) + 15) >> 4), x1 - after - kPieceCost) : 1;
+    const int32_t* table_next = a.tables + (int64_t)s_next * a.max_blocks;
     for (int k = tl; k < te; k += NBUF) {
-      const int32_t ent = ent_next;
-      ent_next = lane < NBUF ? entry(k + NBUF + lane) : 0;
-      if (has_carry && k == tl) carry = lane < NBUF ? table[(min(lane, te_next - 1) * 16) / bs] : 0;
-      T buf[NBUF];
+      int32_t ent[NBUF];
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
-        const int t = min(k + j, te - 1);
-        const int32_t blk = __builtin_amdgcn_readlane(ent, j);
-        const int64_t row = (int64_t)blk * block_rows + head_rows + ((t * 16) % bs);
-        const int rsub =
-            slot_new >= 0 && k + j == n - 1 && (int64_t)blk * bs + off_new == slot_new ? r_new : -1;
-        buf[j].template load_sub<NT>(a.kc, a.vc, row, lane, rsub, kn, vn, a.inv_k, a.inv_v);
+        ent[j] = ent_next[j];
+        ent_next[j] = entry(k + NBUF + j);
+      }
+      if (has_carry && k == tl) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j)
+          carry[j] = ((ctab)table_next)[(min(j, te_next - 1) * 16) / bs];
+      }
+      T buf[NBUF];
+      if (APPEND && slot_new >= 0 && k + NBUF >= n) {
+        // the batch holding the pair's last tile: its new token's rows come
+        // from k / v (a per-lane address choice) when the slot is position ctx-1
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          const int t = min(k + j, te - 1);
+          const int32_t blk = ent[j];
+          const int64_t row = (int64_t)blk * block_rows + head_rows + ((t * 16) % bs);
+          const int rsub = k + j == n - 1 && (int64_t)blk * bs + off_new == slot_new ? r_new : -1;
+          buf[j].template load_sub<NT>(a.kc, a.vc, row, lane, rsub, kn, vn, a.inv_k, a.inv_v);
+        }
+      } else {
+        // every other batch: plain tile loads, nothing computed in front of them
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          const int t = min(k + j, te - 1);
+          const int64_t row = (int64_t)ent[j] * block_rows + head_rows + ((t * 16) % bs);
+          buf[j].template load<NT>(a.kc, a.vc, row, lane);
+        }
       }
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
