@@ -40,10 +40,11 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--workload", default="c2",
-                   choices=["c2", "c3", "c4", "c4bs32", "c5", "cow", "p1", "swap"],
-                   help="cow: copy-on-write block copies of the Qwen-shaped pool; p1: chunked "
-                        "prefill of 8 x 512 tokens over cached prefixes; swap: swap-out gather "
-                        "and swap-in scatter of 4,096 blocks (each its own metric)")
+                   choices=["c2", "c3", "c4", "c4bs32", "c5", "c5write", "cow", "p1", "swap"],
+                   help="c5write: the E4M3 workload's 4,096-token bf16 chunk quantized into its "
+                        "slots, alone; cow: copy-on-write block copies of the Qwen-shaped pool; "
+                        "p1: chunked prefill of 8 x 512 tokens over cached prefixes; swap: "
+                        "swap-out gather and swap-in scatter of 4,096 blocks (each its own metric)")
     p.add_argument("--shared-prefix", action="store_true",
                    help="c3: decode with paged_attention_decode_shared_prefix (the shared "
                         "prefix computed once for all sequences)")
@@ -217,6 +218,73 @@ def cpu_baseline(case, seconds):
         "cpu_model": model,
         "single_thread": single,
     }
+
+
+def bench_chunk_write(args):
+    """The E4M3 workload's KV write on its own: 4,096 bf16 tokens (8 KV heads x
+    128) quantized into distinct random slots of the E4M3 pool.  Algorithmic
+    bytes per call: the bf16 rows read plus the E4M3 codes written (K and V)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_135_amd as pkv
+    import workloads
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    print("[bench] building workload c5 (chunk write)", file=sys.stderr, flush=True)
+    case = workloads.c5_fp8()
+    kc, vc = dev(case.key_cache), dev(case.value_cache)
+    kn, vn, slots = dev(case.k_new), dev(case.v_new), dev(case.slot_mapping)
+    T, H, D = case.k_new.shape
+    moved = 2 * T * H * D * (2 + 1)
+    w = pkv.WriteLaunch(kn, vn, slots, kc, vc, k_scale=case.k_scale, v_scale=case.v_scale)
+    for _ in range(args.warmup):
+        w()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        w()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    per = e0.elapsed_time(e1) / 1e3 / args.steps
+    gbps = moved / per / 1e9
+    print(f"[bench] chunk write: {per*1e6:.2f} us per launch back to back, {gbps:.1f} GB/s",
+          file=sys.stderr, flush=True)
+    res = {
+        "metric": "KV write of a 4,096-token bf16 chunk into an E4M3 cache: GB/s moved (read + write)",
+        "value": round(moved / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "c5_fp8_chunk_write", "tokens": int(T), "num_kv_heads": int(H),
+                   "head_dim": int(D), "block_size": case.block_size},
+        "bytes_per_call": moved, "write_kernel_us": round(per * 1e6, 3),
+        "roofline": {"kernel": "kv_write_kernel (bf16 -> E4M3)", "bound": "hbm",
+                     "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        kh, vh = case.key_cache.copy(), case.value_cache.copy()
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            oracle.paged_kv_write(case.k_new, case.v_new, case.slot_mapping, kh, vh, case.k_scale,
+                                  case.v_scale)
+            reps += 1
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(moved * reps / el / 1e9, 3), "unit": "GB/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"the same 4,096-token write, {reps} times in {el:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def bench_copy_blocks(args):
@@ -480,6 +548,8 @@ def main():
     pkv.load()
     if args.workload == "cow":
         return bench_copy_blocks(args)
+    if args.workload == "c5write":
+        return bench_chunk_write(args)
     if args.workload == "p1":
         return bench_prefill(args)
     if args.workload == "swap":
