@@ -16,8 +16,9 @@ it is read again.
 
 Prints ONE JSON line:
   value  = KV bytes read per step / wall time per step (GB/s, decimal)
-  roofline = KV bytes / the decode call's duration (HIP events around
-             back-to-back calls: every kernel the call launches) vs 8 TB/s
+  roofline = KV bytes / the streaming decode kernel's duration per launch
+             (HIP events around back-to-back launches of it alone) vs 8 TB/s
+  call_roofline = the same bytes / the whole call (streaming kernel + merge)
   cpu_baseline = the fp64 oracle timed on this host on the same workload
 """
 from __future__ import annotations
@@ -40,7 +41,7 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--workload", default="c2",
-                   choices=["c2", "c3", "c4", "c4bs32", "c5", "c5write", "cow", "p1", "swap"],
+                   choices=["c1", "c2", "c3", "c4", "c4bs32", "c5", "c5write", "cow", "p1", "swap"],
                    help="c5write: the E4M3 workload's 4,096-token bf16 chunk quantized into its "
                         "slots, alone; cow: copy-on-write block copies of the Qwen-shaped pool; "
                         "p1: chunked prefill of 8 x 512 tokens over cached prefixes; swap: "
@@ -72,6 +73,8 @@ def parse():
 
 def build_workload(name):
     import workloads
+    if name == "c1":
+        return workloads.c1_tiny_f32()
     if name == "c2":
         return workloads.c2_qwen_decode()
     if name == "c3":
@@ -567,7 +570,11 @@ def main():
         pkv.paged_kv_write(dev(case.fill_k), dev(case.fill_v), dev(case.fill_slots), kc0, vc0,
                            k_scale=case.k_scale, v_scale=case.v_scale)
     pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(layers - 1)]
-    knew, vnew, slots = dev(case.k_new), dev(case.v_new), dev(case.slot_mapping)
+    # the step's own write (none for the tiny f32 workload, whose tokens all
+    # arrive through the fill)
+    has_write = case.k_new is not None
+    knew, vnew, slots = ((dev(case.k_new), dev(case.v_new), dev(case.slot_mapping)) if has_write
+                         else (None, None, None))
     out = torch.empty_like(q)
     nbytes = pkv.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
                                         case.head_dim, case.block_tables.shape[1],
@@ -586,13 +593,15 @@ def main():
         # Not for a shared prefix: there the tails' launch with the write folded
         # in is as much slower as the write launch it saves (115.2 vs 114.8 us
         # per step on the 256-sequence batch); --step append selects it.
-        if case.slot_mapping.shape[0] == case.num_seqs and not prefix_len:
+        if has_write and case.slot_mapping.shape[0] == case.num_seqs and not prefix_len:
             try:
                 pkv.validate_append_slots(case.slot_mapping, case.block_tables, case.context_lens,
                                           case.key_cache.shape[0], case.block_size)
                 step = "append"
             except pkv.PagedKVError:
                 pass
+    if not has_write:
+        step = "split"
     append = step == "append"
     # the streaming hint is for calls that read every block once: decided from
     # the tables (past the shared prefix when it is computed apart)
@@ -617,7 +626,8 @@ def main():
                                 defer_merge=defer, **dkw)
 
     writes = [pkv.WriteLaunch(knew, vnew, slots, kc, vc, k_scale=case.k_scale,
-                              v_scale=case.v_scale) for kc, vc in pools]
+                              v_scale=case.v_scale) if has_write else (lambda: None)
+              for kc, vc in pools]
     decodes = [decode_launch(kc, vc, False) for kc, vc in pools]
     split_decodes = [decode_launch(kc, vc, True) for kc, vc in pools]
     torch.cuda.synchronize()
@@ -698,29 +708,35 @@ def main():
     # hot cache, reported beside the cold figure: every call reads the same
     # layer's pool (above, the pools rotate so each call reads from HBM)
     hot_s = back_to_back(decodes[:1], K)
-    # reference: the streaming kernel alone with its merge deferred to a
-    # second launch (the layout before the merge was fused), and that merge
-    unfused_s = merge_s = None
-    if not prefix_len and args.mode in ("auto", "balanced"):
-        unfused_s = back_to_back(split_decodes, K)
-        both = [lambda d=d: (d(), d.merge()) for d in split_decodes]
-        merge_s = max(0.0, back_to_back(both, K) - unfused_s)
+    # timed region 4: the dominant kernel alone, the streaming kernel (the
+    # call made with its merge deferred, K launches back to back); its merge
+    # kernel is what the whole call adds (nothing for the single pass).  A
+    # shared-prefix call launches its kernels together: there the whole call.
+    if prefix_len:
+        kern_s, merge_s = call_s, 0.0
+    else:
+        kern_s = back_to_back(split_decodes, K)
+        merge_s = max(0.0, call_s - kern_s)
 
     kv = case.kv_bytes()
-    traffic, traffic_kernel = measured_traffic(case.name + ("+cascade" if prefix_len else ""))
+    # counters are keyed by workload and, outside auto mode, by the mode
+    key = case.name + ("+cascade" if prefix_len else "")
+    if args.mode != "auto" and not prefix_len:
+        key += f"+{args.mode}" + (str(args.partition) if args.mode == "partitioned" else "")
+    traffic, traffic_kernel = measured_traffic(key)
     ceiling = read_ceiling(stream)
     value = kv / (ms_per_step / 1e3) / 1e9
     # HBM roofline: bytes that must come from memory; a shared prefix counts once
     roof_bytes = case.unique_kv_bytes() if case.shared_blocks else kv
-    achieved = roof_bytes / call_s / 1e9
+    achieved = roof_bytes / kern_s / 1e9
+    call_achieved = roof_bytes / call_s / 1e9
     same = read_ceiling_same_size(stream, roof_bytes)
     ceiling["same_size"] = dict(same, frac_of_ceiling=round(achieved / same["value"], 4))
-    ref = (f", deferred-merge reference: streaming kernel {unfused_s*1e6:.1f} + merge "
-           f"{merge_s*1e6:.1f} us" if unfused_s is not None else "")
     print(f"[bench] step {step}: decode call {call_s*1e6:.1f} us back to back "
           f"({call_ms.mean()*1e3:.1f} us between events around each, p10 "
-          f"{np.percentile(call_ms,10)*1e3:.1f}, p90 {np.percentile(call_ms,90)*1e3:.1f}), "
-          f"write {wr_ms.mean()*1e3:.1f} us, wall step {ms_per_step*1e3:.1f} us{ref}",
+          f"{np.percentile(call_ms,10)*1e3:.1f}, p90 {np.percentile(call_ms,90)*1e3:.1f}): "
+          f"streaming kernel {kern_s*1e6:.1f} + merge {merge_s*1e6:.1f} us; "
+          f"write {wr_ms.mean()*1e3:.1f} us, wall step {ms_per_step*1e3:.1f} us",
           file=sys.stderr, flush=True)
 
     res = {
@@ -763,16 +779,14 @@ def main():
         "decode_call_event_pair_percentiles_us": {
             f"p{p}": round(float(np.percentile(call_ms, p)) * 1e3, 2) for p in (10, 50, 90)},
         "decode_call_hot_cache_us": round(hot_s * 1e6, 2),
-        "deferred_merge_reference_us": None if unfused_s is None else {
-            "streaming_kernel": round(unfused_s * 1e6, 2), "merge_kernel": round(merge_s * 1e6, 2)},
+        "streaming_kernel_us": round(kern_s * 1e6, 2),
+        "merge_us": round(merge_s * 1e6, 2),
         "write_us": round(float(wr_ms.mean()) * 1e3, 2) if not append else 0.0,
         "roofline": {
-            "kernel": "shared-prefix decode call (prefix kernel + tail kernel with the merge fused)"
-            if prefix_len else "decode call (" + (
-                "append, " if append else "") + {
-                "single": "single pass", "partitioned": "partitions + reduce kernel",
-                "balanced": "balanced split, merge fused",
-                "auto": "auto mode"}[args.mode] + "): every kernel the call launches",
+            "kernel": "shared-prefix decode call (prefix, tail and merge kernels)" if prefix_len
+            else "streaming decode kernel (" + ("append, " if append else "") + {
+                "single": "single pass", "partitioned": "partitions",
+                "balanced": "balanced split", "auto": "auto mode"}[args.mode] + ")",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -780,6 +794,11 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
         },
+        # the whole decode call: every kernel it launches (streaming kernel and,
+        # for split pairs, the merge), back to back
+        "call_roofline": {
+            "achieved": round(call_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(call_achieved / HBM_PEAK_GBPS, 4), "us_per_call": round(call_s * 1e6, 2)},
         # the same kernel's rate against what one plain streaming pass reaches on this machine
         "read_ceiling": dict(ceiling, frac_of_ceiling=round(achieved / ceiling["value"], 4)),
     }

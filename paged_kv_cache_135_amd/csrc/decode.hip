@@ -135,8 +135,11 @@ __device__ __forceinline__ void process_tile(Tile<CT, D>& t, const typename Tile
   st.m = m_new;
 }
 
+// E4M3 (without the folded write) at four wavefronts per SIMD: one more
+// workgroup resident per CU for the many short pairs auto mode sends here
+// (512-sequence E4M3 batch: 194.0 -> 192.6 us); the other variants would spill.
 template <int CT, int D, int NW, int NBUF, bool APPEND, bool NT>
-__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64, (CT == PKV_FP8_E4M3 && !APPEND) ? 4 : 1) void decode_partition_kernel(DecodeArgs a) {
   using T = Tile<CT, D>;
   constexpr int VE = T::VE;
   const int part = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
@@ -285,42 +288,71 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   }
 }
 
-// Merge the partitions of one (sequence, query head) in partition order.
+// Merge the partitions of one (sequence, query head).  256 threads: thread t
+// owns the four columns 4 (t % CW) .. of the rows (partitions) t / CW,
+// t / CW + RS, ... (CW = D / 4 column quads, RS = 256 / CW row sets), with
+// kRows of them loaded before any is used; the common max M and the total L
+// come from a block reduction over the (max, sum) pairs, and the RS partial
+// rows are added in row-set order, so the result does not depend on timing.
 template <int CT, int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
-  constexpr int PER = D / 64;
-  const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+  constexpr int CW = D / 4, RS = 256 / CW, kRows = 8;
+  __shared__ float red[2][4];
+  __shared__ f32x4 part[RS][CW];
+  const int h = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
+  const int wv = t >> 6, c = t % CW, r = t / CW;
   const int ctx = a.lens[s];
   const int ntiles = (ctx + 15) >> 4;
   if (ntiles <= a.part_tiles) return;  // written directly by its only partition
   const int np = (ntiles + a.part_tiles - 1) / a.part_tiles;
   const int64_t prow0 = ((int64_t)s * a.num_q_heads + h) * a.num_parts;
   const float* ml = a.ws_ml + prow0 * 2;
-  float M = kNegInf;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-  float L = 0.f, o[PER];
+  const float* acc = a.ws_acc + prow0 * D + 4 * c;
+
+  // the first batch of rows goes out before the reductions that need M
+  f32x4 v[kRows];
+  float mr[kRows];
+  auto load_rows = [&](int p0) {
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float f = __builtin_amdgcn_exp2f(ml[2 * p] - M);
-    L += f * ml[2 * p + 1];
-    const float* src = a.ws_acc + (prow0 + p) * D + PER * lane;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] += f * src[e];
-  }
-  const float inv = a.v_scale / L;
-  const int64_t oi = ((int64_t)s * a.num_q_heads + h) * D + PER * lane;
-  if constexpr (CT == PKV_F32) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) static_cast<float*>(a.out)[oi + e] = o[e] * inv;
-  } else {
-    uint16_t* out = static_cast<uint16_t*>(a.out) + oi;
-    if constexpr (PER == 2) {
-      *reinterpret_cast<uint32_t*>(out) = pack_bf16(o[0] * inv, o[1] * inv);
-    } else {
-      out[0] = (uint16_t)(pack_bf16(o[0] * inv, 0.f) & 0xffffu);
+    for (int j = 0; j < kRows; ++j) {
+      const int p = p0 + j * RS;
+      v[j] = p < np ? *reinterpret_cast<const f32x4*>(acc + (int64_t)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+      mr[j] = p < np ? ml[2 * p] : kNegInf;
     }
+  };
+  load_rows(r);
+
+  float m = kNegInf;
+  for (int p = t; p < np; p += 256) m = fmaxf(m, ml[2 * p]);
+  m = wave_max_f32(m);
+  if ((t & 63) == 0) red[0][wv] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  float l = 0.f;
+  for (int p = t; p < np; p += 256) l += __builtin_amdgcn_exp2f(ml[2 * p] - M) * ml[2 * p + 1];
+  l = wave_sum_f32(l);
+  if ((t & 63) == 0) red[1][wv] = l;
+
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = r;; p0 += kRows * RS) {
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      const int p = p0 + j * RS;
+      if (p < np) o += __builtin_amdgcn_exp2f(mr[j] - M) * v[j];
+    }
+    if (p0 + kRows * RS >= np) break;
+    load_rows(p0 + kRows * RS);
   }
+  part[r][c] = o;
+  __syncthreads();
+  if (t >= CW) return;
+  f32x4 sum = part[0][c];
+#pragma unroll
+  for (int i = 1; i < RS; ++i) sum += part[i][c];
+  const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  const float inv = a.v_scale / L;
+  const float x[4] = {sum[0] * inv, sum[1] * inv, sum[2] * inv, sum[3] * inv};
+  store_run<CT, 4>(a.out, ((int64_t)s * a.num_q_heads + h) * D + 4 * c, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -679,9 +711,12 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
 
 // Tiles loaded per batch.  More tiles put more bytes in flight per wavefront
 // but cost VGPRs (32 per bf16 D=128 tile) and occupancy.
+#ifndef PKV_DECODE_RING_FP8
+#define PKV_DECODE_RING_FP8 PKV_DECODE_RING
+#endif
 template <int CT, int D>
 constexpr int ring_depth() {
-  return PKV_DECODE_RING;
+  return CT == PKV_FP8_E4M3 ? PKV_DECODE_RING_FP8 : PKV_DECODE_RING;
 }
 
 template <int CT, int D, int NW>
@@ -703,7 +738,7 @@ hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
   }
   if (a.phase == kSplitPhase || a.num_parts == 1) return hipSuccess;
   const dim3 rgrid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((decode_reduce_kernel<CT, D>), rgrid, dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_reduce_kernel<CT, D>), rgrid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
