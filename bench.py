@@ -223,6 +223,41 @@ def cpu_baseline(case, seconds):
     }
 
 
+def copy_calibration(mib: int) -> None:
+    """One device copy of `mib` MiB, for scaling the byte counters of a
+    rocprofv3 --pmc run (a copy of known size read and written once)."""
+    if not mib:
+        return
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def copy_ceiling(nbytes: int, reps: int = 200) -> dict:
+    """A plain device copy moving the same bytes (nbytes / 2 read, nbytes / 2
+    written), back to back between two events: what a simple streaming kernel
+    reaches at this size."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    return {"kind": "torch device copy of the same bytes moved", "bytes": 2 * src.numel(),
+            "us": round(us, 3), "value": round(2 * src.numel() / us / 1e3, 1), "unit": "GB/s"}
+
+
 def bench_chunk_write(args):
     """The E4M3 workload's KV write on its own: 4,096 bf16 tokens (8 KV heads x
     128) quantized into distinct random slots of the E4M3 pool.  Algorithmic
@@ -245,6 +280,7 @@ def bench_chunk_write(args):
     T, H, D = case.k_new.shape
     moved = 2 * T * H * D * (2 + 1)
     w = pkv.WriteLaunch(kn, vn, slots, kc, vc, k_scale=case.k_scale, v_scale=case.v_scale)
+    copy_calibration(args.copy_calibration_mib)
     for _ in range(args.warmup):
         w()
     torch.cuda.synchronize()
@@ -269,23 +305,40 @@ def bench_chunk_write(args):
         "config": {"workload": "c5_fp8_chunk_write", "tokens": int(T), "num_kv_heads": int(H),
                    "head_dim": int(D), "block_size": case.block_size},
         "bytes_per_call": moved, "write_kernel_us": round(per * 1e6, 3),
+        "ceiling": copy_ceiling(moved),
         "roofline": {"kernel": "kv_write_kernel (bf16 -> E4M3)", "bound": "hbm",
                      "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
     }
     if not args.no_cpu_baseline:
+        import ctypes
+
         import oracle
         kh, vh = case.key_cache.copy(), case.value_cache.copy()
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-        reps, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
-            oracle.paged_kv_write(case.k_new, case.v_new, case.slot_mapping, kh, vh, case.k_scale,
-                                  case.v_scale)
-            reps += 1
-        el = time.perf_counter() - t0
+
+        def writes(seconds):
+            reps, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < seconds:
+                oracle.paged_kv_write(case.k_new, case.v_new, case.slot_mapping, kh, vh,
+                                      case.k_scale, case.v_scale)
+                reps += 1
+            return reps, time.perf_counter() - t0
+
+        reps, el = writes(min(args.cpu_seconds, 10.0))
         res["cpu_baseline"] = {"value": round(moved * reps / el / 1e9, 3), "unit": "GB/s",
                                "cores": threads, "kind": "oracle",
                                "sample": f"the same 4,096-token write, {reps} times in {el:.1f} s"}
+        try:
+            gomp = ctypes.CDLL("libgomp.so.1")
+            gomp.omp_set_num_threads(1)
+            r1, e1 = writes(min(args.cpu_seconds, 10.0) / 2)
+            gomp.omp_set_num_threads(threads)
+            res["cpu_baseline"]["single_thread"] = {
+                "value": round(moved * r1 / e1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                "sample": f"the same write, {r1} times in {e1:.1f} s"}
+        except OSError:
+            pass
     print(json.dumps(res), flush=True)
     return 0
 
@@ -309,6 +362,7 @@ def bench_copy_blocks(args):
     pkv.validate_block_pairs(pairs_np, NB)
     block_bytes = H * bs * D * 2
     moved = P * 2 * block_bytes * 2
+    copy_calibration(args.copy_calibration_mib)
     for _ in range(args.warmup):
         pkv.paged_kv_copy_blocks(kc, vc, pairs)
     torch.cuda.synchronize()
@@ -648,13 +702,7 @@ def main():
             if ev is not None:
                 ev[i][2].record(stream)
 
-    if args.copy_calibration_mib:
-        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=q.device)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args.copy_calibration_mib)
     print(f"[bench] warmup {args.warmup} steps, {layers} layer pools", file=sys.stderr, flush=True)
     run_steps(args.warmup)
     torch.cuda.synchronize()
