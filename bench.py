@@ -86,20 +86,23 @@ def build_workload(name):
     return workloads.c5_fp8()
 
 
-def measured_traffic(workload: str, root: str | None = None):
-    """HBM bytes per launch of the measured decode kernel(s) from the committed
+def measured_traffic(workload: str, root: str | None = None,
+                     sources: tuple = ("decode.hip", "tile.h")):
+    """HBM bytes per launch of the measured kernel(s) from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary whose title names exactly this
     workload key ("<case>" or "<case>+cascade"), or None when the kernel
-    sources changed since the counters were taken.  root: the directory with
-    profiles/ (default: this file's)."""
+    sources (the files in `sources`, hashed together) changed since the
+    counters were taken.  root: the directory with profiles/ (default: this
+    file's)."""
     import glob
     import hashlib
     here = root or os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_135_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("decode.hip", "tile.h"):  # the decode kernels' sources
+    for name in sources:
         h.update(open(os.path.join(csrc, name), "rb").read())
     sha = h.hexdigest()
+    field = "+".join(sources) + " sha256"
     for path in sorted(glob.glob(os.path.join(here, "profiles", "*_pmc_traffic.md"))):
         fields = {}
         with open(path) as f:
@@ -110,7 +113,7 @@ def measured_traffic(workload: str, root: str | None = None):
                     fields[k.strip()] = v.strip()
         key = first.split(":", 1)[-1].strip()
         key = key[:-len(" decode step")] if key.endswith(" decode step") else key
-        if key == workload and fields.get("decode.hip+tile.h sha256") == sha:
+        if key == workload and fields.get(field) == sha:
             return int(fields["traffic_bytes_per_launch"]), fields.get("kernel", "")
     return None, None
 
@@ -293,10 +296,33 @@ def bench_chunk_write(args):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    per = e0.elapsed_time(e1) / 1e3 / args.steps
+    eager = e0.elapsed_time(e1) / 1e3 / args.steps
+    # The launch from Python takes about as long as the kernel, so back-to-back
+    # eager launches leave the GPU idle between them; the kernel's own duration
+    # comes from the same launches replayed from a graph (50 per replay).
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        w()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    per_graph = 50
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            w()
+    g.replay()
+    torch.cuda.synchronize()
+    replays = max(1, args.steps // per_graph)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / 1e3 / (replays * per_graph)
     gbps = moved / per / 1e9
-    print(f"[bench] chunk write: {per*1e6:.2f} us per launch back to back, {gbps:.1f} GB/s",
-          file=sys.stderr, flush=True)
+    print(f"[bench] chunk write: {per*1e6:.2f} us per launch replayed from a graph, {gbps:.1f} GB/s "
+          f"({eager*1e6:.2f} us per eager launch back to back)", file=sys.stderr, flush=True)
     res = {
         "metric": "KV write of a 4,096-token bf16 chunk into an E4M3 cache: GB/s moved (read + write)",
         "value": round(moved / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -305,10 +331,12 @@ def bench_chunk_write(args):
         "config": {"workload": "c5_fp8_chunk_write", "tokens": int(T), "num_kv_heads": int(H),
                    "head_dim": int(D), "block_size": case.block_size},
         "bytes_per_call": moved, "write_kernel_us": round(per * 1e6, 3),
+        "eager_launch_us": round(eager * 1e6, 3),
         "ceiling": copy_ceiling(moved),
         "roofline": {"kernel": "kv_write_kernel (bf16 -> E4M3)", "bound": "hbm",
                      "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("c5_fp8_chunk_write", sources=("kv_write.hip", "e4m3.h"))[0]},
     }
     if not args.no_cpu_baseline:
         import ctypes
@@ -387,7 +415,7 @@ def bench_copy_blocks(args):
         "roofline": {"kernel": "copy_blocks_kernel", "bound": "hbm",
                      "achieved": round(moved / (us / 1e6) / 1e9, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(moved / (us / 1e6) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic("cow_block_copy", sources=("copy_blocks.hip",))[0]},
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -33,18 +33,28 @@ __device__ __forceinline__ uint32_t e4m3x4_from_bf16x4(uint32_t w0, uint32_t w1,
          (e4m3_from_f32(x2 * inv) << 16) | (e4m3_from_f32(x3 * inv) << 24);
 }
 
-// The same four codes through gfx950's pack-convert (round to nearest even):
-// inputs are first clamped to +-448, so the instruction never overflows (the
-// saturating behaviour above), and NaN inputs, which the clamp would turn into
-// +-448, are set to 0x7F afterwards.  Equal to the encoder above on every bf16
-// value at several scales (checked exhaustively on the GPU).
+// The same four codes through gfx950's pack-convert (round to nearest even).
+// The inputs are first clamped to +-448 with the NaN-propagating minimum /
+// maximum, so the instruction never overflows (the saturating behaviour above)
+// and a NaN input stays NaN; the convert gives 0x7F or 0xFF for it.  No
+// clamped finite value has all seven low bits set (448 is 0x7E), so those
+// bytes are exactly the NaNs, and clearing their sign bit makes them 0x7F.
+// Equal to the encoder above on every bf16 value at several scales (checked
+// exhaustively on the GPU).
 __device__ __forceinline__ uint32_t e4m3x4_cvt(float y0, float y1, float y2, float y3) {
-  auto c = [](float v) { return __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f); };
+  auto c = [](float v) {
+    return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, -448.0f), 448.0f);
+  };
   uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c(y0), c(y1), 0, false);
   w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c(y2), c(y3), (int)w, true);
-  const uint32_t nan = (__builtin_isnan(y0) ? 0xffu : 0u) | (__builtin_isnan(y1) ? 0xff00u : 0u) |
-                       (__builtin_isnan(y2) ? 0xff0000u : 0u) | (__builtin_isnan(y3) ? 0xff000000u : 0u);
-  return (w & ~nan) | (0x7f7f7f7fu & nan);
+  const uint32_t nan_sign = ((w & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+  return w & ~nan_sign;
+}
+
+// Four bf16 values (two packed dwords, low half first) times inv -> four codes.
+__device__ __forceinline__ uint32_t e4m3x4_cvt_bf16(uint32_t w0, uint32_t w1, float inv) {
+  return e4m3x4_cvt(__uint_as_float(w0 << 16) * inv, __uint_as_float(w0 & 0xffff0000u) * inv,
+                    __uint_as_float(w1 << 16) * inv, __uint_as_float(w1 & 0xffff0000u) * inv);
 }
 
 // Four f32 values -> four E4M3 codes in one dword.

@@ -37,6 +37,13 @@ def test_traffic_summary_is_matched_by_exact_workload_key(bench, tmp_path):
     assert bench.measured_traffic("c3_shared_prefix+cascade", root) == (111, "call")
     assert bench.measured_traffic("c3_shared_prefix", root) == (None, None)
     assert bench.measured_traffic("c2_qwen_decode", root) == (None, None)  # stale hash
+    # another kernel's summary is keyed by its own sources' hash
+    wsha = hashlib.sha256(open(os.path.join(csrc, "copy_blocks.hip"), "rb").read()).hexdigest()
+    (prof / "c_pmc_traffic.md").write_text(
+        "# rocprofv3 PMC byte counters: cow_block_copy\n"
+        f"copy_blocks.hip sha256: {wsha}\nkernel: c\ntraffic_bytes_per_launch: 333\n")
+    assert bench.measured_traffic("cow_block_copy", root, sources=("copy_blocks.hip",)) == (333, "c")
+    assert bench.measured_traffic("cow_block_copy", root) == (None, None)
 
 
 def test_committed_summaries_name_distinct_workloads(bench):

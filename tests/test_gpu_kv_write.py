@@ -30,8 +30,13 @@ def test_c1_f32_write_of_every_token():
     _compare_pools(g, kc, vc, "c1")
 
 
+# head dims 64 / 128 / 256 take the row kernel (power-of-two block sizes by
+# shift, others by division); 96 takes the general kernel
 @pytest.mark.parametrize("elem,bs,H,D", [("bf16", 16, 4, 128), ("bf16", 32, 8, 64),
-                                         ("f32", 16, 2, 128), ("bf16", 64, 1, 128)])
+                                         ("f32", 16, 2, 128), ("bf16", 64, 1, 128),
+                                         ("bf16", 24, 3, 128), ("f32", 12, 2, 64),
+                                         ("bf16", 16, 2, 96), ("f32", 8, 2, 256),
+                                         ("bf16", 16, 2, 256)])
 def test_random_slots_with_padding(elem, bs, H, D):
     rng = np.random.default_rng(bs * 7 + H)
     NB, T = 97, 700
@@ -56,23 +61,27 @@ def test_random_slots_with_padding(elem, bs, H, D):
     _compare_pools(g, okc, ovc, f"{elem} bs{bs}")
 
 
-@pytest.mark.parametrize("scale", [1.0, 0.0173, 1.0 / 448.0, 3.5, 2.0 ** -10, 0.3])
+# 1e-39 is a subnormal scale: 1 / scale overflows to inf in f32, so zeros
+# quantize to NaN (0x7F); head dim 96 takes the general kernel
+@pytest.mark.parametrize("scale", [1.0, 0.0173, 1.0 / 448.0, 3.5, 2.0 ** -10, 0.3, 1e-39])
 @pytest.mark.parametrize("elem", ["bf16", "f32"])
-def test_e4m3_quantizing_write_over_every_bf16_value(scale, elem):
-    # all 65536 bf16 bit patterns (NaN, inf, subnormals, both zeros) as one
-    # head-dim-128 row per token, quantized with the per-tensor scale
-    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+@pytest.mark.parametrize("bs,D", [(16, 128), (12, 64), (32, 256), (16, 96)])
+def test_e4m3_quantizing_write_over_every_bf16_value(scale, elem, bs, D):
+    # all 65536 bf16 bit patterns (NaN, inf, subnormals, both zeros) as rows of
+    # D values, one per token, quantized with the per-tensor scale
+    T = -(-65536 // D)  # rows of D values covering every pattern (wrapping around)
+    bits = (np.arange(T * D, dtype=np.uint32) % 65536).astype(np.uint16)
     if elem == "f32":
         vals = workloads.bf16_to_f32(bits)
     else:
         vals = bits
-    k = vals.reshape(512, 1, 128)
+    k = vals.reshape(T, 1, D)
     v = k[::-1].copy()
-    NB, bs = 40, 16
-    slots = np.random.default_rng(1).choice(NB * bs, size=512, replace=False).astype(np.int32)
-    kc = np.full((NB, 1, bs, 128), 0x7F, np.uint8)
+    NB = (T + bs - 1) // bs + 8
+    slots = np.random.default_rng(1).choice(NB * bs, size=T, replace=False).astype(np.int32)
+    kc = np.full((NB, 1, bs, D), 0x7F, np.uint8)
     vc = kc.copy()
-    case = workloads.PagedCase(name="e4m3", cache_dtype="fp8_e4m3", q=np.zeros((0, 1, 128), np.uint16),
+    case = workloads.PagedCase(name="e4m3", cache_dtype="fp8_e4m3", q=np.zeros((0, 1, D), np.uint16),
                                key_cache=kc, value_cache=vc,
                                block_tables=np.zeros((0, 1), np.int32),
                                context_lens=np.zeros(0, np.int32), block_size=bs, scale=1.0,
