@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--prefill-rows", type=int, default=0,
                    help="p1: (query, head) rows per wavefront (0 = library default)")
     p.add_argument("--mode", default="auto", choices=["single", "partitioned", "balanced", "auto"])
+    p.add_argument("--seq-order", default="lpt", choices=["lpt", "given"],
+                   help="start order of the single pass / partitioned sequences: longest first "
+                        "(the library's pkv_decode_order) or the batch's own")
     p.add_argument("--partition", type=int, default=512, help="tokens per partition (partitioned)")
     p.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (0 = default)")
     p.add_argument("--workers", type=int, default=0, help="balanced workers (0 = default)")
@@ -690,9 +693,15 @@ def main():
     shared = pkv.tables_share_blocks(case.block_tables, case.context_lens, case.block_size,
                                      skip_blocks=prefix_len // case.block_size)
     stream_kv = args.kv_hint == "stream" or (args.kv_hint == "auto" and not shared)
+    # the single pass starts the sequences longest first: the order comes from
+    # the host's lengths (once per step, shared by every layer), made before
+    # the timed region like the tables themselves
+    order = None
+    if args.seq_order == "lpt":
+        order = torch.from_numpy(pkv.decode_order(case.context_lens)).to(q.device)
     dkw = dict(k_scale=case.k_scale, v_scale=case.v_scale, mode=args.mode,
                partition_size=args.partition, waves_per_group=args.waves,
-               num_workers=args.workers, workspace=ws, stream_kv=stream_kv)
+               num_workers=args.workers, workspace=ws, stream_kv=stream_kv, seq_order=order)
 
     if prefix_len:
         dkw["mode"] = "auto"
@@ -846,6 +855,7 @@ def main():
             "shared_prefix_tokens": prefix_len or None,
             "tables_share_blocks": bool(shared),
             "kv_stream_hint": bool(stream_kv),
+            "seq_order": args.seq_order,
         },
         "kv_bytes_per_step": kv,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

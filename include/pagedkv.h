@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 9
+#define PKV_ABI_VERSION 10
 #define PKV_MAX_DIMS 4
 
 typedef enum {
@@ -145,6 +145,17 @@ typedef struct {
                                not needed for SINGLE_PASS */
   size_t workspace_bytes;
   int32_t flags;            /* PKV_DECODE_* flags below, or 0 */
+  const int32_t* seq_order; /* SINGLE_PASS / PARTITIONED (also AUTO when it picks the single
+                               pass): NULL, or device int32 [num_seqs], a permutation of
+                               0..num_seqs-1 giving the order in which the sequences'
+                               workgroups start.  Longest context first (pkv_decode_order)
+                               keeps a long sequence from starting last and running alone
+                               when the lengths vary.  Only the schedule changes: results
+                               are bit-identical for every permutation.  An entry outside
+                               [0, num_seqs) makes its workgroups exit, and a repeated
+                               entry leaves another sequence's rows unwritten
+                               (pkv_validate_seq_order checks a host copy).  BALANCED and
+                               the shared-prefix calls ignore it. */
 } pkv_decode_opts;
 
 /* opts->flags: launch only the streaming kernel and leave its partial states
@@ -457,6 +468,16 @@ size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, in
                                                             const pkv_decode_opts* opts);
 
 /*
+ * Longest-context-first order of a batch, on HOST arrays, for
+ * pkv_decode_opts.seq_order: order[i] is the sequence with the i-th longest
+ * context, ties in index order.  A list schedule that starts the longest jobs
+ * first ends close to the average load; with the sequences in their given
+ * order a long one can start last and run alone.  Returns PKV_OK,
+ * PKV_ERR_NULL or PKV_ERR_SHAPE (num_seqs < 0).
+ */
+pkv_status pkv_decode_order(const int32_t* context_lens, int32_t num_seqs, int32_t* order);
+
+/*
  * Opt-in host-side checks of the caller contract, on HOST copies.
  * pkv_validate_slots: every slot < num_blocks * block_size and no slot
  *   repeated among the non-negative ones.
@@ -489,6 +510,8 @@ pkv_status pkv_validate_prefill_inputs(const int32_t* query_start_loc, const int
 pkv_status pkv_validate_shared_prefix(const int32_t* block_tables, const int32_t* context_lens,
                                       int32_t num_seqs, int32_t max_blocks_per_seq,
                                       int64_t num_blocks, int32_t block_size, int32_t prefix_len);
+/* pkv_validate_seq_order: a permutation of 0..num_seqs-1. */
+pkv_status pkv_validate_seq_order(const int32_t* seq_order, int32_t num_seqs);
 /* pkv_validate_block_ids: every id >= 0 is < num_blocks and none repeats. */
 pkv_status pkv_validate_block_ids(const int32_t* block_ids, int64_t num_ids, int64_t num_blocks);
 /* pkv_validate_block_pairs: rows with both ids >= 0 name blocks < num_blocks,

@@ -29,9 +29,10 @@ EXPORTED = (
     "pkv_validate_block_ids", "paged_attention_decode_shared_prefix",
     "paged_attention_decode_shared_prefix_workspace_bytes", "pkv_validate_shared_prefix",
     "pkv_read_probe_blocks", "pkv_read_probe", "paged_attention_decode_shared_prefix_append",
-    "paged_attention_decode_noalloc", "pkv_noalloc_scratch_bytes",
+    "paged_attention_decode_noalloc", "pkv_noalloc_scratch_bytes", "pkv_decode_order",
+    "pkv_validate_seq_order",
 )
-ABI_VERSION = 9
+ABI_VERSION = 10
 DECODE_DEFER_MERGE = 1
 DECODE_STREAM_KV = 2
 
@@ -62,6 +63,7 @@ class PkvDecodeOpts(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("flags", ctypes.c_int32),
+        ("seq_order", ctypes.c_void_p),
     ]
 
 
@@ -74,12 +76,15 @@ DECODE_MODES = {"single": 0, "partitioned": 1, "balanced": 2, "auto": 3}
 
 def decode_opts(mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
                 num_workers: int = 0, defer_merge: bool = False,
-                stream_kv: bool = False) -> PkvDecodeOpts:
+                stream_kv: bool = False, seq_order=None) -> PkvDecodeOpts:
     """Options struct; mode None means "partitioned" if partition_size > 0, else "auto".
 
     stream_kv: the batch shares no block between sequences (every refcount 1,
     see BlockPool.shares_blocks), so the pool reads may stream past the caches
-    (PKV_DECODE_STREAM_KV); results are bit-identical either way."""
+    (PKV_DECODE_STREAM_KV); results are bit-identical either way.
+    seq_order: None, or a contiguous int32 GPU tensor [S], a permutation of
+    the sequences giving the order in which the single pass starts them
+    (decode_order: longest first); results are bit-identical either way."""
     if mode is None:
         mode = "partitioned" if partition_size > 0 else "auto"
     o = PkvDecodeOpts()
@@ -88,7 +93,31 @@ def decode_opts(mode: str | None = None, partition_size: int = 0, waves_per_grou
     o.waves_per_group = int(waves_per_group)
     o.num_workers = int(num_workers)
     o.flags = (DECODE_DEFER_MERGE if defer_merge else 0) | (DECODE_STREAM_KV if stream_kv else 0)
+    if seq_order is not None:
+        if (seq_order.device.type != "cuda" or seq_order.dim() != 1 or not seq_order.is_contiguous()
+                or str(seq_order.dtype) != "torch.int32"):
+            raise ValueError("seq_order must be a contiguous int32 GPU tensor [num_seqs]")
+        o.seq_order = seq_order.data_ptr() if seq_order.numel() else None
     return o
+
+
+def decode_order(context_lens: np.ndarray) -> np.ndarray:
+    """Longest-context-first order of a batch (host lengths) for seq_order:
+    element i is the sequence with the i-th longest context, ties in index
+    order (the library's pkv_decode_order)."""
+    n = np.ascontiguousarray(context_lens, dtype=np.int32)
+    order = np.empty(n.size, np.int32)
+    _check(load().pkv_decode_order(n.ctypes.data_as(ctypes.c_void_p), n.size,
+                                   order.ctypes.data_as(ctypes.c_void_p)))
+    return order
+
+
+def validate_seq_order(seq_order: np.ndarray, num_seqs: int) -> None:
+    """Host check that seq_order is a permutation of 0..num_seqs-1; raises PagedKVError."""
+    o = np.ascontiguousarray(seq_order, dtype=np.int32)
+    if o.shape != (num_seqs,):
+        raise ValueError(f"seq_order must have shape ({num_seqs},)")
+    _check(load().pkv_validate_seq_order(o.ctypes.data_as(ctypes.c_void_p), num_seqs))
 
 
 _lib = None
@@ -154,6 +183,10 @@ def load():
     lib.paged_kv_scatter_blocks.restype = ctypes.c_int
     lib.pkv_validate_block_ids.argtypes = [P, ctypes.c_int64, ctypes.c_int64]
     lib.pkv_validate_block_ids.restype = ctypes.c_int
+    lib.pkv_decode_order.argtypes = [P, ctypes.c_int32, P]
+    lib.pkv_decode_order.restype = ctypes.c_int
+    lib.pkv_validate_seq_order.argtypes = [P, ctypes.c_int32]
+    lib.pkv_validate_seq_order.restype = ctypes.c_int
     lib.paged_attention_decode_shared_prefix.argtypes = [T, T, T, T, T, T, ctypes.c_int32,
                                                          ctypes.c_float, ctypes.c_int32,
                                                          ctypes.POINTER(PkvDecodeOpts), P]
@@ -263,16 +296,17 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
                            scale: float, block_size: int, *, k_scale: float = 1.0,
                            v_scale: float = 1.0, mode: str | None = None, partition_size: int = 0,
                            waves_per_group: int = 0, num_workers: int = 0, workspace=None,
-                           stream_kv: bool = False, stream=None):
+                           stream_kv: bool = False, seq_order=None, stream=None):
     """Decode attention over the paged pools into ``out`` [S, Hq, D].
 
     mode: "single", "partitioned" (needs partition_size), "balanced" or "auto";
     None picks "partitioned" when partition_size > 0, else "auto".  The split
     modes need a workspace (a uint8 device tensor of at least
     decode_workspace_bytes(...)); it is allocated here when not given.
-    stream_kv: see decode_opts."""
+    stream_kv, seq_order: see decode_opts."""
     _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
-    opts = decode_opts(mode, partition_size, waves_per_group, num_workers, stream_kv=stream_kv)
+    opts = decode_opts(mode, partition_size, waves_per_group, num_workers, stream_kv=stream_kv,
+                       seq_order=seq_order)
     ws = _workspace_for(opts, q, key_cache, block_tables, block_size, workspace)
     dout, dq = describe(out), describe(q)
     dkc, dvc = describe(key_cache, k_scale), describe(value_cache, v_scale)
@@ -290,12 +324,14 @@ def paged_attention_decode_noalloc(out, q, key_cache, value_cache, block_tables,
                                    scale: float, block_size: int, *, k_scale: float = 1.0,
                                    v_scale: float = 1.0, mode: str | None = None,
                                    partition_size: int = 0, waves_per_group: int = 0,
-                                   num_workers: int = 0, stream_kv: bool = False, stream=None):
+                                   num_workers: int = 0, stream_kv: bool = False, seq_order=None,
+                                   stream=None):
     """paged_attention_decode with the library's fixed device scratch as the
     split workspace: allocates nothing (see include/pagedkv.h; calls that
     overlap on one GPU race)."""
     _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
-    opts = decode_opts(mode, partition_size, waves_per_group, num_workers, stream_kv=stream_kv)
+    opts = decode_opts(mode, partition_size, waves_per_group, num_workers, stream_kv=stream_kv,
+                       seq_order=seq_order)
     dout, dq = describe(out), describe(q)
     dkc, dvc = describe(key_cache, k_scale), describe(value_cache, v_scale)
     dt, dl = describe(block_tables), describe(context_lens)
@@ -316,13 +352,14 @@ def paged_attention_decode_append(out, q, k, v, slot_mapping, key_cache, value_c
                                   k_scale: float = 1.0, v_scale: float = 1.0,
                                   mode: str | None = None, partition_size: int = 0,
                                   waves_per_group: int = 0, num_workers: int = 0, workspace=None,
-                                  stream_kv: bool = False, stream=None):
+                                  stream_kv: bool = False, seq_order=None, stream=None):
     """One decode step in one call: write each sequence's new token (k, v
     [S, Hkv, D] at slot_mapping [S]) and attend (see include/pagedkv.h).
     Equal to paged_kv_write followed by paged_attention_decode when every
     slot is position context_lens[s]-1 of its own sequence."""
     _same_device(out, q, k, v, slot_mapping, key_cache, value_cache, block_tables, context_lens)
-    opts = decode_opts(mode, partition_size, waves_per_group, num_workers, stream_kv=stream_kv)
+    opts = decode_opts(mode, partition_size, waves_per_group, num_workers, stream_kv=stream_kv,
+                       seq_order=seq_order)
     ws = _workspace_for(opts, q, key_cache, block_tables, block_size, workspace)
     d = [describe(out), describe(q), describe(k), describe(v), describe(slot_mapping),
          describe(key_cache, k_scale), describe(value_cache, v_scale), describe(block_tables),
@@ -638,21 +675,21 @@ class DecodeLaunch:
                  block_size: int, *, k_scale: float = 1.0, v_scale: float = 1.0,
                  mode: str | None = None, partition_size: int = 0, waves_per_group: int = 0,
                  num_workers: int = 0, workspace=None, append=None, defer_merge: bool = False,
-                 prefix_len: int = 0, stream_kv: bool = False):
+                 prefix_len: int = 0, stream_kv: bool = False, seq_order=None):
         _same_device(out, q, key_cache, value_cache, block_tables, context_lens)
         if prefix_len and defer_merge:
             raise ValueError("a shared-prefix decode takes no deferred merge")
         if prefix_len and mode is None:
             mode = "auto"
         self._opts = decode_opts(mode, partition_size, waves_per_group, num_workers, defer_merge,
-                                 stream_kv)
+                                 stream_kv, seq_order)
         self._merge_opts = decode_opts(mode, partition_size, waves_per_group, num_workers)
         self.workspace = _workspace_for(self._opts, q, key_cache, block_tables, block_size,
                                         workspace, prefix_len)
         _workspace_for(self._merge_opts, q, key_cache, block_tables, block_size, self.workspace,
                        prefix_len)
         self._prefix = int(prefix_len)
-        self._keep = (out, q, key_cache, value_cache, block_tables, context_lens, append)
+        self._keep = (out, q, key_cache, value_cache, block_tables, context_lens, append, seq_order)
         self._d = [describe(out), describe(q), describe(key_cache, k_scale),
                    describe(value_cache, v_scale), describe(block_tables), describe(context_lens)]
         self._refs = [ctypes.byref(d) for d in self._d]

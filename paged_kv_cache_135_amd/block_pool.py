@@ -339,6 +339,12 @@ class BlockPool:
     def context_lens(self, seqs) -> np.ndarray:
         return np.array([self._seqs[q].num_tokens for q in seqs], dtype=np.int32)
 
+    def decode_order(self, seqs) -> np.ndarray:
+        """Positions of ``seqs`` (as batched by block_tables / context_lens),
+        longest context first, ties in batch order: the decode's seq_order
+        (the same order as the library's pkv_decode_order)."""
+        return np.argsort(-self.context_lens(seqs).astype(np.int64), kind="stable").astype(np.int32)
+
     def stats(self) -> dict:
         """Live-KV fraction (tokens held / slots of blocks in use, each physical
         block counted once) and per-sequence tail waste."""

@@ -647,6 +647,8 @@ pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
 
   if (opts && (opts->flags & ~(PKV_DECODE_DEFER_MERGE | PKV_DECODE_STREAM_KV)) != 0)
     return fail(PKV_ERR_UNSUPPORTED, "opts->flags 0x%x: unknown PKV_DECODE_* bits", (unsigned)opts->flags);
+  if (opts && reinterpret_cast<uintptr_t>(opts->seq_order) % 4 != 0)
+    return fail(PKV_ERR_LAYOUT, "opts->seq_order must be 4-byte aligned");
   Plan p;
   PKV_TRY(plan(opts, S, Hq, Hkv, maxb, bs, &p, prefix_len));
   pkv::DecodeArgs a{};
@@ -674,6 +676,9 @@ pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
   a.vc = value_cache->data;
   a.tables = static_cast<const int32_t*>(block_tables->data);
   a.lens = static_cast<const int32_t*>(context_lens->data);
+  // the start order only concerns the grid of the single pass / partitioned kernel
+  if (opts && opts->seq_order && prefix_len == 0 && p.mode != PKV_DECODE_BALANCED)
+    a.seq_order = opts->seq_order;
   a.num_seqs = (int32_t)S;
   a.num_q_heads = (int32_t)Hq;
   a.num_kv_heads = (int32_t)Hkv;
@@ -894,6 +899,29 @@ pkv_status pkv_validate_decode_inputs(const int32_t* block_tables, const int32_t
         return fail(PKV_ERR_RANGE, "block_tables[%d][%lld] = %d outside [0, %lld)", s, (long long)j,
                     b, (long long)num_blocks);
     }
+  }
+  return ok();
+}
+
+pkv_status pkv_decode_order(const int32_t* context_lens, int32_t num_seqs, int32_t* order) {
+  if (num_seqs < 0) return fail(PKV_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > 0 && (!context_lens || !order)) return fail(PKV_ERR_NULL, "NULL input");
+  for (int32_t s = 0; s < num_seqs; ++s) order[s] = s;
+  std::stable_sort(order, order + num_seqs,
+                   [&](int32_t x, int32_t y) { return context_lens[x] > context_lens[y]; });
+  return ok();
+}
+
+pkv_status pkv_validate_seq_order(const int32_t* seq_order, int32_t num_seqs) {
+  if (num_seqs < 0) return fail(PKV_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > 0 && !seq_order) return fail(PKV_ERR_NULL, "seq_order is NULL");
+  std::vector<char> seen((size_t)num_seqs, 0);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t s = seq_order[i];
+    if (s < 0 || s >= num_seqs)
+      return fail(PKV_ERR_RANGE, "seq_order[%d] = %d outside [0, %d)", i, s, num_seqs);
+    if (seen[(size_t)s]) return fail(PKV_ERR_RANGE, "seq_order[%d] = %d repeats", i, s);
+    seen[(size_t)s] = 1;
   }
   return ok();
 }

@@ -142,7 +142,10 @@ template <int CT, int D, int NW, int NBUF, bool APPEND, bool NT>
 __global__ __launch_bounds__(NW * 64, (CT == PKV_FP8_E4M3 && !APPEND) ? 4 : 1) void decode_partition_kernel(DecodeArgs a) {
   using T = Tile<CT, D>;
   constexpr int VE = T::VE;
-  const int part = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
+  const int part = blockIdx.x, hk = blockIdx.y;
+  // grid row z takes sequence seq_order[z] (e.g. longest first), or z
+  const int s = a.seq_order ? a.seq_order[blockIdx.z] : (int)blockIdx.z;
+  if (s < 0 || s >= a.num_seqs) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int ctx = a.lens[s];

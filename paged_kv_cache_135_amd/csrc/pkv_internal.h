@@ -39,6 +39,7 @@ struct DecodeArgs {
   const void* vc;
   const int32_t* tables;
   const int32_t* lens;
+  const int32_t* seq_order;  // single pass / partitioned: sequence of grid row z, or null
   // split workspace.  Partitioned: [S][Hq][NP][D] and [S][Hq][NP][2].
   // Balanced: slot = worker + segment, [slots][G][D] and [slots][G][2], plus
   // per segment (sequence, KV head) the first and last worker of its partials.

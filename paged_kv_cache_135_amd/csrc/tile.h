@@ -48,6 +48,14 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // E4M3 pairs -> f32 (exact): bytes 0,1 or 2,3 of a dword.
 __device__ __forceinline__ f32x2 fp8x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, false); }
 __device__ __forceinline__ f32x2 fp8x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, true); }
+// E4M3 pairs -> packed bf16 pairs in one instruction (gfx950's scaled convert
+// with scale 1: every E4M3 value is a bf16 value, so it is exact).
+__device__ __forceinline__ uint32_t bf16x2_from_fp8x2_lo(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t bf16x2_from_fp8x2_hi(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
 // two f32 holding bf16-exact values -> packed bf16 pair (truncation is exact)
 __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), kSelHi);
@@ -233,9 +241,8 @@ struct Tile<PKV_FP8_E4M3, D> {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t w0 = k[c][2 * h], w1 = k[c][2 * h + 1];
-        const f32x2 a = fp8x2_lo(w0), b = fp8x2_hi(w0), e = fp8x2_lo(w1), f = fp8x2_hi(w1);
-        const u32x4 kb = {pack_exact(a[0], a[1]), pack_exact(b[0], b[1]),
-                          pack_exact(e[0], e[1]), pack_exact(f[0], f[1])};
+        const u32x4 kb = {bf16x2_from_fp8x2_lo(w0), bf16x2_from_fp8x2_hi(w0),
+                          bf16x2_from_fp8x2_lo(w1), bf16x2_from_fp8x2_hi(w1)};
         s = mfma_bf16_k32(kb, qf.q[2 * c + h], s);
       }
     }

@@ -74,20 +74,23 @@ class GpuCase:
         if c.k_new is not None:
             self.write(c.k_new, c.v_new, c.slot_mapping)
 
-    def decode(self, partition_size=0, waves=0, out=None, mode=None, workers=0, stream_kv=False):
+    def decode(self, partition_size=0, waves=0, out=None, mode=None, workers=0, stream_kv=False,
+               seq_order=None):
+        """seq_order: None, or a host int32 permutation (copied to the GPU)."""
         c = self.case
         out = self.out if out is None else out
+        order = None if seq_order is None else dev(np.ascontiguousarray(seq_order, np.int32))
         pkv.paged_attention_decode(out, self.q, self.kc, self.vc, self.tables, self.lens, c.scale,
                                    c.block_size, k_scale=c.k_scale, v_scale=c.v_scale, mode=mode,
                                    partition_size=partition_size, waves_per_group=waves,
-                                   num_workers=workers, stream_kv=stream_kv)
+                                   num_workers=workers, stream_kv=stream_kv, seq_order=order)
         return out
 
-    def decode_mode(self, m, stream_kv=False):
+    def decode_mode(self, m, stream_kv=False, seq_order=None):
         """m = (mode, partition_size, waves_per_group, num_workers)."""
         mode, part, waves, workers = m
         return self.decode(partition_size=part, waves=waves, mode=mode, workers=workers,
-                           stream_kv=stream_kv)
+                           stream_kv=stream_kv, seq_order=seq_order)
 
 
 def oracle_caches(case: PagedCase, tokens_mask=None):

@@ -471,3 +471,38 @@ def test_noalloc_refuses_what_the_scratch_cannot_hold():
     assert call(_decode_args(opts=o)) == 5  # PKV_ERR_UNSUPPORTED
     # validation errors come back as for paged_attention_decode
     assert call(_decode_args(out=None)) == 1
+
+
+def test_decode_order_is_longest_first_with_ties_in_index_order():
+    rng = np.random.default_rng(11)
+    for S in (0, 1, 7, 512, 1000):
+        lens = rng.integers(0, 40, size=S).astype(np.int32)  # many ties
+        got = B.decode_order(lens)
+        want = np.argsort(-lens.astype(np.int64), kind="stable")
+        assert np.array_equal(got, want)
+        if S:
+            assert np.all(np.diff(lens[got].astype(np.int64)) <= 0)
+            B.validate_seq_order(got, S)
+
+
+def test_seq_order_validator_and_decode_refusal():
+    B.validate_seq_order(np.array([2, 0, 1], np.int32), 3)
+    for bad in ([0, 0, 1], [0, 1, 3], [-1, 0, 1]):
+        with pytest.raises(B.PagedKVError) as e:
+            B.validate_seq_order(np.array(bad, np.int32), 3)
+        assert e.value.status == 8
+    with pytest.raises(ValueError):
+        B.validate_seq_order(np.array([0, 1], np.int32), 3)
+    o = _opts(mode=0)
+    o.seq_order = FAKE + (7 << 20) + 2  # misaligned device pointer: refused before any launch
+    assert _decode(_decode_args(opts=o)) == 4
+
+
+def test_block_pool_decode_order_matches_the_library():
+    from paged_kv_cache_135_amd import BlockPool
+    pool = BlockPool(num_blocks=64, block_size=16)
+    lens = [5, 40, 40, 17, 0, 33]
+    for i, n in enumerate(lens):
+        pool.allocate(i, n)
+    seqs = [3, 1, 5, 2, 0, 4]
+    assert np.array_equal(pool.decode_order(seqs), B.decode_order(pool.context_lens(seqs)))

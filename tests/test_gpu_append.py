@@ -125,6 +125,26 @@ def test_append_matches_write_then_decode(name, mode):
     gu.assert_close(gu.host(got), ref, case.cache_dtype, f"{name} {_mid(mode)}")
 
 
+@pytest.mark.parametrize("mode", [("single", 0, 4, 0), ("partitioned", 32, 2, 0)], ids=_mid)
+@pytest.mark.parametrize("name", list(SMALL))
+def test_append_with_seq_order(name, mode):
+    """The one-call step with the sequences started longest first: the same
+    pools and the same output bits as in the given order."""
+    case, k, v, slots, (okc, ovc, ref) = _prepared(name)
+    g1 = _pre_step(case)
+    base = _append(g1, k, v, slots, mode)
+    g2 = _pre_step(case)
+    c = g2.case
+    got = torch.empty_like(g2.q)
+    order = gu.dev(pkv.decode_order(case.context_lens))
+    pkv.paged_attention_decode_append(got, g2.q, gu.dev(k), gu.dev(v), gu.dev(slots), g2.kc, g2.vc,
+                                      g2.tables, g2.lens, c.scale, c.block_size, seq_order=order,
+                                      **_kw(c, mode))
+    torch.cuda.synchronize()
+    assert _same_pools(g2, okc, ovc)
+    assert np.array_equal(_bits(gu.host(got)), _bits(gu.host(base))), "order changed the output"
+
+
 @pytest.mark.parametrize("mode", [("single", 0, 4, 0), ("partitioned", 32, 2, 0),
                                   ("balanced", 0, 0, 5)], ids=_mid)
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8_e4m3"])

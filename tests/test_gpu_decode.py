@@ -10,6 +10,7 @@ import math
 import numpy as np
 import pytest
 
+import paged_kv_cache_135_amd as pkv
 import workloads
 from tests import gpu_util as gu
 
@@ -177,13 +178,38 @@ def test_c5_e4m3_whole_pool_bit_exact():
     assert np.array_equal(gu.host(g.vc), vc), "value pool differs from the oracle's write"
 
 
-@pytest.mark.parametrize("mode,stream", [(("auto", 0, 0, 0), True), (("balanced", 0, 0, 0), False),
-                                         (("partitioned", 512, 4, 0), False)])
-def test_c5_e4m3_every_row(mode, stream):
+# the first case is the launch the benchmark times: auto (single pass), the
+# streaming hint and the sequences started longest first
+@pytest.mark.parametrize("mode,stream,lpt", [(("auto", 0, 0, 0), True, True),
+                                             (("auto", 0, 0, 0), True, False),
+                                             (("balanced", 0, 0, 0), False, False),
+                                             (("partitioned", 512, 4, 0), False, True)])
+def test_c5_e4m3_every_row(mode, stream, lpt):
     case, g, _, _, ref = _fp8_case()
-    got = gu.host(g.decode_mode(mode, stream_kv=stream))
+    order = pkv.decode_order(case.context_lens) if lpt else None
+    got = gu.host(g.decode_mode(mode, stream_kv=stream, seq_order=order))
     assert got.shape == (512, 32, 128)
-    gu.assert_close(got, ref, "fp8_e4m3", f"c5 {_mid(mode)} stream={stream}")
+    gu.assert_close(got, ref, "fp8_e4m3", f"c5 {_mid(mode)} stream={stream} lpt={lpt}")
+
+
+ORDER_MODES = [("single", 0, 4, 0), ("single", 0, 1, 0), ("auto", 0, 0, 0),
+               ("partitioned", 32, 2, 0), ("balanced", 0, 0, 5)]
+
+
+@pytest.mark.parametrize("mode", ORDER_MODES, ids=_mid)
+@pytest.mark.parametrize("name", list(SMALL))
+def test_seq_order_changes_no_bit(name, mode):
+    """Starting the sequences in another order (longest first, or a random
+    permutation) only reschedules the workgroups: every output bit is the same
+    (the balanced split ignores the order)."""
+    case, g, _ = _prepared(name)
+    base = gu.host(g.decode_mode(mode)).copy()
+    S = case.context_lens.size
+    for order in (pkv.decode_order(case.context_lens),
+                  np.random.default_rng(S).permutation(S).astype(np.int32)):
+        pkv.validate_seq_order(order, S)
+        got = gu.host(g.decode_mode(mode, seq_order=order))
+        assert np.array_equal(got.view(np.uint8), base.view(np.uint8)), f"{name} {_mid(mode)} {order}"
 
 
 def test_many_sequences_take_the_long_scan_path():
