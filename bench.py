@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--prefill-rows", type=int, default=0,
                    help="p1: (query, head) rows per wavefront (0 = library default)")
     p.add_argument("--mode", default="auto", choices=["single", "partitioned", "balanced", "auto"])
+    p.add_argument("--q-heads", type=int, default=0,
+                   help="Qwen-shaped batch with this many query heads over its 4 KV heads "
+                        "(same K/V bytes, another group size; 0 = 28)")
     p.add_argument("--seq-order", default="lpt", choices=["lpt", "given"],
                    help="start order of the single pass / partitioned sequences: longest first "
                         "(the library's pkv_decode_order) or the batch's own")
@@ -74,12 +77,12 @@ def parse():
     return p.parse_args()
 
 
-def build_workload(name):
+def build_workload(name, q_heads: int = 0):
     import workloads
     if name == "c1":
         return workloads.c1_tiny_f32()
     if name == "c2":
-        return workloads.c2_qwen_decode()
+        return workloads.c2_qwen_decode(num_q_heads=q_heads or 28)
     if name == "c3":
         return workloads.c3_shared_prefix()
     if name == "c4":
@@ -169,6 +172,52 @@ def read_ceiling_same_size(stream, nbytes: int, regions: int = 4, reps: int = 20
     del bufs
     return {"value": round(n / s / 1e9, 1), "unit": "GB/s", "bytes": n, "regions": regions,
             "us_per_pass": round(s * 1e6, 2)}
+
+
+def gather_ceiling(case, pools, stream, workers: int = 0, reps: int = 20) -> dict:
+    """The decode's tile gather alone (pkv_tile_gather_probe) over this batch's
+    tiles in the balanced split's order, the same worker count, rotating over
+    the layer pools: mode 0 loads the MFMA operands straight to registers (the
+    decode's way), mode 1 stages every tile through LDS first.  Both read the
+    same words, so their sinks must agree."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_135_amd as pkv
+    H, bs = case.num_kv_heads, case.block_size
+    rows = []
+    for s, n in enumerate(case.context_lens):
+        for h in range(H):
+            for j in range((int(n) + 15) // 16):
+                tok = 16 * j
+                rows.append((int(case.block_tables[s, tok // bs]) * H + h) * bs + tok % bs)
+    tile_rows = torch.tensor(rows, dtype=torch.int32, device="cuda")
+    W = workers or 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"workers": W, "tiles": len(rows), "bytes": len(rows) * 8192}
+    sinks = {}
+    for mode, name in ((0, "direct"), (1, "lds_staged")):
+        sink = pkv.tile_gather_probe(pools[0][0], pools[0][1], tile_rows, W, mode, stream=stream)
+        for kc, vc in pools:
+            pkv.tile_gather_probe(kc, vc, tile_rows, W, mode, sink, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            kc, vc = pools[i % len(pools)]
+            pkv.tile_gather_probe(kc, vc, tile_rows, W, mode, sink, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        pkv.tile_gather_probe(pools[0][0], pools[0][1], tile_rows, W, mode, sink, stream=stream)
+        torch.cuda.synchronize()
+        x = 0
+        for w in sink.cpu().numpy().view(np.uint32):
+            x ^= int(w)
+        sinks[name] = x
+        out[name + "_us"] = round(us, 2)
+        out[name + "_gbps"] = round(out["bytes"] / us / 1e3, 1)
+    out["same_words"] = sinks["direct"] == sinks["lds_staged"]
+    return out
 
 
 def _oracle_steps(case, seconds):
@@ -643,7 +692,10 @@ def main():
     if args.workload == "swap":
         return bench_swap(args)
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
-    case = build_workload(args.workload)
+    if args.q_heads and args.workload != "c2":
+        print("--q-heads applies to the Qwen-shaped workload (c2) only", file=sys.stderr)
+        return 2
+    case = build_workload(args.workload, args.q_heads)
     pool_bytes = case.key_cache.nbytes * 2
     layers = args.layers or max(2, math.ceil(4 * MALL_BYTES / pool_bytes))
     layers = min(layers, 16)
@@ -817,6 +869,8 @@ def main():
     call_achieved = roof_bytes / call_s / 1e9
     same = read_ceiling_same_size(stream, roof_bytes)
     ceiling["same_size"] = dict(same, frac_of_ceiling=round(achieved / same["value"], 4))
+    if case.cache_dtype == "bf16" and case.head_dim == 128 and not prefix_len:
+        ceiling["tile_gather"] = gather_ceiling(case, pools, stream, args.workers or 0)
     print(f"[bench] step {step}: decode call {call_s*1e6:.1f} us back to back "
           f"({call_ms.mean()*1e3:.1f} us between events around each, p10 "
           f"{np.percentile(call_ms,10)*1e3:.1f}, p90 {np.percentile(call_ms,90)*1e3:.1f}): "

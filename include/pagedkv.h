@@ -451,6 +451,25 @@ pkv_status paged_kv_scatter_blocks(const pkv_tensor* in_k, const pkv_tensor* in_
 int32_t pkv_read_probe_blocks(void);
 pkv_status pkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream);
 
+/* Measurement support, not a step of the method: the gather ceiling of the
+ * decode's tile stream on a bf16, head-dim-128 pool (rows of 256 bytes).
+ * tile_rows (device int32 [num_tiles]) names the first of 16 consecutive pool
+ * rows of each tile (row = (block * num_kv_heads + head) * block_size +
+ * offset); K comes from key_cache, V from value_cache, at the same rows.
+ * `workers` wavefronts (4 per workgroup) each read an equal contiguous run of
+ * the list, the balanced split without its arithmetic:
+ *   mode 0: the decode's own operand loads, straight into registers;
+ *   mode 1: each tile staged through LDS first (global-to-LDS copies, 1 KB
+ *           contiguous per instruction, two tiles in flight per wavefront),
+ *           then the same operands read from LDS.
+ * sink[b] gets the XOR of what workgroup b read; sink holds (workers + 3) / 4
+ * words.  A row outside [0, num_rows - 16] reads row 0 instead.  Device
+ * pointers (PKV_ERR_LAYOUT), 16-byte aligned pools (PKV_ERR_SHAPE), workers in
+ * [1, 2^20] and mode 0 or 1 (PKV_ERR_UNSUPPORTED).  Asynchronous on hip_stream. */
+pkv_status pkv_tile_gather_probe(const void* key_cache, const void* value_cache,
+                                 const int32_t* tile_rows, int64_t num_tiles, int64_t num_rows,
+                                 int32_t workers, int32_t mode, uint32_t* sink, void* hip_stream);
+
 /* Workspace bytes paged_attention_decode needs with these sizes and options
  * (0 when none is needed: single pass, or one partition per sequence).
  * Returns 0 as well for invalid arguments. */

@@ -30,7 +30,7 @@ EXPORTED = (
     "paged_attention_decode_shared_prefix_workspace_bytes", "pkv_validate_shared_prefix",
     "pkv_read_probe_blocks", "pkv_read_probe", "paged_attention_decode_shared_prefix_append",
     "paged_attention_decode_noalloc", "pkv_noalloc_scratch_bytes", "pkv_decode_order",
-    "pkv_validate_seq_order",
+    "pkv_validate_seq_order", "pkv_tile_gather_probe",
 )
 ABI_VERSION = 10
 DECODE_DEFER_MERGE = 1
@@ -183,6 +183,9 @@ def load():
     lib.paged_kv_scatter_blocks.restype = ctypes.c_int
     lib.pkv_validate_block_ids.argtypes = [P, ctypes.c_int64, ctypes.c_int64]
     lib.pkv_validate_block_ids.restype = ctypes.c_int
+    lib.pkv_tile_gather_probe.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_int32, P, P]
+    lib.pkv_tile_gather_probe.restype = ctypes.c_int
     lib.pkv_decode_order.argtypes = [P, ctypes.c_int32, P]
     lib.pkv_decode_order.restype = ctypes.c_int
     lib.pkv_validate_seq_order.argtypes = [P, ctypes.c_int32]
@@ -510,6 +513,27 @@ def read_probe(buf, sink=None, *, stream=None):
     _check(lib.pkv_read_probe(ctypes.c_void_p(buf.data_ptr()),
                               buf.numel() * buf.element_size(),
                               ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
+    return sink
+
+
+def tile_gather_probe(key_cache, value_cache, tile_rows, workers: int, mode: int, sink=None, *,
+                      stream=None):
+    """Measurement support: the decode's tile gather alone over a bf16,
+    head-dim-128 pool (see include/pagedkv.h, pkv_tile_gather_probe): mode 0
+    loads the MFMA operands straight to registers, mode 1 stages each tile
+    through LDS first.  tile_rows: int32 GPU tensor of first pool rows.
+    Returns the sink (int32 device tensor, one word per workgroup)."""
+    import torch
+    if key_cache.dtype != torch.bfloat16 or key_cache.shape[-1] != 128:
+        raise ValueError("the gather probe reads bf16 pools of head dim 128")
+    if sink is None:
+        sink = torch.empty((workers + 3) // 4, dtype=torch.int32, device=key_cache.device)
+    num_rows = key_cache.numel() // 128
+    s = stream if stream is not None else torch.cuda.current_stream(key_cache.device)
+    _check(load().pkv_tile_gather_probe(
+        ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
+        ctypes.c_void_p(tile_rows.data_ptr()), tile_rows.numel(), num_rows, int(workers), int(mode),
+        ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
     return sink
 
 

@@ -538,6 +538,26 @@ pkv_status pkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* h
   return ok();
 }
 
+pkv_status pkv_tile_gather_probe(const void* key_cache, const void* value_cache,
+                                 const int32_t* tile_rows, int64_t num_tiles, int64_t num_rows,
+                                 int32_t workers, int32_t mode, uint32_t* sink, void* hip_stream) {
+  if (num_tiles <= 0) return ok();  // nothing to read, nothing launched
+  if (!key_cache || !value_cache || !tile_rows || !sink)
+    return fail(PKV_ERR_NULL, "pkv_tile_gather_probe: null pointer");
+  if (workers < 1 || workers > (1 << 20) || (mode != 0 && mode != 1))
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_tile_gather_probe: workers %d, mode %d", workers, mode);
+  if (reinterpret_cast<uintptr_t>(key_cache) % 16 != 0 || reinterpret_cast<uintptr_t>(value_cache) % 16 != 0 ||
+      num_rows < 16)
+    return fail(PKV_ERR_SHAPE, "pkv_tile_gather_probe: pools must be 16-byte aligned with >= 16 rows");
+  if (!device_memory(key_cache) || !device_memory(value_cache) || !device_memory(tile_rows) ||
+      !device_memory(sink))
+    return fail(PKV_ERR_LAYOUT, "pkv_tile_gather_probe: pointers must be device memory");
+  const hipError_t e = pkv::launch_gather_probe(key_cache, value_cache, tile_rows, num_tiles, num_rows,
+                                                workers, mode, sink, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_tile_gather_probe: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim,
                                               int32_t max_blocks_per_seq, int32_t block_size,

@@ -155,6 +155,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks,
                              hipStream_t stream);
+hipError_t launch_gather_probe(const void* kc, const void* vc, const int32_t* rows, int64_t num_tiles,
+                               int64_t num_rows, int32_t workers, int32_t mode, uint32_t* sink,
+                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // The allocation-free decode's scratch: a fixed device array of kScratchBytes;

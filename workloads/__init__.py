@@ -356,12 +356,16 @@ def c1_tiny_f32() -> PagedCase:
                       scale=1.0 / 8.0, num_blocks=64, fill_via_write=True, new_token_step=False)
 
 
-def c2_qwen_decode(seed: int = 1001, num_seqs: int = 64, block_size: int = 16) -> PagedCase:
+def c2_qwen_decode(seed: int = 1001, num_seqs: int = 64, block_size: int = 16,
+                   num_q_heads: int = 28) -> PagedCase:
     """Qwen2.5-7B-shaped decode layer, bf16: 28 q / 4 KV heads, head dim 128,
-    lengths uniform in [128, 4096], pool sized to fit plus 10% free."""
+    lengths uniform in [128, 4096], pool sized to fit plus 10% free.
+    num_q_heads: another multiple of 4 gives the same K/V with another group
+    size (named c2_qwen_decode_hq<N>)."""
     rng = np.random.default_rng([seed, 99])
     ctx = rng.integers(128, 4097, size=num_seqs)
-    return build_case("c2_qwen_decode", seed=seed, context_lens=ctx, num_q_heads=28,
+    name = "c2_qwen_decode" if num_q_heads == 28 else f"c2_qwen_decode_hq{num_q_heads}"
+    return build_case(name, seed=seed, context_lens=ctx, num_q_heads=num_q_heads,
                       num_kv_heads=4, head_dim=128, block_size=block_size, cache_dtype="bf16",
                       std=0.5, scale=1.0 / math.sqrt(128))
 
