@@ -138,7 +138,8 @@ typedef struct {
   int32_t mode;             /* pkv_decode_mode */
   int32_t partition_size;   /* PARTITIONED: tokens per partition, a positive multiple of 16 */
   int32_t waves_per_group;  /* SINGLE_PASS / PARTITIONED: wavefronts per workgroup walking
-                               disjoint tiles: 0 = library default, else 1, 2, 4 or 8 */
+                               disjoint tiles: 0 = library default (1 for partitions of at
+                               most 512 tokens, else 4), else 1, 2, 4 or 8 */
   int32_t num_workers;      /* BALANCED: wavefronts sharing the work; 0 = library default
                                (4 per compute unit of the current device) */
   void* workspace;          /* device memory, >= paged_attention_decode_workspace_bytes();

@@ -51,12 +51,14 @@ constexpr int kChunkTiles = 1024;  // block ids staged in LDS per pass (4 KiB)
 // Block tables read as constant memory (uniform indices: scalar loads).
 typedef const __attribute__((address_space(4))) int32_t* ctab;
 // Balanced split: work units charged for starting a piece, in tiles.  A piece
-// start (q rows, block ids, the partial write) costs about two bf16 tile times
-// on MI355X; an E4M3 tile streams in half the time, so the same start costs
-// about four of them.
-template <int CT>
-constexpr int piece_cost() {
-  return CT == PKV_FP8_E4M3 ? 4 : CT == PKV_BF16 ? 2 : 1;
+// start (q rows, block ids, the partial write) costs two to three bf16 tile
+// times on MI355X; an E4M3 tile streams in half the time, so the same start
+// costs about four of them.  bf16 takes 3 (Qwen-shaped call: 1 -> 51.2 us,
+// 2 -> 49.8, 3 -> 49.5, 4 -> 50.7), but 2 for the tails of a shared-prefix
+// call, whose many short pairs all end in pieces (256-sequence batch: 110.1 us
+// at 2, 112.1 at 3).
+__host__ __device__ constexpr int piece_cost(int ct, bool cascade) {
+  return ct == PKV_FP8_E4M3 ? 4 : ct == PKV_BF16 ? (cascade ? 2 : 3) : 1;
 }
 
 // The new token's K and V rows of one KV head, one 16-byte chunk per lane
@@ -399,8 +401,8 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
   // readlane instead of a dependent load; longer batches re-read the rest.
   // Sequences with no tokens have no tiles: worker s % W writes their zero rows.
   constexpr int kScanRegs = 8;
-  constexpr int kPieceCost = piece_cost<CT>();
-  auto units = [](uint32_t n) { return n ? n + (uint32_t)kPieceCost : 0u; };
+  const int kPieceCost = piece_cost(CT, a.cascade != 0);
+  auto units = [kPieceCost](uint32_t n) { return n ? n + (uint32_t)kPieceCost : 0u; };
   int creg[kScanRegs];
 #pragma unroll
   for (int i = 0; i < kScanRegs; ++i) creg[i] = 0;
