@@ -161,8 +161,9 @@ pkv_status plan(const pkv_decode_opts* opts, int64_t S, int64_t Hq, int64_t Hkv,
     if (mode != PKV_DECODE_AUTO && mode != PKV_DECODE_BALANCED && opts)
       return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode runs the balanced split: mode must "
                                        "be AUTO or BALANCED");
-    const int64_t pairs = S * Hkv, cus = device_cus();
-    auto_workers = (int32_t)((pairs >= 8 * cus ? 8 : 4) * cus);
+    // 4 workers per CU: the 256-sequence batch's tails take 106 us at 4,
+    // 110 at 8 (118 at 3, 134 at 5: counts that leave CUs unevenly loaded lose)
+    auto_workers = 4 * device_cus();
     mode = PKV_DECODE_BALANCED;
     p->prefix_splits = prefix_splits(S, Hq / Hkv, Hkv, prefix_len);
   } else if (mode == PKV_DECODE_AUTO) {

@@ -383,10 +383,10 @@ def test_shared_prefix_workspace_and_refusals():
     lib = B.load()
     o = _opts(mode=3)
     ws = lambda *a: lib.paged_attention_decode_shared_prefix_workspace_bytes(*a, ctypes.byref(o))
-    # 256 x 8 pairs (8 per CU of a 256-CU device -> 2048 workers); prefix of 64 tiles;
-    # 8 row groups of 128 rows x 8 KV heads -> 4 key splits per pair
+    # 256 x 8 pairs, tails on 4 workers per CU of a 256-CU device (1024); prefix of 64
+    # tiles; 8 row groups of 128 rows x 8 KV heads -> 4 key splits per pair
     S, Hq, Hkv, D = 256, 32, 8, 128
-    slots = 2048 + S * Hkv + S * Hkv * 4
+    slots = 1024 + S * Hkv + S * Hkv * 4
     assert ws(S, Hq, Hkv, D, 600, 16, 1024) == slots * 4 * (D + 2) * 4 + S * Hkv * 8
     assert ws(S, Hq, Hkv, D, 600, 16, 1000) == 0   # not a multiple of the block size
     assert ws(S, Hq, Hkv, D, 600, 16, 0) == 0
