@@ -62,11 +62,20 @@ struct RowState {
   f32x4 acc[VE];
 };
 
+// Max over the four lanes l, l^16, l^32, l^48 (one column's lane groups).
+// IEEE maximum: no input canonicalisation, and a NaN score propagates.
+__device__ __forceinline__ float column_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float m = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Max of one raw-score column over the lane's keys and the other lane groups,
 // scaled into log2 units, and the lazy rescale it may call for.
 template <int VE>
 __device__ __forceinline__ float raise_max(RowState<VE>& st, float local_max, float qs) {
-  const float bm = max_over_lane_groups(local_max) * qs;
+  const float bm = column_max(local_max) * qs;
   // a column's first tile holds a visible key (tile 0 holds key 0), so its
   // running max is finite from then on; a fully masked tile leaves bm = -inf
   const bool grow = bm > st.m + kLazyMax;
@@ -98,17 +107,27 @@ constexpr int f32_pitch() {
 // K: rows of 2D bytes, the 16-byte chunk n of key row k stored at chunk
 // n ^ k_swizzle(k), so that the 16 rows one MFMA operand read touches (one
 // chunk each) fall in distinct banks.
-// V: transposed per tile pair into the A operand of V^T.P: for MFMA row m
-// (d = VE*m + r) and lane group q, 16 bytes hold the bf16 values at d of keys
-// 4q..4q+3 of tile a, then of tile b, at byte 1024 r + 256 q + 16 m of the
-// pair's block, so each 16-lane group of one read covers 256 contiguous bytes.
+// V: column-chunk major.  Region r (d = 16 r .. 16 r + 15, 32 bytes per key)
+// holds the stage's keys in order, key k at byte 32 k of the region, so the
+// 16 keys of a tile make 512 contiguous bytes.  The A operand of V^T.P comes
+// from gfx950's LDS transpose read: lane l reads the 8 bytes at 8 l of a
+// tile's 512 bytes, and within each 16-lane group the hardware hands lane
+// 4 b + e element j of the lane 4 j + b read, i.e. lane l receives d = 16 r +
+// l % 16 of keys 4 (l / 16) .. 4 (l / 16) + 3, the key order of the scores'
+// P.  Two such reads (tiles a and b of a pair) make one 16-byte operand.  This
+// replaces a transposing copy through registers (per-element permutes in the
+// staging) with a plain 16-byte copy.
 template <int D>
 __device__ __forceinline__ int k_swizzle(int key) {
   return D == 128 ? (key & 15) : ((key >> 1) & 7);  // rows 256 / 128 bytes long
 }
-template <int D>
-constexpr int vpair_bytes() {
-  return 64 * D;
+constexpr int kVRegion = 16 * kBlockTiles * 32;  // one 32-byte column chunk of a stage's 64 keys
+
+// gfx950 LDS transpose read of four bf16 (see the V layout above).
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
 }
 
 // Probabilities of one column from raw scores x (dropped keys at -inf).
@@ -116,7 +135,7 @@ template <int VE, int N>
 __device__ __forceinline__ void probabilities(RowState<VE>& st, const float (&x)[N], float qs, float (&p)[N]) {
   float mx = x[0];
 #pragma unroll
-  for (int i = 1; i < N; ++i) mx = fmaxf(mx, x[i]);
+  for (int i = 1; i < N; ++i) mx = __builtin_elementwise_maximum(mx, x[i]);
   const float m = raise_max(st, mx, qs);
 #pragma unroll
   for (int i = 0; i < N; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qs, -m));
@@ -150,8 +169,8 @@ __device__ __forceinline__ void update_tile_f32(const Tile<PKV_F32, D>& tl,
 // rescale, probabilities) and block_pv (P.V and the row sums).  Scores come from the K image (kt: the block's
 // first tile, ko: the lane's chunk offsets); P.V runs per tile pair a, b on the
 // double-rate K=32 MFMA, lane group q carrying keys 4q..4q+3 of a, then of b,
-// in P and in V^T alike.  V^T is read from its LDS image one MFMA row group r
-// at a time (vt + pair block + 1024 r) and feeds every row block.  The column
+// in P and in V^T alike.  V^T is read from the V image one group of 16 d (r)
+// and tile pair at a time and feeds every row block.  The column
 // sums come from one more MFMA against an all-ones A operand, so every lane's
 // l[0] is its column's full sum of the rounded probabilities.
 // masked: tiles from `live` on and keys past lim[rb] (the column's position -
@@ -200,8 +219,9 @@ __device__ __forceinline__ void block_probs(const char* kt, const int (&ko)[D / 
   }
 }
 
-// P.V of one block: V^T from its LDS image (vt: the block's first pair, this
-// lane's offset) against the probabilities pk, plus the row sums.
+// P.V of one block: V^T from its LDS image (vt: the stage's V image plus 8
+// lane bytes) against the probabilities pk, plus the row sums.  acc[r] row m
+// is d = 16 r + m.
 template <int D, int R, int NT>
 __device__ __forceinline__ void block_pv(const char* vt, const u32x4 (&pk)[R][NT / 2],
                                          RowState<D / 16> (&st)[R]) {
@@ -211,7 +231,9 @@ __device__ __forceinline__ void block_pv(const char* vt, const u32x4 (&pk)[R][NT
   for (int h = 0; h < NT / 2; ++h) {
 #pragma unroll
     for (int r = 0; r < VE; ++r) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(vt + h * vpair_bytes<D>() + 1024 * r);
+      const u32x2 va = lds_read_tr16(vt + r * kVRegion + 2 * h * 512);
+      const u32x2 vb = lds_read_tr16(vt + r * kVRegion + (2 * h + 1) * 512);
+      const u32x4 v = {va[0], va[1], vb[0], vb[1]};
 #pragma unroll
       for (int rb = 0; rb < R; ++rb) st[rb].acc[r] = mfma_bf16_k32(v, pk[rb][h], st[rb].acc[r]);
     }
@@ -585,7 +607,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
   __shared__ int64_t sm_row[kPrefillChunkTiles];  // pool row of each tile's first key
   // bf16 images: stage buffers for K (two: one read, the next written) and V
   // (three: the lagging half of the wavefronts still reads the previous one)
-  constexpr int K_STAGE = 16 * kBlockTiles * 2 * D, V_STAGE = (kBlockTiles / 2) * vpair_bytes<D>();
+  constexpr int K_STAGE = 16 * kBlockTiles * 2 * D, V_STAGE = 16 * kBlockTiles * 2 * D;
   constexpr int K_BYTES = F32 ? kStageKeys * f32_pitch<D>() : 2 * K_STAGE;
   constexpr int V_BYTES = F32 ? kStageKeys * f32_pitch<D>() : 3 * V_STAGE;
   __shared__ __attribute__((aligned(16))) char sm_k[K_BYTES];
@@ -739,56 +761,34 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
           }
         }
       } else {
-        // Stages of one softmax block (kBlockTiles tiles).  The first half of
-        // the wavefronts stages V, the second half K.  V unit (pair pp, quad qd, 8-byte half column
-        // hcol): keys 4qd..4qd+3 of both tiles of the pair at those 8 bytes,
-        // so the thread holds the 8 keys of every 16-byte piece of the
-        // transposed image it writes; lanes are ordered so that 16 of them
-        // write 256 contiguous bytes.  K: the stage's 16-byte pieces.
+        // Stages of one softmax block (kBlockTiles tiles).  Every thread
+        // copies up to KP 16-byte K pieces and VP V pieces of the stage.  K
+        // piece p: key p / PER_ROW, column p % PER_ROW.  V piece p (bf16): key
+        // (p / 2) % SK, 16-byte half p % 2 of column chunk p / (2 SK), which
+        // lands at byte 16 p of the V image; V piece p (E4M3, 16 codes = one
+        // column chunk): key p % SK, chunk p / SK, at byte 32 p.  A wavefront's
+        // writes then cover contiguous LDS bytes.
         constexpr int NT = kBlockTiles;
-        constexpr int SK = 16 * NT;       // keys per stage
-        constexpr int HPR = RB / 8;       // 8-byte half columns per key row
-        constexpr int EH = 8 / EB;        // elements per half column
-        constexpr int SUBS = VE > EH ? VE / EH : 1;  // half columns per MFMA row m
-        constexpr int HALF = NW * 32;  // threads per staging role
-        constexpr int VUNITS = (NT / 2) * 4 * HPR;
-        constexpr int KTOTAL = SK * PER_ROW;  // 16-byte K pieces per stage
-        constexpr int KPIECES = (KTOTAL + HALF - 1) / HALF;
-        static_assert(VUNITS <= HALF && KPIECES <= 4 && (KTOTAL % HALF == 0 || KTOTAL < HALF), "staging split");
-        static_assert(SUBS == 1 || (SUBS == 2 && HPR == 32), "half-column order");
-        const bool v_stager = threadIdx.x < VUNITS;
-        const bool k_stager = threadIdx.x >= HALF;
-        const int u = threadIdx.x, uk = threadIdx.x - HALF;
-        const int hcol = SUBS == 2 ? 2 * (u & 15) + ((u >> 4) & 1) : u % HPR;
-        const int vrest = SUBS == 2 ? u >> 5 : u / HPR;
-        const int qd = vrest & 3, pp = vrest >> 2;
-        // V: pre[i] = key 4qd+i of tile a (dwords 0-1) and of tile b (dwords 2-3);
-        // K: pre[i] = piece i
-        u32x4 pre[4];
-        int nva = 0, nvb = 0;  // V keys of tiles a, b inside the context and the range
+        constexpr int SK = 16 * NT;           // keys per stage
+        constexpr int NTH = NW * 64;
+        constexpr int KTOTAL = SK * PER_ROW;  // 16-byte cache pieces per stage, K and V alike
+        constexpr int KP = (KTOTAL + NTH - 1) / NTH;
+        static_assert(KP <= 2 && (KTOTAL % NTH == 0 || KTOTAL < NTH), "staging split");
+        u32x4 pre_k[KP], pre_v[KP];
         auto fetch = [&](int tile0) {
-          if (v_stager) {
-            const int ta = tile0 + 2 * pp, tb = ta + 1;
-            // past the end: a valid tile, its V zeroed
-            const char* va = static_cast<const char*>(a.vc) + (sm_row[min(ta, c1 - 1) - c0] + 4 * qd) * RB + hcol * 8;
-            const char* vb = static_cast<const char*>(a.vc) + (sm_row[min(tb, c1 - 1) - c0] + 4 * qd) * RB + hcol * 8;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const u32x2 x = *reinterpret_cast<const u32x2*>(va + i * RB);
-              const u32x2 y = *reinterpret_cast<const u32x2*>(vb + i * RB);
-              pre[i] = u32x4{x[0], x[1], y[0], y[1]};
-            }
-            nva = ta < c1 ? min(4, max(0, ctx - (ta * 16 + 4 * qd))) : 0;
-            nvb = tb < c1 ? min(4, max(0, ctx - (tb * 16 + 4 * qd))) : 0;
-          } else if (k_stager) {
-#pragma unroll
-            for (int i = 0; i < KPIECES; ++i) {
-              const int p = uk + HALF * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
-              if (KTOTAL < HALF && p >= KTOTAL) break;  // fewer pieces than threads
-              const int tc = min(tile0 + key / 16, c1 - 1);
-              pre[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) +
-                                                       (sm_row[tc - c0] + (key & 15)) * RB + kcol * 16);
-            }
+          for (int i = 0; i < KP; ++i) {
+            const int p = threadIdx.x + NTH * i;
+            if (KTOTAL < NTH && p >= KTOTAL) break;  // fewer pieces than threads
+            const int key = p / PER_ROW, kcol = p - key * PER_ROW;
+            const int tk = min(tile0 + key / 16, c1 - 1);  // past the end: a valid tile, zeroed
+            pre_k[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) +
+                                                       (sm_row[tk - c0] + (key & 15)) * RB + kcol * 16);
+            const int vkey = EB == 2 ? (p >> 1) & (SK - 1) : p & (SK - 1);
+            const int vcol = EB == 2 ? 2 * (p / (2 * SK)) + (p & 1) : p / SK;
+            const int tv = min(tile0 + vkey / 16, c1 - 1);
+            pre_v[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.vc) +
+                                                       (sm_row[tv - c0] + (vkey & 15)) * RB + vcol * 16);
           }
         };
         // lane's K chunk offsets within a tile: row lane % 16, d = 32 c + 8 (lane / 16) + 0..7
@@ -798,82 +798,43 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
           ko[c] = (lane & 15) * 2 * D + (((lane >> 4) + 4 * c) ^ k_swizzle<D>(lane & 15)) * 16;
         // the fetched stage (tiles t0s .. t0s + NT - 1) into the buffers kd0 / vd0
         auto stage_write = [&](int t0s, char* kd0, char* vd0) {
-          if (v_stager) {
-            // V of keys past the context or the range: zero, as its
-            // probabilities are, so that no stray bits reach the sums
-            if (nva < 4 || nvb < 4) {
+          // keys past the context or the range: zero (finite K, so that a
+          // score accumulator started at -inf stays -inf; V as its
+          // probabilities, so that no stray bits reach the sums)
+          if (t0s * 16 + SK > ctx || t0s + NT > c1) {  // workgroup-uniform
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                pre[i] = u32x4{i < nva ? pre[i][0] : 0u, i < nva ? pre[i][1] : 0u, i < nvb ? pre[i][2] : 0u,
-                               i < nvb ? pre[i][3] : 0u};
+            for (int i = 0; i < KP; ++i) {
+              const int p = threadIdx.x + NTH * i;
+              if (KTOTAL < NTH && p >= KTOTAL) break;
+              const int key = p / PER_ROW, tk = t0s + key / 16;
+              if (tk >= c1 || tk * 16 + (key & 15) >= ctx) pre_k[i] = u32x4{0, 0, 0, 0};
+              const int vkey = EB == 2 ? (p >> 1) & (SK - 1) : p & (SK - 1), tv = t0s + vkey / 16;
+              if (tv >= c1 || tv * 16 + (vkey & 15) >= ctx) pre_v[i] = u32x4{0, 0, 0, 0};
             }
-            char* vd = vd0 + pp * vpair_bytes<D>() + 256 * qd;
+          }
+#pragma unroll
+          for (int i = 0; i < KP; ++i) {
+            const int p = threadIdx.x + NTH * i;
+            if (KTOTAL < NTH && p >= KTOTAL) break;
+            const int key = p / PER_ROW, kcol = p - key * PER_ROW;
+            char* kd = kd0 + key * 2 * D;
+            const int sw = k_swizzle<D>(key);
             if constexpr (CT == PKV_BF16) {
+              *reinterpret_cast<u32x4*>(kd + ((kcol ^ sw) * 16)) = pre_k[i];
+              *reinterpret_cast<u32x4*>(vd0 + 16 * p) = pre_v[i];
+            } else {  // E4M3 codes -> bf16 (exact): K chunks 2 kcol, 2 kcol + 1; V one column chunk
+              uint32_t b[8], c[8];  // bf16 pairs of elements 2n, 2n+1
 #pragma unroll
-              for (int e = 0; e < EH; ++e) {
-                const int d = EH * hcol + e, m = d / VE, r = d % VE, w = e >> 1;
-                const uint32_t sel = (e & 1) ? kSelHi : kSelLo;
-                *reinterpret_cast<u32x4*>(vd + 1024 * r + 16 * m) =
-                    u32x4{__builtin_amdgcn_perm(pre[1][w], pre[0][w], sel),
-                          __builtin_amdgcn_perm(pre[3][w], pre[2][w], sel),
-                          __builtin_amdgcn_perm(pre[1][2 + w], pre[0][2 + w], sel),
-                          __builtin_amdgcn_perm(pre[3][2 + w], pre[2][2 + w], sel)};
+              for (int w = 0; w < 4; ++w) {
+                b[2 * w] = bf16x2_from_fp8x2_lo(pre_k[i][w]);
+                b[2 * w + 1] = bf16x2_from_fp8x2_hi(pre_k[i][w]);
+                c[2 * w] = bf16x2_from_fp8x2_lo(pre_v[i][w]);
+                c[2 * w + 1] = bf16x2_from_fp8x2_hi(pre_v[i][w]);
               }
-            } else {  // E4M3 codes -> bf16 (exact)
-#pragma unroll
-              for (int w = 0; w < 2; ++w) {
-                float f[8][4];  // f[i][b]: key i of tile a (i < 4) or b, element 4w + b
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                  for (int h = 0; h < 2; ++h) {
-                    const uint32_t word = pre[i][2 * h + w];
-                    const f32x2 x = fp8x2_lo(word), y = fp8x2_hi(word);
-                    f[4 * h + i][0] = x[0];
-                    f[4 * h + i][1] = x[1];
-                    f[4 * h + i][2] = y[0];
-                    f[4 * h + i][3] = y[1];
-                  }
-                }
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                  const int d = EH * hcol + 4 * w + b, m = d / VE, r = d % VE;
-                  *reinterpret_cast<u32x4*>(vd + 1024 * r + 16 * m) =
-                      u32x4{pack_exact(f[0][b], f[1][b]), pack_exact(f[2][b], f[3][b]),
-                            pack_exact(f[4][b], f[5][b]), pack_exact(f[6][b], f[7][b])};
-                }
-              }
-            }
-          } else if (k_stager) {
-            // K of keys past the context or the range: zero (finite), so that
-            // a score accumulator started at -inf stays -inf
-            if (t0s * 16 + SK > ctx || t0s + NT > c1) {  // workgroup-uniform
-#pragma unroll
-              for (int i = 0; i < KPIECES; ++i) {
-                if (KTOTAL < HALF && uk + HALF * i >= KTOTAL) break;
-                const int key = (uk + HALF * i) / PER_ROW, t = t0s + key / 16;
-                if (t >= c1 || t * 16 + (key & 15) >= ctx) pre[i] = u32x4{0, 0, 0, 0};
-              }
-            }
-#pragma unroll
-            for (int i = 0; i < KPIECES; ++i) {
-              const int p = uk + HALF * i, key = p / PER_ROW, kcol = p - key * PER_ROW;
-              if (KTOTAL < HALF && p >= KTOTAL) break;
-              char* kd = kd0 + key * 2 * D;
-              const int sw = k_swizzle<D>(key);
-              if constexpr (CT == PKV_BF16) {
-                *reinterpret_cast<u32x4*>(kd + ((kcol ^ sw) * 16)) = pre[i];
-              } else {  // E4M3 codes -> bf16 (exact): chunks 2 kcol, 2 kcol + 1
-                uint32_t b[8];  // bf16 pairs of elements 2n, 2n+1
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                  const f32x2 x = fp8x2_lo(pre[i][w]), y = fp8x2_hi(pre[i][w]);
-                  b[2 * w] = pack_exact(x[0], x[1]);
-                  b[2 * w + 1] = pack_exact(y[0], y[1]);
-                }
-                *reinterpret_cast<u32x4*>(kd + (((2 * kcol) ^ sw) * 16)) = u32x4{b[0], b[1], b[2], b[3]};
-                *reinterpret_cast<u32x4*>(kd + (((2 * kcol + 1) ^ sw) * 16)) = u32x4{b[4], b[5], b[6], b[7]};
-              }
+              *reinterpret_cast<u32x4*>(kd + (((2 * kcol) ^ sw) * 16)) = u32x4{b[0], b[1], b[2], b[3]};
+              *reinterpret_cast<u32x4*>(kd + (((2 * kcol + 1) ^ sw) * 16)) = u32x4{b[4], b[5], b[6], b[7]};
+              *reinterpret_cast<u32x4*>(vd0 + 32 * p) = u32x4{c[0], c[1], c[2], c[3]};
+              *reinterpret_cast<u32x4*>(vd0 + 32 * p + 16) = u32x4{c[4], c[5], c[6], c[7]};
             }
           }
         };
@@ -885,7 +846,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
         // the previous block's P.V MFMAs, and each half's softmax VALU work then
         // meets the other half's MFMAs instead of its own partner's softmax.
         const bool lagging = wave >= NW / 2;
-        const int voff = (lane >> 4) * 256 + (lane & 15) * 16;
+        const int voff = 8 * lane;
         u32x4 pk[R][NT / 2];  // a block's probabilities (lagging waves: until the next stage)
         int late_buf = -1;    // lagging waves: the V buffer pk goes with (-1: none)
         fetch(c0);
@@ -933,26 +894,43 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void rows_ke
         const int rr = row_w0 + 16 * rb + (lane & 15);
         if (rr >= rows) continue;
         const int t = rr / G, g = rr - t * G;
+        // the lane's outputs: d = VE m + r (f32 fragments) or d = 16 r + m
+        // (bf16 images), m = 4 (lane / 16) + i
         if constexpr (JOB == kPrefillJob) {
           const int64_t orow = (int64_t)(q0 + t) * Hq + hk * G + g;
           const float inv = a.v_scale / l_run;
+          if constexpr (F32) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x[VE];
+            for (int i = 0; i < 4; ++i) {
+              float x[VE];
 #pragma unroll
-            for (int r = 0; r < VE; ++r) x[r] = st[rb].acc[r][i] * inv;
-            store_run<CT, VE>(a.out, orow * D + VE * (4 * (lane >> 4) + i), x);
+              for (int r = 0; r < VE; ++r) x[r] = st[rb].acc[r][i] * inv;
+              store_run<CT, VE>(a.out, orow * D + VE * (4 * (lane >> 4) + i), x);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < VE; ++r) {
+              const float x[4] = {st[rb].acc[r][0] * inv, st[rb].acc[r][1] * inv, st[rb].acc[r][2] * inv,
+                                  st[rb].acc[r][3] * inv};
+              store_run<CT, 4>(a.out, orow * D + 16 * r + 4 * (lane >> 4), x);
+            }
           }
         } else {
           const int64_t slot = a.slot0 + ((int64_t)t * a.num_kv_heads + hk) * a.splits + blockIdx.y;
           float* o = a.ws_acc + (slot * G + g) * D;
+          if constexpr (F32) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int q4 = 0; q4 < VE / 4; ++q4)
-              *reinterpret_cast<f32x4*>(o + VE * (4 * (lane >> 4) + i) + 4 * q4) =
-                  f32x4{st[rb].acc[4 * q4][i], st[rb].acc[4 * q4 + 1][i], st[rb].acc[4 * q4 + 2][i],
-                        st[rb].acc[4 * q4 + 3][i]};
+              for (int q4 = 0; q4 < VE / 4; ++q4)
+                *reinterpret_cast<f32x4*>(o + VE * (4 * (lane >> 4) + i) + 4 * q4) =
+                    f32x4{st[rb].acc[4 * q4][i], st[rb].acc[4 * q4 + 1][i], st[rb].acc[4 * q4 + 2][i],
+                          st[rb].acc[4 * q4 + 3][i]};
+          } else {
+#pragma unroll
+            for (int r = 0; r < VE; ++r)
+              *reinterpret_cast<f32x4*>(o + 16 * r + 4 * (lane >> 4)) = st[rb].acc[r];
+          }
           if (lane < 16) *reinterpret_cast<f32x2*>(a.ws_ml + (slot * G + g) * 2) = f32x2{st[rb].m, l_run};
         }
       }
