@@ -141,8 +141,8 @@ struct Plan {
 
 // Key splits of a shared prefix: about one (128-row workgroup, KV head, split)
 // unit per compute unit, at least four tiles per split; more splits cost more
-// in the merge than they save (256-sequence batch, whole call: 2 splits
-// 111.9 us, 4: 110.5, 8: 119.2).
+// in the merge than they save (256-sequence batch, whole call: 1 split
+// 113.9 us, 2: 105.0, 3: 104.5, 4: 103.4, 6: 111.5).
 int32_t prefix_splits(int64_t S, int64_t G, int64_t Hkv, int64_t prefix_len) {
   const int64_t tiles = prefix_len / 16;
   const int64_t row_groups = (S * G + 127) / 128;
