@@ -116,10 +116,15 @@ typedef enum {
 typedef enum {
   /* one workgroup per (sequence, KV head) walks the whole context */
   PKV_DECODE_SINGLE_PASS = 0,
-  /* split-K: one workgroup per (partition of partition_size tokens, KV head,
-     sequence); partial softmax states go to the workspace and a merge kernel
-     combines a sequence's partitions in partition order (sequences that fit
-     in one partition are finalised in place) */
+  /* split-K: the context of each (sequence, KV head) is cut into partitions
+     of partition_size tokens; each partition's partial softmax state goes to
+     the workspace and a merge kernel combines a sequence's partitions in
+     partition order (sequences that fit in one partition are finalised in
+     place).  With one wavefront per partition (the default up to 512 tokens)
+     persistent wavefronts, 4 per compute unit, stream equal runs of the
+     (sequence, KV head, partition) list back to back; otherwise one
+     workgroup per partition.  Either way a partition's state is computed from
+     the same tiles in the same order, so the results are the same. */
   PKV_DECODE_PARTITIONED = 1,
   /* balanced split: the 16-token tiles of all (sequence, KV head) pairs are
      flattened and num_workers wavefronts each take an equal contiguous run,
@@ -140,14 +145,16 @@ typedef struct {
   int32_t waves_per_group;  /* SINGLE_PASS / PARTITIONED: wavefronts per workgroup walking
                                disjoint tiles: 0 = library default (1 for partitions of at
                                most 512 tokens, else 4), else 1, 2, 4 or 8 */
-  int32_t num_workers;      /* BALANCED: wavefronts sharing the work; 0 = library default
-                               (4 per compute unit of the current device) */
+  int32_t num_workers;      /* BALANCED, and PARTITIONED with one wavefront per partition:
+                               wavefronts sharing the work; 0 = library default (4 per
+                               compute unit of the current device) */
   void* workspace;          /* device memory, >= paged_attention_decode_workspace_bytes();
                                not needed for SINGLE_PASS */
   size_t workspace_bytes;
   int32_t flags;            /* PKV_DECODE_* flags below, or 0 */
-  const int32_t* seq_order; /* SINGLE_PASS / PARTITIONED (also AUTO when it picks the single
-                               pass): NULL, or device int32 [num_seqs], a permutation of
+  const int32_t* seq_order; /* SINGLE_PASS / PARTITIONED with more than one wavefront per
+                               workgroup (also AUTO when it picks the single pass): NULL,
+                               or device int32 [num_seqs], a permutation of
                                0..num_seqs-1 giving the order in which the sequences'
                                workgroups start.  Longest context first (pkv_decode_order)
                                keeps a long sequence from starting last and running alone
@@ -155,8 +162,9 @@ typedef struct {
                                are bit-identical for every permutation.  An entry outside
                                [0, num_seqs) makes its workgroups exit, and a repeated
                                entry leaves another sequence's rows unwritten
-                               (pkv_validate_seq_order checks a host copy).  BALANCED and
-                               the shared-prefix calls ignore it. */
+                               (pkv_validate_seq_order checks a host copy).  BALANCED,
+                               one-wavefront PARTITIONED and the shared-prefix calls
+                               ignore it. */
 } pkv_decode_opts;
 
 /* opts->flags: launch only the streaming kernel and leave its partial states

@@ -48,6 +48,24 @@ namespace {
 #endif
 
 constexpr int kChunkTiles = 1024;  // block ids staged in LDS per pass (4 KiB)
+
+// Split-K partial rows in the workspace: a lane holds, for each i, the VE
+// consecutive columns d = VE (4 q + i) .. + VE - 1 (q = lane / 16).  They are
+// stored permuted so that the four lanes of a row write 64 contiguous bytes
+// per store instruction (four of them, one per q, at float 4 P, P = (i VE/4 +
+// q4) 4 + q) instead of four 16-byte pieces 128 bytes apart: partial-line
+// writes behind which the next loads of the wavefront wait.  part_pos is the
+// float offset of the chunk (i, q4) of lane group q; part_d0 the first column
+// of chunk P.
+template <int VE>
+__device__ __forceinline__ int part_pos(int i, int q4, int q) {
+  return ((i * (VE / 4) + q4) * 4 + q) * 4;
+}
+template <int VE>
+__device__ __forceinline__ int part_d0(int P) {
+  const int q = P & 3, t = P >> 2, q4 = t % (VE / 4), i = t / (VE / 4);
+  return VE * (4 * q + i) + 4 * q4;
+}
 // Block tables read as constant memory (uniform indices: scalar loads).
 typedef const __attribute__((address_space(4))) int32_t* ctab;
 // Balanced split: work units charged for starting a piece, in tiles.  A piece
@@ -282,13 +300,11 @@ __global__ __launch_bounds__(NW * 64, (CT == PKV_FP8_E4M3 && !APPEND) ? 4 : 1) v
   } else {
     const int64_t prow = row * a.num_parts + part;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* o = a.ws_acc + prow * D + VE * (4 * (lane >> 4) + i);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int w = 0; w < VE / 4; ++w)
-        *reinterpret_cast<f32x4*>(o + 4 * w) =
+        *reinterpret_cast<f32x4*>(a.ws_acc + prow * D + part_pos<VE>(i, w, lane >> 4)) =
             f32x4{acc[4 * w][i], acc[4 * w + 1][i], acc[4 * w + 2][i], acc[4 * w + 3][i]};
-    }
     if (lane < 16) *reinterpret_cast<f32x2*>(a.ws_ml + prow * 2) = f32x2{m_run, l_run};
   }
 }
@@ -357,7 +373,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
   const float inv = a.v_scale / L;
   const float x[4] = {sum[0] * inv, sum[1] * inv, sum[2] * inv, sum[3] * inv};
-  store_run<CT, 4>(a.out, ((int64_t)s * a.num_q_heads + h) * D + 4 * c, x);
+  store_run<CT, 4>(a.out, ((int64_t)s * a.num_q_heads + h) * D + part_d0<D / 16>(c), x);
 }
 
 // ---------------------------------------------------------------------------
@@ -465,6 +481,37 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
 
   const int g = lane & 15;
   const bool g_ok = g < G;
+  // Partial states of this run's pieces, staged in LDS and written out at the
+  // end of the run (or when the buffer is full): a global store in the middle
+  // of the run would hold up the next piece's loads until it completes.
+  // Slot: G rows of D floats, then G (max, sum) pairs; meta: (workspace slot,
+  // segment, and the segment's piece record when this is its last piece).
+  constexpr int kPendFloats = 4096;  // 16 KiB per wavefront
+  __shared__ __attribute__((aligned(16))) float sm_pend[4][kPendFloats];
+  __shared__ int4 sm_pend_meta[4][16];
+  const int wv = threadIdx.x >> 6;
+  float* const pend = sm_pend[wv];
+  int4* const pend_meta = sm_pend_meta[wv];
+  const int kSlotFloats = (G * (D + 2) + 3) & ~3;
+  const int kPendSlots = min(16, kPendFloats / kSlotFloats);
+  int npend = 0;
+  auto flush = [&]() {
+    for (int j = 0; j < npend; ++j) {
+      const int4 meta = pend_meta[j];
+      const float* slot = pend + j * kSlotFloats;
+      float* dst = a.ws_acc + (int64_t)meta.x * G * D;
+      for (int u = lane; u < G * D / 4; u += 64)
+        *reinterpret_cast<f32x4*>(dst + 4 * u) = *reinterpret_cast<const f32x4*>(slot + 4 * u);
+      if (lane < G)
+        *reinterpret_cast<f32x2*>(a.ws_ml + ((int64_t)meta.x * G + lane) * 2) =
+            *reinterpret_cast<const f32x2*>(slot + G * D + 2 * lane);
+      if (lane == 0 && meta.z != INT32_MIN) {
+        a.ws_meta[2 * (int64_t)meta.y] = meta.z;
+        a.ws_meta[2 * (int64_t)meta.y + 1] = meta.w;
+      }
+    }
+    npend = 0;
+  };
   int64_t x = x0;
   int32_t carry[NBUF] = {};  // first-batch block ids of the next piece, loaded ahead
   bool has_carry = false;
@@ -597,16 +644,13 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
     l_run = sum_over_lane_groups(l_run);
 
     const bool whole = tl == 0 && te == n && !a.cascade;  // cascade: always pieces
-    if (whole || te == n) {
-      // the segment's last piece records where its pieces are
+    if (whole) {
+      // finalised in place; its record says so
       if (lane == 0) {
-        const int64_t first_tile_unit = p_cur + (int64_t)h * u + kPieceCost;
-        a.ws_meta[2 * (int64_t)seg] = whole ? -1 : (int32_t)(first_tile_unit / chunk);
-        a.ws_meta[2 * (int64_t)seg + 1] = whole ? -1 : w;
+        a.ws_meta[2 * (int64_t)seg] = -1;
+        a.ws_meta[2 * (int64_t)seg + 1] = -1;
       }
-    }
-    if (g_ok) {
-      if (whole) {
+      if (g_ok) {
         const int64_t row = (int64_t)s_cur * a.num_q_heads + qh;
         const float inv = a.v_scale / l_run;
 #pragma unroll
@@ -616,18 +660,27 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
           for (int r = 0; r < VE; ++r) xo[r] = st.acc[r][i] * inv;
           store_run<CT, VE>(a.out, row * D + VE * (4 * (lane >> 4) + i), xo);
         }
-      } else {
-        const int64_t slot = (int64_t)w + seg;
-        float* o = a.ws_acc + (slot * G + g) * D;
+      }
+    } else {
+      if (npend == kPendSlots) flush();
+      float* slot = pend + npend * kSlotFloats;
+      if (g_ok) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int q4 = 0; q4 < VE / 4; ++q4)
-            *reinterpret_cast<f32x4*>(o + VE * (4 * (lane >> 4) + i) + 4 * q4) =
+            *reinterpret_cast<f32x4*>(slot + g * D + VE * (4 * (lane >> 4) + i) + 4 * q4) =
                 f32x4{st.acc[4 * q4][i], st.acc[4 * q4 + 1][i], st.acc[4 * q4 + 2][i],
                       st.acc[4 * q4 + 3][i]};
-        if (lane < 16) *reinterpret_cast<f32x2*>(a.ws_ml + (slot * G + g) * 2) = f32x2{st.m, l_run};
+        if (lane < 16) *reinterpret_cast<f32x2*>(slot + G * D + 2 * g) = f32x2{st.m, l_run};
       }
+      if (lane == 0) {
+        // the segment's last piece records where its pieces are
+        const int64_t first_tile_unit = p_cur + (int64_t)h * u + kPieceCost;
+        pend_meta[npend] = te == n ? int4{w + seg, seg, (int32_t)(first_tile_unit / chunk), w}
+                                   : int4{w + seg, seg, INT32_MIN, 0};
+      }
+      ++npend;
     }
     x += ve - vt;
     if (ve == u && h == Hkv - 1) {
@@ -635,6 +688,248 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
       ++s_cur;
     }
   }
+  flush();
+}
+
+// ---------------------------------------------------------------------------
+// Split-K partitions streamed by persistent wavefronts.  The tasks of a call
+// are the (sequence, KV head, partition) triples in that order, a partition
+// being part_tiles tiles of one pair (the last one shorter).  num_workers
+// wavefronts each take an equal contiguous run of tasks and stream them back
+// to back: the next task's first block ids are loaded during the current
+// task's first batch, and q is reloaded only when the pair changes, so a
+// partition boundary costs no dependent round trip.  Every partition's state
+// is computed exactly as by decode_partition_kernel with one wavefront (same
+// tiles, same order), so the partial states, and the reduce, are the same.
+// ---------------------------------------------------------------------------
+template <int CT, int D, int NBUF, bool APPEND, bool NT>
+__global__ __launch_bounds__(256, 1) void decode_partition_run_kernel(DecodeArgs a) {
+  using T = Tile<CT, D>;
+  constexpr int VE = T::VE;
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = a.num_workers;
+  if (w >= W) return;
+  const int S = a.num_seqs, Hkv = a.num_kv_heads, G = a.group, bs = a.block_size;
+  const int PT = a.part_tiles;
+  auto parts_of = [PT](int ctx) { return ctx > 0 ? (((ctx + 15) >> 4) + PT - 1) / PT : 0; };
+
+  // Task count; sequences with no tokens have no task: worker s % W writes
+  // their zero rows.
+  int64_t total = 0;
+  for (int c = 0; c < S; c += 64) {
+    const int s = c + lane;
+    const int ctx = s < S ? a.lens[s] : 0;
+    total += wave_sum_u32((uint32_t)parts_of(ctx));
+    uint64_t zmask = __ballot(s < S && ctx <= 0 && s % W == w);
+    while (zmask) {
+      const int l = __builtin_ctzll(zmask);
+      zmask &= zmask - 1;
+      write_zero_rows<CT, D>(a, c + l, lane);
+      if constexpr (APPEND)
+        for (int h = 0; h < Hkv; ++h) append_row<CT, D>(a, c + l, h, lane);
+    }
+  }
+  total *= Hkv;
+  if (total == 0) return;
+  const int64_t chunk = (total + W - 1) / W;
+  const int64_t t0 = (int64_t)w * chunk;
+  const int64_t t1 = min(total, t0 + chunk);
+  if (t0 >= t1) return;
+
+  // Sequence holding task t0, and the tasks before it.
+  int s_cur = 0;
+  int64_t p_cur = 0;
+  {
+    int64_t base = 0;
+    for (int c = 0; c < S; c += 64) {
+      const int s = c + lane;
+      const uint32_t u = s < S ? (uint32_t)parts_of(a.lens[s]) : 0u;
+      const uint32_t incl = wave_incl_scan_u32(u);
+      const int64_t tot = (int64_t)Hkv * __builtin_amdgcn_readlane(incl, 63);
+      if (t0 < base + tot) {
+        const uint64_t hit = __ballot(t0 < base + (int64_t)Hkv * incl);
+        const int l = __builtin_ctzll(hit);
+        s_cur = c + l;
+        p_cur = base + (int64_t)Hkv * __builtin_amdgcn_readlane(incl - u, l);
+        break;
+      }
+      base += tot;
+    }
+  }
+
+  const int g = lane & 15;
+  const bool g_ok = g < G;
+  const int64_t block_rows = (int64_t)Hkv * bs;
+  // Partial states of this wavefront's partitions, staged in LDS and written
+  // out when the buffer is full and at the end of the run, so that no store
+  // sits in front of the next partition's loads.  Slot: G rows of D floats,
+  // then G (max, sum) pairs.
+  constexpr int kPendFloats = 8192;  // 32 KiB per wavefront
+  __shared__ __attribute__((aligned(16))) float sm_pend[4][kPendFloats];
+  __shared__ int2 sm_pend_meta[4][64];
+  const int wv = threadIdx.x >> 6;
+  float* const pend = sm_pend[wv];
+  int2* const pend_meta = sm_pend_meta[wv];
+  const int kSlotFloats = (G * (D + 2) + 3) & ~3;
+  const int kPendSlots = min(64, kPendFloats / kSlotFloats);
+  int npend = 0;
+  auto flush = [&]() {
+    for (int j = 0; j < npend; ++j) {
+      const int2 meta = pend_meta[j];  // (pair, partition)
+      const int sj = meta.x / Hkv, hj = meta.x - sj * Hkv;
+      const int64_t row0 = (int64_t)sj * a.num_q_heads + hj * G;
+      const float* slot = pend + j * kSlotFloats;
+      for (int u = lane; u < G * D / 4; u += 64) {
+        const int gg = u / (D / 4), c4 = u - gg * (D / 4);
+        *reinterpret_cast<f32x4*>(a.ws_acc + ((row0 + gg) * a.num_parts + meta.y) * D + 4 * c4) =
+            *reinterpret_cast<const f32x4*>(slot + 4 * u);
+      }
+      if (lane < G)
+        *reinterpret_cast<f32x2*>(a.ws_ml + ((row0 + lane) * a.num_parts + meta.y) * 2) =
+            *reinterpret_cast<const f32x2*>(slot + G * D + 2 * lane);
+    }
+    npend = 0;
+  };
+  typename T::QFrag qf;
+  int q_seg = -1;            // pair whose q rows qf holds
+  int32_t carry[NBUF] = {};  // first-batch block ids of the next task, loaded ahead
+  bool has_carry = false;
+  for (int64_t t = t0; t < t1 && s_cur < S;) {
+    const int ctx = max(0, a.lens[s_cur]);
+    const int n = (ctx + 15) >> 4;
+    const int np = (n + PT - 1) / PT;
+    if (np == 0) {
+      ++s_cur;
+      continue;
+    }
+    const int64_t rel = t - p_cur;
+    const int h = (int)(rel / np), part = (int)(rel - (int64_t)h * np);
+    const int tl = part * PT, te = min(n, tl + PT);
+    const int seg = s_cur * Hkv + h;
+    const int qh = h * G + g;
+    if (seg != q_seg) {
+      const QElem<CT>* qrow = static_cast<const QElem<CT>*>(a.q) +
+                              ((int64_t)s_cur * a.num_q_heads + (g_ok ? qh : 0)) * D;
+      qf = T::load_q(qrow, g_ok, lane);
+      q_seg = seg;
+    }
+    const int32_t* table = a.tables + (int64_t)s_cur * a.max_blocks;
+    const int64_t head_rows = (int64_t)h * bs;
+    const ctab ctable = (ctab)table;  // address-space cast: C-style only
+    auto entry = [&](int tt) { return ctable[(min(tt, te - 1) * 16) / bs]; };
+    int32_t ent_next[NBUF];
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) ent_next[j] = has_carry ? carry[j] : entry(tl + j);
+    // the next task: the next partition of this pair, the next KV head, or
+    // the next sequence with tokens; its first block ids come with the first
+    // batch of this one
+    int s_next = s_cur, tl_next = te, te_next = 0;
+    if (te < n) {
+      te_next = min(n, te + PT);
+    } else if (h + 1 < Hkv) {
+      tl_next = 0;
+      te_next = min(n, PT);
+    } else {
+      do ++s_next; while (s_next < S && a.lens[s_next] <= 0);
+      tl_next = 0;
+      te_next = s_next < S ? min((a.lens[s_next] + 15) >> 4, PT) : 0;
+    }
+    has_carry = t + 1 < t1 && te_next > tl_next;
+    const int32_t* table_next = a.tables + (int64_t)min(s_next, S - 1) * a.max_blocks;
+
+    Softmax<VE> st;
+#pragma unroll
+    for (int r = 0; r < VE; ++r) st.acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Append: the partition holding the pair's last tile writes the new
+    // token's rows to their slot (loaded now, stored at the end) and, when
+    // that slot is position ctx-1, reads them from k / v.
+    const int32_t slot_new = APPEND && te == n ? a.slots[s_cur] : -1;
+    const int r_new = (ctx - 1) & 15;
+    const int64_t off_new = (ctx - 1) % bs;
+    const int64_t new_row = (int64_t)s_cur * Hkv + h;
+    const void* kn = static_cast<const QElem<CT>*>(a.kn) + new_row * D;
+    const void* vn = static_cast<const QElem<CT>*>(a.vn) + new_row * D;
+    NewRow<CT, D> nrow;
+    if (slot_new >= 0) nrow.load(a, s_cur, h, lane);
+    for (int k = tl; k < te; k += NBUF) {
+      int32_t ent[NBUF];
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        ent[j] = ent_next[j];
+        ent_next[j] = entry(k + NBUF + j);
+      }
+      if (has_carry && k == tl) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j)
+          carry[j] = ((ctab)table_next)[(min(tl_next + j, te_next - 1) * 16) / bs];
+      }
+      T buf[NBUF];
+      if (APPEND && slot_new >= 0 && k + NBUF >= n) {
+        // the batch holding the pair's last tile: its new token's rows come
+        // from k / v when the slot is position ctx-1
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          const int tt = min(k + j, te - 1);
+          const int32_t blk = ent[j];
+          const int64_t row = (int64_t)blk * block_rows + head_rows + ((tt * 16) % bs);
+          const int rsub = k + j == n - 1 && (int64_t)blk * bs + off_new == slot_new ? r_new : -1;
+          buf[j].template load_sub<NT>(a.kc, a.vc, row, lane, rsub, kn, vn, a.inv_k, a.inv_v);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          const int tt = min(k + j, te - 1);
+          const int64_t row = (int64_t)ent[j] * block_rows + head_rows + ((tt * 16) % bs);
+          buf[j].template load<NT>(a.kc, a.vc, row, lane);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        if (k + j >= te) break;
+        process_tile<CT, D>(buf[j], qf, st, (k + j) * 16, ctx, a.qk_scale, lane);
+      }
+    }
+    if (slot_new >= 0) nrow.store(a, slot_new, h, lane);
+    const float m_run = st.m;
+    const float l_run = sum_over_lane_groups(st.l);
+    if (g_ok) {
+      const int64_t row = (int64_t)s_cur * a.num_q_heads + qh;
+      if (np == 1) {  // one partition holds the whole context: the final rows
+        const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x[VE];
+#pragma unroll
+          for (int r = 0; r < VE; ++r) x[r] = st.acc[r][i] * inv;
+          store_run<CT, VE>(a.out, row * D + VE * (4 * (lane >> 4) + i), x);
+        }
+      }
+    }
+    if (np > 1) {
+      // the partial state waits in LDS: a global store here would hold up the
+      // next partition's loads until it completes
+      if (npend == kPendSlots) flush();
+      float* slot = pend + npend * kSlotFloats;
+      if (g_ok) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q4 = 0; q4 < VE / 4; ++q4)
+            *reinterpret_cast<f32x4*>(slot + g * D + part_pos<VE>(i, q4, lane >> 4)) =
+                f32x4{st.acc[4 * q4][i], st.acc[4 * q4 + 1][i], st.acc[4 * q4 + 2][i], st.acc[4 * q4 + 3][i]};
+        if (lane < 16) *reinterpret_cast<f32x2*>(slot + G * D + 2 * g) = f32x2{m_run, l_run};
+      }
+      if (lane == 0) pend_meta[npend] = int2{seg, part};
+      ++npend;
+    }
+    ++t;
+    if (part == np - 1 && h == Hkv - 1) {
+      p_cur += (int64_t)Hkv * np;
+      ++s_cur;
+    }
+  }
+  flush();
 }
 
 // Merge the pieces of one segment (sequence, KV head) for one query head.
@@ -726,7 +1021,21 @@ constexpr int ring_depth() {
 
 template <int CT, int D, int NW>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
-  if (a.phase != kMergePhase) {
+  if (a.phase != kMergePhase && NW == 1 && a.num_workers > 0) {
+    // one-wavefront partitions: persistent wavefronts stream runs of them
+    constexpr int B = ring_depth<CT, D>();
+    const dim3 grid((unsigned)((a.num_workers + 3) / 4));
+    if (a.append && a.stream_kv)
+      hipLaunchKernelGGL((decode_partition_run_kernel<CT, D, B, true, true>), grid, dim3(256), 0, stream, a);
+    else if (a.append)
+      hipLaunchKernelGGL((decode_partition_run_kernel<CT, D, B, true, false>), grid, dim3(256), 0, stream, a);
+    else if (a.stream_kv)
+      hipLaunchKernelGGL((decode_partition_run_kernel<CT, D, B, false, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_partition_run_kernel<CT, D, B, false, false>), grid, dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (a.phase != kMergePhase) {
     const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     constexpr int B = ring_depth<CT, D>();
     const dim3 block(NW * 64);

@@ -27,7 +27,8 @@ def _gpu():
 
 
 MODES = [("single", 0, 1, 0), ("single", 0, 8, 0), ("partitioned", 64, 2, 0),
-         ("partitioned", 32, 4, 0), ("balanced", 0, 0, 0), ("balanced", 0, 0, 7), ("auto", 0, 0, 0)]
+         ("partitioned", 32, 4, 0), ("partitioned", 16, 1, 5), ("partitioned", 64, 0, 0),
+         ("balanced", 0, 0, 0), ("balanced", 0, 0, 7), ("auto", 0, 0, 0)]
 
 
 def _mid(m):
