@@ -481,11 +481,12 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
 
   const int g = lane & 15;
   const bool g_ok = g < G;
-  // Partial states of this run's pieces, staged in LDS and written out at the
-  // end of the run (or when the buffer is full): a global store in the middle
-  // of the run would hold up the next piece's loads until it completes.
-  // Slot: G rows of D floats, then G (max, sum) pairs; meta: (workspace slot,
-  // segment, and the segment's piece record when this is its last piece).
+  // States of this run's pieces (partial states, or the final rows of a pair
+  // the run holds whole), staged in LDS and written out at the end of the run
+  // (or when the buffer is full): a global store in the middle of the run
+  // would hold up the next piece's loads until it completes.  Slot: G rows of
+  // D floats, then G (max, sum) pairs; meta: (workspace slot, or -1 for final
+  // rows; segment; the segment's piece record when this is its last piece).
   constexpr int kPendFloats = 4096;  // 16 KiB per wavefront
   __shared__ __attribute__((aligned(16))) float sm_pend[4][kPendFloats];
   __shared__ int4 sm_pend_meta[4][16];
@@ -499,6 +500,20 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
     for (int j = 0; j < npend; ++j) {
       const int4 meta = pend_meta[j];
       const float* slot = pend + j * kSlotFloats;
+      if (meta.x < 0) {  // a whole pair: G consecutive output rows
+        const int sj = meta.y / Hkv, hj = meta.y - sj * Hkv;
+        const int64_t row0 = (int64_t)sj * a.num_q_heads + hj * G;
+        for (int u = lane; u < G * D / 4; u += 64) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(slot + 4 * u);
+          const float xv[4] = {v[0], v[1], v[2], v[3]};
+          store_run<CT, 4>(a.out, row0 * D + 4 * u, xv);
+        }
+        if (lane == 0) {
+          a.ws_meta[2 * (int64_t)meta.y] = meta.z;
+          a.ws_meta[2 * (int64_t)meta.y + 1] = meta.w;
+        }
+        continue;
+      }
       float* dst = a.ws_acc + (int64_t)meta.x * G * D;
       for (int u = lane; u < G * D / 4; u += 64)
         *reinterpret_cast<f32x4*>(dst + 4 * u) = *reinterpret_cast<const f32x4*>(slot + 4 * u);
@@ -644,26 +659,23 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
     l_run = sum_over_lane_groups(l_run);
 
     const bool whole = tl == 0 && te == n && !a.cascade;  // cascade: always pieces
+    if (npend == kPendSlots) flush();
+    float* slot = pend + npend * kSlotFloats;
     if (whole) {
-      // finalised in place; its record says so
-      if (lane == 0) {
-        a.ws_meta[2 * (int64_t)seg] = -1;
-        a.ws_meta[2 * (int64_t)seg + 1] = -1;
-      }
+      // finalised in place (the rows in column order); its record says so
       if (g_ok) {
-        const int64_t row = (int64_t)s_cur * a.num_q_heads + qh;
         const float inv = a.v_scale / l_run;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float xo[VE];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int r = 0; r < VE; ++r) xo[r] = st.acc[r][i] * inv;
-          store_run<CT, VE>(a.out, row * D + VE * (4 * (lane >> 4) + i), xo);
-        }
+          for (int q4 = 0; q4 < VE / 4; ++q4)
+            *reinterpret_cast<f32x4*>(slot + g * D + VE * (4 * (lane >> 4) + i) + 4 * q4) =
+                f32x4{st.acc[4 * q4][i] * inv, st.acc[4 * q4 + 1][i] * inv, st.acc[4 * q4 + 2][i] * inv,
+                      st.acc[4 * q4 + 3][i] * inv};
       }
+      if (lane == 0) pend_meta[npend] = int4{-1, seg, -1, -1};
+      ++npend;
     } else {
-      if (npend == kPendSlots) flush();
-      float* slot = pend + npend * kSlotFloats;
       if (g_ok) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -761,10 +773,11 @@ __global__ __launch_bounds__(256, 1) void decode_partition_run_kernel(DecodeArgs
   const int g = lane & 15;
   const bool g_ok = g < G;
   const int64_t block_rows = (int64_t)Hkv * bs;
-  // Partial states of this wavefront's partitions, staged in LDS and written
-  // out when the buffer is full and at the end of the run, so that no store
-  // sits in front of the next partition's loads.  Slot: G rows of D floats,
-  // then G (max, sum) pairs.
+  // States of this wavefront's partitions (partial states, or the final rows
+  // of a pair held by one partition), staged in LDS and written out when the
+  // buffer is full and at the end of the run, so that no store sits in front
+  // of the next partition's loads.  Slot: G rows of D floats, then G (max,
+  // sum) pairs.
   constexpr int kPendFloats = 8192;  // 32 KiB per wavefront
   __shared__ __attribute__((aligned(16))) float sm_pend[4][kPendFloats];
   __shared__ int2 sm_pend_meta[4][64];
@@ -776,10 +789,18 @@ __global__ __launch_bounds__(256, 1) void decode_partition_run_kernel(DecodeArgs
   int npend = 0;
   auto flush = [&]() {
     for (int j = 0; j < npend; ++j) {
-      const int2 meta = pend_meta[j];  // (pair, partition)
+      const int2 meta = pend_meta[j];  // (pair, partition or -1 for final rows)
       const int sj = meta.x / Hkv, hj = meta.x - sj * Hkv;
       const int64_t row0 = (int64_t)sj * a.num_q_heads + hj * G;
       const float* slot = pend + j * kSlotFloats;
+      if (meta.y < 0) {  // the pair's final rows: G consecutive output rows
+        for (int u = lane; u < G * D / 4; u += 64) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(slot + 4 * u);
+          const float xv[4] = {v[0], v[1], v[2], v[3]};
+          store_run<CT, 4>(a.out, row0 * D + 4 * u, xv);
+        }
+        continue;
+      }
       for (int u = lane; u < G * D / 4; u += 64) {
         const int gg = u / (D / 4), c4 = u - gg * (D / 4);
         *reinterpret_cast<f32x4*>(a.ws_acc + ((row0 + gg) * a.num_parts + meta.y) * D + 4 * c4) =
@@ -893,25 +914,23 @@ __global__ __launch_bounds__(256, 1) void decode_partition_run_kernel(DecodeArgs
     if (slot_new >= 0) nrow.store(a, slot_new, h, lane);
     const float m_run = st.m;
     const float l_run = sum_over_lane_groups(st.l);
-    if (g_ok) {
-      const int64_t row = (int64_t)s_cur * a.num_q_heads + qh;
-      if (np == 1) {  // one partition holds the whole context: the final rows
-        const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x[VE];
-#pragma unroll
-          for (int r = 0; r < VE; ++r) x[r] = st.acc[r][i] * inv;
-          store_run<CT, VE>(a.out, row * D + VE * (4 * (lane >> 4) + i), x);
-        }
-      }
-    }
-    if (np > 1) {
-      // the partial state waits in LDS: a global store here would hold up the
-      // next partition's loads until it completes
+    {
+      // the state waits in LDS: a global store here would hold up the next
+      // partition's loads until it completes
       if (npend == kPendSlots) flush();
       float* slot = pend + npend * kSlotFloats;
-      if (g_ok) {
+      if (np == 1) {  // one partition holds the whole context: the final rows, in column order
+        const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
+        if (g_ok) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < VE / 4; ++q4)
+              *reinterpret_cast<f32x4*>(slot + g * D + VE * (4 * (lane >> 4) + i) + 4 * q4) =
+                  f32x4{st.acc[4 * q4][i] * inv, st.acc[4 * q4 + 1][i] * inv, st.acc[4 * q4 + 2][i] * inv,
+                        st.acc[4 * q4 + 3][i] * inv};
+        }
+      } else if (g_ok) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -920,7 +939,7 @@ __global__ __launch_bounds__(256, 1) void decode_partition_run_kernel(DecodeArgs
                 f32x4{st.acc[4 * q4][i], st.acc[4 * q4 + 1][i], st.acc[4 * q4 + 2][i], st.acc[4 * q4 + 3][i]};
         if (lane < 16) *reinterpret_cast<f32x2*>(slot + G * D + 2 * g) = f32x2{m_run, l_run};
       }
-      if (lane == 0) pend_meta[npend] = int2{seg, part};
+      if (lane == 0) pend_meta[npend] = int2{seg, np == 1 ? -1 : part};  // -1: final rows
       ++npend;
     }
     ++t;
