@@ -497,6 +497,7 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
   const int kPendSlots = min(16, kPendFloats / kSlotFloats);
   int npend = 0;
   auto flush = [&]() {
+    wave_lds_sync();  // slots and meta were written by other lanes
     for (int j = 0; j < npend; ++j) {
       const int4 meta = pend_meta[j];
       const float* slot = pend + j * kSlotFloats;
@@ -525,6 +526,7 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
         a.ws_meta[2 * (int64_t)meta.y + 1] = meta.w;
       }
     }
+    wave_lds_sync();  // every lane is done reading before the slots are reused
     npend = 0;
   };
   int64_t x = x0;
@@ -788,6 +790,7 @@ __global__ __launch_bounds__(256, 1) void decode_partition_run_kernel(DecodeArgs
   const int kPendSlots = min(64, kPendFloats / kSlotFloats);
   int npend = 0;
   auto flush = [&]() {
+    wave_lds_sync();  // slots and meta were written by other lanes
     for (int j = 0; j < npend; ++j) {
       const int2 meta = pend_meta[j];  // (pair, partition or -1 for final rows)
       const int sj = meta.x / Hkv, hj = meta.x - sj * Hkv;
@@ -810,6 +813,7 @@ __global__ __launch_bounds__(256, 1) void decode_partition_run_kernel(DecodeArgs
         *reinterpret_cast<f32x2*>(a.ws_ml + ((row0 + lane) * a.num_parts + meta.y) * 2) =
             *reinterpret_cast<const f32x2*>(slot + G * D + 2 * lane);
     }
+    wave_lds_sync();  // every lane is done reading before the slots are reused
     npend = 0;
   };
   typename T::QFrag qf;
