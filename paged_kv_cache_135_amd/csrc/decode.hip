@@ -395,6 +395,16 @@ __device__ void write_zero_rows(const DecodeArgs& a, int s, int lane) {
   for (int i = lane; i < n16; i += 64) reinterpret_cast<u32x4*>(o)[i] = u32x4{0, 0, 0, 0};
 }
 
+// Orders one wavefront's LDS accesses across its lanes: what any lane wrote
+// before is visible to every lane after, and no access moves across it.
+// Emits no barrier instruction (a wavefront's LDS operations already complete
+// in issue order); it only fixes the compiler's order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // At most two wavefronts per SIMD (the split runs 4 or 8 workers per CU): with
 // the tighter three-per-SIMD budget the loop lost its load scheduling (the
 // Qwen-shaped batch: 44.5 us per launch at two, 52 us when it spilled at three).

@@ -474,16 +474,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
   return x;
 }
 
-// Orders one wavefront's LDS accesses across its lanes: what any lane wrote
-// before is visible to every lane after, and no access moves across it.
-// Emits no barrier instruction (a wavefront's LDS operations already complete
-// in issue order); it only fixes the compiler's order.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Online-softmax state of one wavefront: per lane, head g = lane % 16.
 template <int VE>
 struct Softmax {
