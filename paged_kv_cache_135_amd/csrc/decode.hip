@@ -585,46 +585,38 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
     const int qh = h * G + g;
     const QElem<CT>* qrow = static_cast<const QElem<CT>*>(a.q) +
                             ((int64_t)s_cur * a.num_q_heads + (g_ok ? qh : 0)) * D;
+    const typename T::QFrag qf = T::load_q(qrow, g_ok, lane);
     const int32_t* table = a.tables + (int64_t)s_cur * a.max_blocks;
     const int64_t head_rows = (int64_t)h * bs;
     const int64_t block_rows = (int64_t)Hkv * bs;
-    // Load order at a piece start.  The vector-memory counter retires loads
-    // in issue order, so the first batch's tile loads must not follow a load
-    // they do not need.  Its block ids come first: only the run's first piece
-    // reads them here, every later piece was handed them by the piece before.
-    // q, the append row and slot, the next batch's block ids and the next
-    // piece's first block ids are issued after the tiles.
-    // Block ids: tiles past the piece clamp to its last tile (in bounds,
-    // result unused).
-    const ctab ctable = (ctab)table;  // address-space cast: C-style only
-    auto entry = [&](int t) { return ctable[(min(t, te - 1) * 16) / bs]; };
-    int32_t ent_next[NBUF];
-    if (has_carry) {
-#pragma unroll
-      for (int j = 0; j < NBUF; ++j) ent_next[j] = carry[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < NBUF; ++j) ent_next[j] = entry(tl + j);
-    }
 
     Softmax<VE> st;
 #pragma unroll
     for (int r = 0; r < VE; ++r) st.acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Append: the piece holding the pair's last tile writes the new token's rows
-    // to their slot (loaded with its first batch, stored at its end) and, when
-    // that slot is position ctx-1, reads them from k / v in its last batch.
-    const bool ends_pair = APPEND && te == n;
-    int32_t slot_new = -1;
-    NewRow<CT, D> nrow;
+    // to their slot (loaded now, stored at the end) and, when that slot is
+    // position ctx-1, reads them from k / v.
+    const int32_t slot_new = APPEND && te == n ? a.slots[s_cur] : -1;
     const int r_new = (ctx - 1) & 15;
     const int64_t off_new = (ctx - 1) % bs;
     const int64_t new_row = (int64_t)s_cur * Hkv + h;
     const void* kn = static_cast<const QElem<CT>*>(a.kn) + new_row * D;
     const void* vn = static_cast<const QElem<CT>*>(a.vn) + new_row * D;
+    NewRow<CT, D> nrow;
+    if (slot_new >= 0) nrow.load(a, s_cur, h, lane);
+    // Block ids of the next batch arrive one batch ahead, through scalar loads
+    // (the tables are read-only here, so they are read as constant memory:
+    // the ids never wait in the vector-memory queue behind the tile loads);
+    // tiles past the piece clamp to its last tile (in bounds, result unused).
+    const ctab ctable = (ctab)table;  // address-space cast: C-style only
+    auto entry = [&](int t) { return ctable[(min(t, te - 1) * 16) / bs]; };
+    int32_t ent_next[NBUF];
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) ent_next[j] = has_carry ? carry[j] : entry(tl + j);
     // When the run goes on into the next pair (the next KV head of this
     // sequence, or the next sequence with tokens), that piece starts at tile 0
-    // of its table row: its first block ids are fetched during this piece's
-    // first batch, so the piece change costs no dependent table read.
+    // of its table row: fetch its first block ids now, so the piece change
+    // costs no dependent table read.
     const int64_t after = x + (ve - vt);
     has_carry = ve == u && x1 - after > kPieceCost;
     int s_next = s_cur;
@@ -635,20 +627,22 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
     const int te_next =
         has_carry ? (int)min((int64_t)((ctx_of(s_next) + 15) >> 4), x1 - after - kPieceCost) : 1;
     const int32_t* table_next = a.tables + (int64_t)s_next * a.max_blocks;
-    typename T::QFrag qf;
     for (int k = tl; k < te; k += NBUF) {
       int32_t ent[NBUF];
 #pragma unroll
-      for (int j = 0; j < NBUF; ++j) ent[j] = ent_next[j];
+      for (int j = 0; j < NBUF; ++j) {
+        ent[j] = ent_next[j];
+        ent_next[j] = entry(k + NBUF + j);
+      }
+      if (has_carry && k == tl) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j)
+          carry[j] = ((ctab)table_next)[(min(j, te_next - 1) * 16) / bs];
+      }
       T buf[NBUF];
-      if (APPEND && ends_pair && k + NBUF >= n) {
+      if (APPEND && slot_new >= 0 && k + NBUF >= n) {
         // the batch holding the pair's last tile: its new token's rows come
-        // from k / v (a per-lane address choice) when the slot is position
-        // ctx-1; a piece of one batch reads the slot and the rows first
-        if (k == tl) {
-          slot_new = a.slots[s_cur];
-          nrow.load(a, s_cur, h, lane);
-        }
+        // from k / v (a per-lane address choice) when the slot is position ctx-1
 #pragma unroll
         for (int j = 0; j < NBUF; ++j) {
           const int t = min(k + j, te - 1);
@@ -665,23 +659,6 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
           const int64_t row = (int64_t)ent[j] * block_rows + head_rows + ((t * 16) % bs);
           buf[j].template load<NT>(a.kc, a.vc, row, lane);
         }
-        if (ends_pair && k == tl) {
-          slot_new = a.slots[s_cur];
-          nrow.load(a, s_cur, h, lane);
-        }
-      }
-      // behind the tiles: q (first batch), the next batch's block ids and the
-      // next piece's first block ids.  q is loaded without a per-lane select
-      // (a select would wait for the load right here, and with it for the
-      // tiles): padding columns (g >= G) read head 0's row, and their scores,
-      // sums and outputs are never stored.
-      if (k == tl) qf = T::load_q(qrow, true, lane);
-#pragma unroll
-      for (int j = 0; j < NBUF; ++j) ent_next[j] = entry(k + NBUF + j);
-      if (has_carry && k == tl) {
-#pragma unroll
-        for (int j = 0; j < NBUF; ++j)
-          carry[j] = ((ctab)table_next)[(min(j, te_next - 1) * 16) / bs];
       }
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
@@ -689,12 +666,7 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(DecodeArgs a) {
         process_tile<CT, D>(buf[j], qf, st, (k + j) * 16, ctx, a.qk_scale, lane);
       }
     }
-    // The next piece's first block ids (uniform: one table entry) move to
-    // scalar registers before the row store below is issued, so the next
-    // piece's first tile loads wait for neither.
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j) carry[j] = __builtin_amdgcn_readfirstlane(carry[j]);
-    if (ends_pair && slot_new >= 0) nrow.store(a, slot_new, h, lane);
+    if (slot_new >= 0) nrow.store(a, slot_new, h, lane);
     float l_run = st.l;
     l_run = sum_over_lane_groups(l_run);
 
