@@ -839,8 +839,9 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / n
 
-    # timed region 3: the whole decode call (every kernel it launches: for the
-    # balanced split one launch that also merges) K times back to back
+    # timed region 3: the whole decode call (every kernel it launches: the
+    # streaming kernel and, for split pairs or partitions, its merge or reduce
+    # kernel) K times back to back
     call_s = back_to_back(decodes, K)
     # hot cache, reported beside the cold figure: every call reads the same
     # layer's pool (above, the pools rotate so each call reads from HBM)
