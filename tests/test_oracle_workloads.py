@@ -41,3 +41,21 @@ def test_waste_is_below_one_block_per_sequence():
     waste = [(-int(n)) % bs for n in case.context_lens]
     assert waste == [15, 15, 8, 12]
     assert max(waste) <= bs - 1
+
+
+def test_step_writes_into_a_shared_block_come_from_one_sequence():
+    # "PagedAttention Memory Management", "Complex Topologies and Memory
+    # Sharing": a block listed by several tables is copied before one of them
+    # writes into it.  Sequences whose context ends inside the shared prefix
+    # would all write its last slot; the generator lets the first of them write
+    # and skips the others (slot -1), so no two writes of one step collide.
+    case = workloads.build_case("ends_in_prefix", seed=5, context_lens=[64, 64, 70, 64, 90],
+                                num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=32,
+                                cache_dtype="bf16", std=0.5, scale=0.125, shared_prefix_blocks=2)
+    slots = case.slot_mapping
+    assert slots.size == 5
+    live = slots[slots >= 0]
+    assert np.unique(live).size == live.size
+    last_prefix_slot = int(case.block_tables[0, 1]) * 32 + 31
+    assert slots[0] == last_prefix_slot and slots[1] == -1 and slots[3] == -1
+    assert slots[2] >= 0 and slots[4] >= 0

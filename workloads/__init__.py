@@ -298,6 +298,13 @@ def build_case(name: str, *, seed: int, context_lens, num_q_heads: int, num_kv_h
         live = np.nonzero(ctx > 0)[0]
         slots = np.array([slots_of(tables, int(s), [int(ctx[s]) - 1], bs)[0] for s in live],
                          dtype=np.int32)
+        # a slot in a block several tables share (a sequence whose context
+        # ends inside the shared prefix) is written by the first of them only:
+        # the others would first need a copy-on-write of that block
+        _, first = np.unique(slots, return_index=True)
+        dup = np.ones(slots.size, dtype=bool)
+        dup[first] = False
+        slots[dup] = -1
         kn = np.empty((live.size, Hkv, D), dtype=_np_dtype(in_elem))
         vn = np.empty_like(kn)
         fill_normal(kn, std, seed, _STREAM_NEWK)
