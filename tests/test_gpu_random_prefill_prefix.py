@@ -108,3 +108,39 @@ def test_random_shared_prefix(seed):
     assert np.array_equal(bits(gu.host(g.kc)), bits(kc)), what + ": key pool"
     assert np.array_equal(bits(gu.host(g.vc)), bits(vc)), what + ": value pool"
     gu.assert_close(gu.host(out), gu.oracle_decode(case, kc, vc), dtype, what)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_shared_prefix_append_step(seed):
+    """The one-call shared-prefix step (the step's write folded in): every
+    tail holds at least the new token."""
+    rng = np.random.default_rng([seed, 7171])
+    dtype, D, bs, Hkv, G = _shape(rng)
+    S = int(rng.integers(1, 40))
+    shared = int(rng.integers(1, 9))
+    tails = [int(rng.choice([1, 2, int(rng.integers(3, 400))])) for _ in range(S)]
+    workers = [0, 0, int(rng.integers(1, 64))][int(rng.integers(0, 3))]
+    stream_kv = bool(rng.integers(0, 2))
+    case = workloads.build_case(f"rprefixapp{seed}", seed=5000 + seed,
+                                context_lens=[shared * bs + t for t in tails], num_q_heads=Hkv * G,
+                                num_kv_heads=Hkv, head_dim=D, block_size=bs, cache_dtype=dtype,
+                                std=1.0 if dtype == "f32" else 0.5, scale=1.0 / math.sqrt(D),
+                                shared_prefix_blocks=shared)
+    prefix = shared * bs
+    what = (f"seed {seed}: {dtype} D={D} bs={bs} Hq={Hkv * G} Hkv={Hkv} S={S} shared={shared} "
+            f"blocks workers={workers} stream_kv={stream_kv}")
+    print(what, flush=True)
+    g = gu.GpuCase(case)
+    if case.fill_k is not None:
+        g.write(case.fill_k, case.fill_v, case.fill_slots)
+    out = torch.full_like(g.q, float("nan"))
+    pkv.paged_attention_decode_shared_prefix_append(
+        out, g.q, gu.dev(case.k_new), gu.dev(case.v_new), gu.dev(case.slot_mapping), g.kc, g.vc,
+        g.tables, g.lens, prefix, case.scale, case.block_size, k_scale=case.k_scale,
+        v_scale=case.v_scale, num_workers=workers, stream_kv=stream_kv)
+    torch.cuda.synchronize()
+    kc, vc = gu.oracle_caches(case)
+    bits = lambda a: a.view(np.uint32) if a.dtype == np.float32 else a
+    assert np.array_equal(bits(gu.host(g.kc)), bits(kc)), what + ": key pool"
+    assert np.array_equal(bits(gu.host(g.vc)), bits(vc)), what + ": value pool"
+    gu.assert_close(gu.host(out), gu.oracle_decode(case, kc, vc), dtype, what)
