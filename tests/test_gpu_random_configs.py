@@ -6,7 +6,8 @@ Each case draws its shape and launch at random from a fixed seed: cache format
 empty, single-token, tile-edge and ragged contexts, and one decode launch
 (single pass with 1-8 wavefronts, split-K partitions, the balanced split with
 its default or a small worker count, auto), with or without streaming pool
-reads.  The step's KV write is done either by paged_kv_write followed by the
+reads.  A second set draws near the supported limits: 9-16 query heads per KV
+head and blocks of 128 or 256 tokens.  The step's KV write is done either by paged_kv_write followed by the
 decode or folded into paged_attention_decode_append; both must leave the
 oracle's written pool bit for bit and give the oracle's output on that pool,
 within the format's tolerance, and empty sequences must give zero rows.  The cases complement the
@@ -25,6 +26,7 @@ torch = gu.torch
 import paged_kv_cache_135_amd as pkv  # noqa: E402
 
 NUM_CASES = 160
+NUM_NEAR_LIMITS = 48
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -52,13 +54,20 @@ def _lengths(rng, n, block_size):
     return out
 
 
-def _draw(seed):
-    rng = np.random.default_rng([seed, 4242])
+def _draw(seed, near_limits=False):
+    rng = np.random.default_rng([seed, 4242 if not near_limits else 4343])
     dtype = ["f32", "bf16", "bf16", "fp8_e4m3"][int(rng.integers(0, 4))]
     D = [64, 128][int(rng.integers(0, 2))]
-    bs = [16, 32, 64][int(rng.integers(0, 3))]
-    Hkv = [1, 2, 4, 8][int(rng.integers(0, 4))]
-    G = [1, 2, 4, 7, 8][int(rng.integers(0, 5))]
+    if near_limits:
+        # the largest group sizes (up to 16 query heads per KV head) and block
+        # sizes (up to 256 tokens, 16 tiles a block)
+        bs = [128, 256, 256][int(rng.integers(0, 3))]
+        Hkv = [1, 2, 3][int(rng.integers(0, 3))]
+        G = int(rng.integers(9, 17))
+    else:
+        bs = [16, 32, 64][int(rng.integers(0, 3))]
+        Hkv = [1, 2, 4, 8][int(rng.integers(0, 4))]
+        G = [1, 2, 4, 7, 8][int(rng.integers(0, 5))]
     S = int(rng.integers(1, 25))
     lens = _lengths(rng, S, bs)
     modes = [("single", 0, 1, 0), ("single", 0, 4, 0), ("single", 0, 8, 0),
@@ -86,9 +95,10 @@ def _rows_per_sequence(case):
     return k, v, slots
 
 
-@pytest.mark.parametrize("seed", range(NUM_CASES))
-def test_random_configuration(seed):
-    case, (mode, part, waves, workers), stream_kv, append = _draw(seed)
+@pytest.mark.parametrize("near_limits,seed",
+                         [(False, s) for s in range(NUM_CASES)] + [(True, s) for s in range(NUM_NEAR_LIMITS)])
+def test_random_configuration(near_limits, seed):
+    case, (mode, part, waves, workers), stream_kv, append = _draw(seed, near_limits)
     what = (f"seed {seed}: {case.cache_dtype} D={case.head_dim} bs={case.block_size} "
             f"Hq={case.num_q_heads} Hkv={case.num_kv_heads} S={case.num_seqs} "
             f"{mode}/{part}/{waves}/{workers} stream_kv={stream_kv} append={append}")

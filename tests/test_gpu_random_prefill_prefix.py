@@ -7,7 +7,9 @@ number of sequences, each sequence's cached prefix (often none) and chunk
 length (0, 1 or many tokens), and the rows per wavefront.  Shared-prefix cases
 draw the same shape parameters, the number of shared blocks and each
 sequence's private tail (often empty or one token), and the balanced split's
-worker count; the pools the writes leave must be the oracle's bit for bit.
+worker count; the pools the writes leave must be the oracle's bit for bit.  A
+second set of each draws near the supported limits: 9-16 query heads per KV
+head and blocks of 128 or 256 tokens.
 Every output is compared with the plain oracle, which knows nothing of chunks
 or sharing, within the format's tolerance."""
 import math
@@ -24,6 +26,7 @@ import paged_kv_cache_135_amd as pkv  # noqa: E402
 
 NUM_PREFILL = 64
 NUM_PREFIX = 64
+NUM_NEAR_LIMITS = 24
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -31,20 +34,32 @@ def _gpu():
     gu.need_gpu()
 
 
-def _shape(rng):
+def _shape(rng, near_limits):
     dtype = ["f32", "bf16", "bf16", "fp8_e4m3"][int(rng.integers(0, 4))]
     D = [64, 128][int(rng.integers(0, 2))]
+    if near_limits:
+        # up to 16 query heads per KV head and blocks of 128 or 256 tokens
+        return dtype, D, [128, 256][int(rng.integers(0, 2))], int(rng.integers(1, 4)), \
+            int(rng.integers(9, 17))
     bs = [16, 32, 64][int(rng.integers(0, 3))]
     Hkv = [1, 2, 4, 8][int(rng.integers(0, 4))]
     G = [1, 2, 4, 7, 8][int(rng.integers(0, 5))]
     return dtype, D, bs, Hkv, G
 
 
-@pytest.mark.parametrize("seed", range(NUM_PREFILL))
-def test_random_prefill(seed):
+def _cases(n, n_near):
+    return [(False, s) for s in range(n)] + [(True, s) for s in range(n_near)]
+
+
+def _rng(seed, salt, near_limits):
+    return np.random.default_rng([seed, salt, 1] if near_limits else [seed, salt])
+
+
+@pytest.mark.parametrize("near_limits,seed", _cases(NUM_PREFILL, NUM_NEAR_LIMITS))
+def test_random_prefill(near_limits, seed):
     import oracle
-    rng = np.random.default_rng([seed, 5151])
-    dtype, D, bs, Hkv, G = _shape(rng)
+    rng = _rng(seed, 5151, near_limits)
+    dtype, D, bs, Hkv, G = _shape(rng, near_limits)
     S = int(rng.integers(1, 9))
     prefix = [0 if rng.integers(0, 3) == 0 else int(rng.integers(1, 700)) for _ in range(S)]
     chunk = [int(rng.choice([0, 1, int(rng.integers(2, 300))])) for _ in range(S)]
@@ -77,10 +92,10 @@ def test_random_prefill(seed):
     gu.assert_close(gu.host(out), ref, dtype, what)
 
 
-@pytest.mark.parametrize("seed", range(NUM_PREFIX))
-def test_random_shared_prefix(seed):
-    rng = np.random.default_rng([seed, 6161])
-    dtype, D, bs, Hkv, G = _shape(rng)
+@pytest.mark.parametrize("near_limits,seed", _cases(NUM_PREFIX, NUM_NEAR_LIMITS))
+def test_random_shared_prefix(near_limits, seed):
+    rng = _rng(seed, 6161, near_limits)
+    dtype, D, bs, Hkv, G = _shape(rng, near_limits)
     S = int(rng.integers(1, 40))
     shared = int(rng.integers(1, 9))
     tails = [int(rng.choice([0, 1, int(rng.integers(2, 400))])) for _ in range(S)]
@@ -110,12 +125,12 @@ def test_random_shared_prefix(seed):
     gu.assert_close(gu.host(out), gu.oracle_decode(case, kc, vc), dtype, what)
 
 
-@pytest.mark.parametrize("seed", range(32))
-def test_random_shared_prefix_append_step(seed):
+@pytest.mark.parametrize("near_limits,seed", _cases(32, NUM_NEAR_LIMITS // 2))
+def test_random_shared_prefix_append_step(near_limits, seed):
     """The one-call shared-prefix step (the step's write folded in): every
     tail holds at least the new token."""
-    rng = np.random.default_rng([seed, 7171])
-    dtype, D, bs, Hkv, G = _shape(rng)
+    rng = _rng(seed, 7171, near_limits)
+    dtype, D, bs, Hkv, G = _shape(rng, near_limits)
     S = int(rng.integers(1, 40))
     shared = int(rng.integers(1, 9))
     tails = [int(rng.choice([1, 2, int(rng.integers(3, 400))])) for _ in range(S)]
