@@ -95,7 +95,8 @@ typedef struct {
   int32_t dtype;                 /* pkv_dtype */
   int32_t ndim;                  /* number of used entries in shape/stride, <= 4 */
   int64_t shape[PKV_MAX_DIMS];
-  int64_t stride[PKV_MAX_DIMS];  /* in elements; the kernels require dense row-major */
+  int64_t stride[PKV_MAX_DIMS];  /* in elements; the kernels require dense row-major (a
+                                    tensor with no elements may have any strides) */
   float scale;                   /* E4M3 tensors: dequantisation scale (> 0, finite);
                                     ignored for other element types */
 } pkv_tensor;

@@ -52,15 +52,19 @@ pkv_status check_tensor(const pkv_tensor* t, const char* name, int ndim) {
   if (!t) return fail(PKV_ERR_NULL, "%s: descriptor is NULL", name);
   if (t->ndim != ndim) return fail(PKV_ERR_SHAPE, "%s: expected %d dims, got %d", name, ndim, t->ndim);
   if (elem_bytes(t->dtype) == 0) return fail(PKV_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(PKV_ERR_SHAPE, "%s: negative size in dim %d", name, i);
+  // a tensor with no elements has no layout (frameworks report any strides
+  // for one, zero included)
+  if (numel(t) == 0) return PKV_OK;
   int64_t expect = 1;
   for (int i = ndim - 1; i >= 0; --i) {
-    if (t->shape[i] < 0) return fail(PKV_ERR_SHAPE, "%s: negative size in dim %d", name, i);
     if (t->shape[i] > 1 && t->stride[i] != expect)
       return fail(PKV_ERR_LAYOUT, "%s: not dense row-major (dim %d stride %lld, expected %lld)",
                   name, i, (long long)t->stride[i], (long long)expect);
     expect *= t->shape[i];
   }
-  if (numel(t) > 0 && !t->data) return fail(PKV_ERR_NULL, "%s: data pointer is NULL", name);
+  if (!t->data) return fail(PKV_ERR_NULL, "%s: data pointer is NULL", name);
   return PKV_OK;
 }
 

@@ -192,6 +192,12 @@ def test_write_rejects_bad_descriptors():
     # empty batch: nothing to launch, OK
     e = desc([0, H, D], B.PKV_BF16, 0)
     assert _write(e, desc([0, H, D], B.PKV_BF16, 0), desc([0], B.PKV_I32, 0), kc, vc) == 0
+    # a tensor with no elements may carry any strides (torch reports zeros for
+    # some empty tensors); a non-empty one must still be dense
+    z = desc([0, H, D], B.PKV_BF16, 0, strides=[0, 0, 0])
+    assert _write(z, desc([0, H, D], B.PKV_BF16, 0, strides=[7, 3, 0]),
+                  desc([0], B.PKV_I32, 0, strides=[0]), kc, vc) == 0
+    assert _write(desc([T, H, D], B.PKV_BF16, strides=[H * D, D, 2]), v, s, kc, vc) == 4
 
 
 def test_host_validators():
