@@ -481,7 +481,8 @@ pkv_status pkv_tile_gather_probe(const void* key_cache, const void* value_cache,
                                  int32_t workers, int32_t mode, uint32_t* sink, void* hip_stream);
 
 /* Workspace bytes paged_attention_decode needs with these sizes and options
- * (0 when none is needed: single pass, or one partition per sequence).
+ * (0 when none is needed: no sequences, single pass, or one partition per
+ * sequence).
  * Returns 0 as well for invalid arguments. */
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim,

@@ -581,7 +581,7 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
                                               int32_t num_kv_heads, int32_t head_dim,
                                               int32_t max_blocks_per_seq, int32_t block_size,
                                               const pkv_decode_opts* opts) {
-  if (num_seqs < 0 || num_q_heads < 0 || num_kv_heads <= 0 || head_dim < 0 ||
+  if (num_seqs <= 0 || num_q_heads < 0 || num_kv_heads <= 0 || head_dim < 0 ||
       max_blocks_per_seq < 0 || block_size < 0 || num_q_heads % num_kv_heads != 0)
     return 0;
   Plan p;
@@ -690,6 +690,7 @@ pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
     return fail(PKV_ERR_LAYOUT, "opts->seq_order must be 4-byte aligned");
   Plan p;
   PKV_TRY(plan(opts, S, Hq, Hkv, maxb, bs, &p, prefix_len));
+  if (S == 0) return ok();  // nothing to compute, so no workspace either
   pkv::DecodeArgs a{};
   const size_t need = p.workspace_floats(S, Hq, Hkv, D) * 4u + p.meta_bytes(S, Hkv);
   if (need > 0) {
@@ -707,7 +708,6 @@ pkv_status decode_impl(const char* fn, pkv_tensor* out, const pkv_tensor* q,
       a.ws_ml = a.ws_acc + (size_t)S * Hq * p.partitions * D;
     }
   }
-  if (S == 0) return ok();
 
   a.q = q->data;
   a.out = out->data;

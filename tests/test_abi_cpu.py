@@ -59,6 +59,9 @@ def test_workspace_bytes():
     # balanced: (workers + sequences x KV heads) slots of G x (D + 2) floats, plus 2 ints per pair
     assert ws(64, 28, 4, 128, 256, 16, mode=2, workers=2048) == (2048 + 256) * 7 * 130 * 4 + 256 * 8
     assert lib.paged_attention_decode_workspace_bytes(64, 28, 4, 128, 256, 16, None) == 0
+    # no sequences: nothing to split, in any mode
+    for mode in (1, 2, 3):
+        assert ws(0, 28, 4, 128, 256, 16, mode=mode, part=512) == 0
     # auto: 512 x 8 pairs (>= 16 per CU of a 256-CU device) -> single pass, no workspace;
     # 64 x 4 pairs -> balanced with 4 workers per CU
     assert ws(512, 32, 8, 128, 128, 16, mode=3) == 0
